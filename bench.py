@@ -1,0 +1,212 @@
+"""Benchmark of the GPTQ layer-quantization hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config opt2.7b-fc1]
+
+One step = the whole hot path on one layer with W and X already resident in
+HBM: H accumulated over the layer's calibration tokens in chunks of 16
+sequences (32768 tokens per call), the fp64 inverse-Hessian factor, then the
+column loop with lazy 128-column updates, trailing GEMMs and packing.
+Prints one JSON line (rank 0). The per-stage device times come from HIP events
+recorded on the stream the library launches on (torch's current stream).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import torch
+
+from post_weight_quantization_18_amd import gptq as G
+from post_weight_quantization_18_amd import synthetic as S
+
+PEAK_FP16_TFLOPS = 2516.6     # MI355X dense fp16/bf16 MFMA, fp32 accumulate
+PEAK_FP64_TFLOPS = 78.6       # MI355X fp64 (vector and matrix)
+PEAK_FP32_MFMA_TFLOPS = 157.3
+CHUNK_TOKENS = 32768          # 16 sequences of 2048 tokens per accumulate call
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--config", default="opt2.7b-fc1", choices=sorted(S.CONFIGS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=512)
+    p.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    return p.parse_args()
+
+
+class LayerRun:
+    """Preallocated buffers for one layer; step() enqueues the whole hot path."""
+
+    def __init__(self, cfg: S.LayerConfig, w: torch.Tensor, x: torch.Tensor):
+        self.cfg = cfg
+        self.w, self.x = w, x
+        dev = w.device
+        d, m = cfg.d, cfg.m
+        self.H = torch.empty(d, d, dtype=torch.float64, device=dev)
+        self.U = torch.empty(d, d, dtype=torch.float32, device=dev)
+        self.ws_h = torch.empty(max(1, G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, d, CHUNK_TOKENS)),
+                                dtype=torch.uint8, device=dev)
+        self.ws_c = torch.empty(G.workspace_bytes(G.WS_PREPARE_HINV, 0, d), dtype=torch.uint8, device=dev)
+        qcfg = G.make_qcfg(cfg.bits, cfg.group, cfg.grid)
+        self.ws_q = torch.empty(G.workspace_bytes(G.WS_QUANTIZE_LAYER, m, d, 0, qcfg), dtype=torch.uint8, device=dev)
+        ng = d // cfg.group if cfg.group else 1
+        self.out = {
+            "qcodes": torch.empty(m, d * cfg.bits // 32, dtype=torch.int32, device=dev),
+            "scales": torch.empty(m, ng, dtype=torch.float32, device=dev),
+            "zeros": torch.empty(m, ng, dtype=torch.uint8, device=dev),
+            "w_hat": torch.empty(m, d, dtype=torch.float32, device=dev),
+            "err_sq": torch.empty(m, dtype=torch.float32, device=dev),
+        }
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        self.ev_h = [torch.cuda.Event(enable_timing=True) for _ in range(2 * self.n_chunks())]
+        self.info = None
+
+    def n_chunks(self):
+        return (self.cfg.n_tokens + CHUNK_TOKENS - 1) // CHUNK_TOKENS
+
+    def step(self, timed_chunks=False):
+        cfg = self.cfg
+        self.ev[0].record()
+        for i in range(self.n_chunks()):
+            t0 = i * CHUNK_TOKENS
+            if timed_chunks:
+                self.ev_h[2 * i].record()
+            G.accumulate_hessian(self.H, self.x[t0:t0 + CHUNK_TOKENS], accumulate=i > 0, workspace=self.ws_h)
+            if timed_chunks:
+                self.ev_h[2 * i + 1].record()
+        self.ev[1].record()
+        _, self.info, self.lam = G.prepare_hinv(self.H, cfg.damp, U=self.U, workspace=self.ws_c)
+        self.ev[2].record()
+        G.quantize_layer(self.w, self.U, cfg.bits, cfg.group, cfg.grid, workspace=self.ws_q, out=self.out)
+        self.ev[3].record()
+
+    def stage_ms(self):
+        return {"hessian": self.ev[0].elapsed_time(self.ev[1]), "hinv_chain": self.ev[1].elapsed_time(self.ev[2]),
+                "quantize": self.ev[2].elapsed_time(self.ev[3]), "total": self.ev[0].elapsed_time(self.ev[3])}
+
+    def syrk_call_ms(self):
+        return [self.ev_h[2 * i].elapsed_time(self.ev_h[2 * i + 1]) for i in range(self.n_chunks())]
+
+
+def cpu_baseline(cfg, w, x, rows, tokens):
+    """The fp64 oracle, as it stands, on a bounded sample of the same layer:
+    H over `tokens` calibration tokens (scaled by N / tokens), the full chain on
+    d, and the column loop on `rows` rows (scaled by m / rows)."""
+    import numpy as np
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else os.cpu_count()
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    rows = min(rows, cfg.m)
+    tokens = min(tokens, cfg.n_tokens)
+    xs = x[:tokens].cpu().numpy()
+    ws = w[:rows].double().cpu().numpy()
+    t0 = time.perf_counter()
+    h = O.hessian([xs[i:i + 4096] for i in range(0, tokens, 4096)])
+    t1 = time.perf_counter()
+    hd, _ = O.damp(h, cfg.damp)
+    u = O.inverse_hessian_factor(hd)
+    t2 = time.perf_counter()
+    O.gptq_quantize(ws, u, cfg.bits, cfg.grid, cfg.group)
+    t3 = time.perf_counter()
+    t_h = (t1 - t0) * cfg.n_tokens / tokens
+    t_chain = t2 - t1
+    t_loop = (t3 - t2) * cfg.m / rows
+    total = t_h + t_chain + t_loop
+    return {
+        "value": cfg.n_weights / total,
+        "unit": "weights/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{cfg.name}: H over {tokens} of {cfg.n_tokens} tokens (x{cfg.n_tokens / tokens:g}), full fp64 "
+                   f"chain at d={cfg.d}, column loop on {rows} of {cfg.m} rows (x{cfg.m / rows:g}); measured "
+                   f"{t3 - t0:.1f} s, extrapolated {total:.1f} s per layer"),
+        "stage_s": {"hessian": t_h, "chain": t_chain, "loop": t_loop},
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding notes in the design "
+              "document); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    cfg = S.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    G.load_library()
+    w = S.make_weights(cfg, dev)
+    x = S.make_activations(cfg, dev)
+    torch.cuda.synchronize()
+    run = LayerRun(cfg, w, x)
+    for _ in range(args.warmup):
+        run.step()
+    torch.cuda.synchronize()
+    if run.info is not None and int(run.info.item()) != 0:
+        raise RuntimeError("H + lambda I not positive definite")
+
+    stage_acc = {}
+    syrk_calls = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run.step(timed_chunks=True)
+        torch.cuda.synchronize()
+        for k, v in run.stage_ms().items():
+            stage_acc[k] = stage_acc.get(k, 0.0) + v
+        syrk_calls += run.syrk_call_ms()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = {k: v / args.steps for k, v in stage_acc.items()}
+    ms_per_step = wall * 1e3 / args.steps
+
+    d, m, n = cfg.d, cfg.m, cfg.n_tokens
+    # algorithmic work
+    f_syrk_call = CHUNK_TOKENS * d * (d + 1)                     # lower triangle of 2 X^T X per call
+    f_syrk = n * d * (d + 1)
+    f_chain = 2 * d ** 3 / 3                                     # Cholesky + triangular inverse
+    syrk_call_ms = sum(syrk_calls) / len(syrk_calls)
+    syrk_tflops = f_syrk_call / (syrk_call_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "gptq_accumulate_hessian (syrk_kernel + split-K fp64 combine)",
+                "achieved": round(syrk_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(syrk_tflops / PEAK_FP16_TFLOPS, 4), "traffic": None,
+                "per_launch": {"flops": f_syrk_call, "tokens": CHUNK_TOKENS, "avg_ms": round(syrk_call_ms, 4)}}
+    result = {
+        "metric": "GPTQ layer quantize throughput (weights quantized per second, whole hot path)",
+        "value": cfg.n_weights / (ms_per_step * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA->f32/f64 (H), f64 (U), f32 (column loop, trailing GEMM)",
+        "data": "synthetic (seeded correlated-Gaussian X with outlier channels, N(0,0.02^2) W with outlier columns)",
+        "config": {"workload": f"{cfg.name}: W {m}x{d} {cfg.w_dtype}, X {n}x{d} fp16, {cfg.bits}-bit {cfg.grid} "
+                               f"{'per-row' if cfg.group == 0 else 'g' + str(cfg.group)}, block 128, damp {cfg.damp}",
+                   "chunk_tokens": CHUNK_TOKENS, "m": m, "d": d, "n_tokens": n},
+        "stages_ms": {k: round(v, 4) for k, v in stage.items()},
+        "mfma_frac": {"syrk_fp16": round(f_syrk / (stage["hessian"] * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
+                      "chain_fp64": round(f_chain / (stage["hinv_chain"] * 1e-3) / 1e12 / PEAK_FP64_TFLOPS, 4)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, w, x, args.cpu_sample_rows, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

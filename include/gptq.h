@@ -1,0 +1,163 @@
+/*
+ * gptq.h -- C ABI of the MI355X (gfx950) GPTQ layer-quantization library
+ * (libgptq_mi355x.so).
+ *
+ * The method: for one linear layer with weights W [m, d] and calibration
+ * activations X [N, d], form H = 2 X^T X, damp it, take the upper Cholesky
+ * factor U of H^-1, then round the columns of W one by one in natural order,
+ * pushing each column's error (w_i - q_i) / U_ii onto the columns not yet
+ * rounded, with the updates applied lazily in blocks of 128 columns.
+ * Sources: "GPTQ: Accurate Post-Training Quantization for Generative
+ * Pre-trained Transformers", breakdown by FDE Interviews -- section 01 "The
+ * paper in one minute" and the figure "Quantize a column, correct the rest",
+ * steps 1-4; "[Paper Review] GPTQ ..." (nubint), "Proposed method".
+ *
+ * Conventions for every entry point
+ *  - Pointers named d_* / H / X / U / W / outputs are DEVICE pointers (HIP
+ *    global memory of the current device); `cfg` and `info_host` style
+ *    arguments are host pointers where stated. The caller owns every buffer;
+ *    the library never allocates or frees device memory. Scratch memory comes
+ *    only from `workspace`, sized with gptq_workspace_bytes().
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *    call validates its arguments on the host, enqueues its kernels on
+ *    `stream` and returns; outputs are valid once the stream has synchronized.
+ *    Calls on distinct streams with distinct buffers are independent.
+ *  - Matrices are row-major with a leading dimension (elements) `ld*`.
+ *  - Errors: host-detectable problems (null pointer, size <= 0, bad ld,
+ *    unsupported option, workspace too small) return a status synchronously and
+ *    enqueue nothing. A failed launch returns GPTQ_ERR_HIP. Numerical failure
+ *    (H_d not positive definite) is reported through the device int `*info`.
+ *    No C++ exception crosses this interface.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = 1,
+  GPTQ_ERR_WORKSPACE = 2,
+  GPTQ_ERR_HIP = 3,
+  GPTQ_ERR_UNSUPPORTED = 4
+} gptq_status_t;
+
+typedef enum { GPTQ_GRID_ASYM_MINMAX = 0, GPTQ_GRID_TERNARY = 1 } gptq_grid_t;
+
+typedef enum { GPTQ_F16 = 0, GPTQ_F32 = 1, GPTQ_F64 = 2 } gptq_dtype_t;
+
+/* Quantizer configuration (host struct).
+ *  bits       2, 3, 4 or 8 (ternary: 2; codes 0, 1, 2 stand for -s, 0, +s).
+ *  grid       gptq_grid_t. Asymmetric min-max: lo = min(min v, 0),
+ *             hi = max(max v, 0) (both 0 -> -1, +1), s = (hi - lo) / (2^b - 1),
+ *             z = rint(-lo / s). Ternary: s = max|v| (0 -> 1), z = 1.
+ *             The pages only name "3/4-bit grids", grouping, 2-bit and ternary
+ *             levels (nubint review, "Key findings"); this fit is the reading
+ *             the library implements.
+ *  group_size 0 = one grid per output row, fitted on the original row;
+ *             32, 64 or 128 = a grid per group of columns, fitted at the group's
+ *             first column on the current (error-updated) weights;
+ *             k * 128 = the same, for groups spanning k blocks.
+ *  block_size must be 128 (the lazy-update block of the figure's step 4). */
+typedef struct {
+  int32_t bits;
+  int32_t grid;
+  int32_t group_size;
+  int32_t block_size;
+} gptq_qcfg_t;
+
+/* Which call a workspace is sized for. */
+enum { GPTQ_WS_ACCUMULATE_HESSIAN = 0, GPTQ_WS_PREPARE_HINV = 1, GPTQ_WS_QUANTIZE_LAYER = 2 };
+
+/* ABI version of this header (incremented on incompatible changes). */
+int32_t gptq_abi_version(void);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* gptq_status_string(int32_t status);
+
+/* Bytes of workspace the named call needs for these sizes (0 = none).
+ *  which = GPTQ_WS_ACCUMULATE_HESSIAN: uses d and n (tokens per call); a
+ *          smaller workspace (even NULL / 0) is accepted and only lowers the
+ *          token-split parallelism.
+ *  which = GPTQ_WS_PREPARE_HINV: uses d.
+ *  which = GPTQ_WS_QUANTIZE_LAYER: uses m, d and cfg (host pointer, may be NULL
+ *          for the defaults). */
+size_t gptq_workspace_bytes(int32_t which, int64_t m, int64_t d, int64_t n, const gptq_qcfg_t* cfg);
+
+/* Hessian accumulation: H[i][j] = (accumulate ? H[i][j] : 0) + 2 sum_t X[t][i] X[t][j]
+ * for i >= j (lower triangle; the strictly upper triangle is not touched).
+ * FDE breakdown, section 01: the curvature of the layer-wise least-squares
+ * problem is H = 2XX^T from the calibration inputs (X = [d, N] there; here X is
+ * token-major [N, d], the same matrix).
+ *  H        device, [d][ldh], h_dtype GPTQ_F64 (recommended) or GPTQ_F32.
+ *  X        device, fp16, token-major [n][ldx]; 16-byte aligned, ldx % 8 == 0.
+ *  d        features, d % 32 == 0. n tokens in this call, n >= 0 (n = 0 with
+ *           accumulate = 0 zeroes the lower triangle).
+ *  Products are exact fp16 x fp16 -> fp32 on the matrix cores; partial sums are
+ *  carried in fp32 with their rounding error folded back every 1024 tokens and
+ *  combined in fp64, so H is accurate to a fraction of an fp32 ulp.
+ *  Call it once per chunk of tokens with accumulate = 1 after the first. */
+gptq_status_t gptq_accumulate_hessian(void* H, int32_t h_dtype, int64_t d, int64_t ldh,
+                                      const void* X, int64_t n, int64_t ldx, int32_t accumulate,
+                                      void* workspace, size_t ws_bytes, void* stream);
+
+/* Inverse-Hessian factor: U (upper, row-major, zeros below the diagonal) with
+ * U^T U = (H + lambda I)^-1, lambda = damp * mean(diag H).
+ * FDE breakdown, figure step 2: U = chol(H^-1); section 01: the rows of the
+ * inverse Hessian come from a Cholesky decomposition for numerical stability;
+ * nubint review, "Proposed method": Cholesky reformulation and dampening.
+ * Computed in fp64 as U = J inv(L) J with L L^T = J H_d J (J the reversal
+ * permutation), the same unique factor in half the flops of
+ * Cholesky -> inverse -> Cholesky.
+ *  H        device [d][ldh] (lower triangle read), h_dtype GPTQ_F32 | GPTQ_F64.
+ *  U        device [d][ldu], u_dtype GPTQ_F32 | GPTQ_F64. May not alias H.
+ *  damp     relative dampening (0.01 in the pages' defaults), >= 0.
+ *  info     device int32: 0 = success, k > 0 = the reversed leading minor of
+ *           order k is not positive definite (U is then undefined).
+ *  lambda_out device double, may be NULL: receives lambda.
+ *  workspace gptq_workspace_bytes(GPTQ_WS_PREPARE_HINV, 0, d, 0, NULL) bytes. */
+gptq_status_t gptq_prepare_hinv(const void* H, int32_t h_dtype, int64_t d, int64_t ldh, double damp,
+                                void* U, int32_t u_dtype, int64_t ldu, int32_t* info,
+                                double* lambda_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Column-by-column quantization in natural order with lazy 128-column blocks.
+ * FDE breakdown, figure steps 1-4, for column i: round w_i to the grid (q_i);
+ * err = (w_i - q_i) / U_ii; W[:, i+1:] -= err x U[i, i+1:]; updates applied in
+ * blocks of 128 columns. Section 01: one column order shared by every row.
+ *  W        device [m][ldw], w_dtype GPTQ_F16 | GPTQ_F32. Read only (the library
+ *           works on an fp32 copy in the workspace).
+ *  U        device [d][ldu] upper factor from gptq_prepare_hinv, u_dtype
+ *           GPTQ_F32 | GPTQ_F64 (GPTQ_F64 is converted to fp32 per block).
+ *  cfg      host pointer to the quantizer configuration.
+ *  qcodes   device uint32 [m][d * bits / 32]: row-wise LSB-first bitstream,
+ *           code j at bits [j*bits, (j+1)*bits) of its row. d * bits % 32 == 0.
+ *  scales   device float [m][ngroups], ngroups = group_size ? d / group_size : 1.
+ *  zeros    device uint8 [m][ngroups] (integer zero points).
+ *  W_hat    device float [m][d] = s * (code - z), may be NULL.
+ *  err_sq   device float [m]: sum over the row of err^2 / 2 (the optimal-brain-
+ *           surgeon loss increments), may be NULL.
+ *  Sizes: m >= 1, d % 128 == 0 when group_size > 128, else d % 32 == 0. */
+gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int64_t d, int64_t ldw,
+                                  const void* U, int32_t u_dtype, int64_t ldu, const gptq_qcfg_t* cfg,
+                                  uint32_t* qcodes, float* scales, uint8_t* zeros, float* W_hat,
+                                  float* err_sq, void* workspace, size_t ws_bytes, void* stream);
+
+/* Bit packing of integer codes (one byte per code) into the row-wise LSB-first
+ * bitstream gptq_quantize_layer writes (which packs in its own epilogue).
+ * FDE breakdown, section 01: the output is 3-bit (or 4-bit) weights that an
+ * inference kernel dequantizes on the fly; the layout is this library's.
+ *  codes    device uint8 [m][d], values < 2^bits.   out device uint32 [m][d*bits/32].
+ *  bits     2, 3, 4 or 8; d * bits % 32 == 0. */
+gptq_status_t gptq_pack_codes(const uint8_t* codes, int64_t m, int64_t d, int32_t bits,
+                              uint32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

@@ -1,0 +1,59 @@
+// Shared device/host helpers of the gfx950 GPTQ library (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gptq.h"
+
+namespace gptq {
+
+typedef _Float16 half_t;
+typedef half_t half8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef double double4v __attribute__((ext_vector_type(4)));
+
+#define GPTQ_LDS __attribute__((address_space(3)))
+
+// Returns GPTQ_ERR_HIP from the enclosing function when a launch failed.
+#define GPTQ_CHECK_LAUNCH()                         \
+  do {                                              \
+    if (hipGetLastError() != hipSuccess) return GPTQ_ERR_HIP; \
+  } while (0)
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Logical block index that gives each of the 8 XCDs a contiguous range of
+// logical ids (the dispatcher hands consecutive workgroups to XCDs round-robin),
+// so that neighbouring tiles share one L2. A bijection for any grid size.
+__device__ inline int xcd_logical_block(int id, int nblocks) {
+  const int nx = 8;
+  int x = id % nx, local = id / nx;
+  int base = nblocks / nx, rem = nblocks % nx;
+  return x * base + (x < rem ? x : rem) + local;
+}
+
+
+// Entry points of the individual kernel families (implemented in the .hip files).
+gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const half_t* X, int64_t n,
+                           int64_t ldx, int accumulate, void* ws, size_t ws_bytes, hipStream_t st);
+size_t syrk_workspace_bytes(int64_t d, int64_t n);
+
+gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, double damp, void* U,
+                            int u_f64, int64_t ldu, int32_t* info, double* lambda_out, void* ws,
+                            size_t ws_bytes, hipStream_t st);
+size_t chain_workspace_bytes(int64_t d);
+
+gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int64_t ldw, const void* U,
+                            int u_f64, int64_t ldu, const gptq_qcfg_t& cfg, uint32_t* qcodes,
+                            float* scales, uint8_t* zeros, float* W_hat, float* err_sq, void* ws,
+                            size_t ws_bytes, hipStream_t st);
+size_t quant_workspace_bytes(int64_t m, int64_t d, const gptq_qcfg_t& cfg);
+
+gptq_status_t pack_enqueue(const uint8_t* codes, int64_t ldc, int64_t m, int64_t d, int bits,
+                           uint32_t* out, hipStream_t st);
+
+}  // namespace gptq

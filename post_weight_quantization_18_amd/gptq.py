@@ -1,0 +1,213 @@
+"""Python binding of libgptq_mi355x.so (argument marshalling only).
+
+Every step of the hot path runs in the library's HIP kernels. PyTorch supplies
+device memory (torch.empty on a ROCm device) and the current stream. There is
+no CPU fallback: if the library is missing, loading raises.
+
+Entry points (same names as include/gptq.h):
+    accumulate_hessian(H, X, accumulate)      H (+)= 2 X^T X, lower triangle
+    prepare_hinv(H, damp)                      U = chol_upper((H + lambda I)^-1)
+    quantize_layer(W, U, bits, group_size, grid)
+    pack_codes(codes, bits)
+and quantize(W, x_chunks, ...) which runs the three stages of one layer.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgptq_mi355x.so")
+
+GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP, GPTQ_ERR_UNSUPPORTED = range(5)
+GPTQ_F16, GPTQ_F32, GPTQ_F64 = 0, 1, 2
+GPTQ_GRID_ASYM_MINMAX, GPTQ_GRID_TERNARY = 0, 1
+WS_ACCUMULATE_HESSIAN, WS_PREPARE_HINV, WS_QUANTIZE_LAYER = 0, 1, 2
+
+EXPORTED = ["gptq_abi_version", "gptq_status_string", "gptq_workspace_bytes", "gptq_accumulate_hessian",
+            "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack_codes"]
+
+
+class QCfg(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("grid", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("block_size", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library (raises when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m post_weight_quantization_18_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.gptq_abi_version.restype = i32
+    lib.gptq_abi_version.argtypes = []
+    lib.gptq_status_string.restype = ctypes.c_char_p
+    lib.gptq_status_string.argtypes = [i32]
+    lib.gptq_workspace_bytes.restype = sz
+    lib.gptq_workspace_bytes.argtypes = [i32, i64, i64, i64, ctypes.POINTER(QCfg)]
+    lib.gptq_accumulate_hessian.restype = i32
+    lib.gptq_accumulate_hessian.argtypes = [vp, i32, i64, i64, vp, i64, i64, i32, vp, sz, vp]
+    lib.gptq_prepare_hinv.restype = i32
+    lib.gptq_prepare_hinv.argtypes = [vp, i32, i64, i64, ctypes.c_double, vp, i32, i64, vp, vp, vp, sz, vp]
+    lib.gptq_quantize_layer.restype = i32
+    lib.gptq_quantize_layer.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, ctypes.POINTER(QCfg), vp, vp, vp, vp,
+                                        vp, vp, sz, vp]
+    lib.gptq_pack_codes.restype = i32
+    lib.gptq_pack_codes.argtypes = [vp, i64, i64, i32, vp, vp]
+    _lib = lib
+    return lib
+
+
+class GPTQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = load_library().gptq_status_string(status).decode()
+        super().__init__(f"{what}: {msg}")
+        self.status = status
+
+
+def _check(status: int, what: str):
+    if status != GPTQ_OK:
+        raise GPTQError(status, what)
+
+
+_DT = {torch.float16: GPTQ_F16, torch.float32: GPTQ_F32, torch.float64: GPTQ_F64}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(t, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a tensor on a ROCm device")
+
+
+def _rowmajor_ld(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a row-major 2-D tensor (unit column stride)")
+    return t.stride(0)
+
+
+def make_qcfg(bits: int, group_size: int = 0, grid: str = "asym", block_size: int = 128) -> QCfg:
+    g = {"asym": GPTQ_GRID_ASYM_MINMAX, "ternary": GPTQ_GRID_TERNARY}[grid]
+    return QCfg(bits, g, group_size, block_size)
+
+
+def workspace_bytes(which: int, m: int = 0, d: int = 0, n: int = 0, cfg: QCfg | None = None) -> int:
+    lib = load_library()
+    return int(lib.gptq_workspace_bytes(which, m, d, n, ctypes.byref(cfg) if cfg is not None else None))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def accumulate_hessian(H: torch.Tensor, X: torch.Tensor, accumulate: bool = True, workspace=None):
+    """H[i][j] (+)= 2 sum_t X[t][i] X[t][j] for i >= j. H fp64 or fp32 [d, d]; X fp16 [n, d]."""
+    lib = load_library()
+    _need_cuda(H, "H")
+    _need_cuda(X, "X")
+    if X.dtype != torch.float16:
+        raise ValueError("X must be fp16")
+    d = H.shape[0]
+    ldh = _rowmajor_ld(H, "H")
+    ldx = _rowmajor_ld(X, "X") if X.shape[0] > 0 else d
+    n = X.shape[0]
+    ws = _workspace(workspace_bytes(WS_ACCUMULATE_HESSIAN, 0, d, n), H.device, workspace)
+    nbytes = 0 if ws is None else ws.numel()
+    _check(lib.gptq_accumulate_hessian(_ptr(H), _DT[H.dtype], d, ldh, _ptr(X) if n else ctypes.c_void_p(0), n, ldx,
+                                       int(bool(accumulate)), _ptr(ws), nbytes, _stream(H.device)),
+           "gptq_accumulate_hessian")
+    return H
+
+
+def prepare_hinv(H: torch.Tensor, damp: float = 0.01, U: torch.Tensor | None = None,
+                 u_dtype: torch.dtype = torch.float32, workspace=None):
+    """Returns (U, info, lam): U upper [d, d] with U^T U = (H + lam I)^-1, info a
+    1-element int32 device tensor (0 = ok), lam a 1-element fp64 device tensor."""
+    lib = load_library()
+    _need_cuda(H, "H")
+    d = H.shape[0]
+    if U is None:
+        U = torch.empty(d, d, dtype=u_dtype, device=H.device)
+    info = torch.empty(1, dtype=torch.int32, device=H.device)
+    lam = torch.empty(1, dtype=torch.float64, device=H.device)
+    ws = _workspace(workspace_bytes(WS_PREPARE_HINV, 0, d), H.device, workspace)
+    _check(lib.gptq_prepare_hinv(_ptr(H), _DT[H.dtype], d, _rowmajor_ld(H, "H"), float(damp), _ptr(U), _DT[U.dtype],
+                                 _rowmajor_ld(U, "U"), _ptr(info), _ptr(lam), _ptr(ws), ws.numel(),
+                                 _stream(H.device)), "gptq_prepare_hinv")
+    return U, info, lam
+
+
+def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, group_size: int = 0, grid: str = "asym",
+                   block_size: int = 128, want_w_hat: bool = True, workspace=None, out=None):
+    """Returns dict(qcodes uint32 [m, d*bits/32] (as int32 storage), scales fp32 [m, ng],
+    zeros uint8 [m, ng], w_hat fp32 [m, d] or None, err_sq fp32 [m])."""
+    lib = load_library()
+    _need_cuda(W, "W")
+    _need_cuda(U, "U")
+    m, d = W.shape
+    cfg = make_qcfg(bits, group_size, grid, block_size)
+    ng = d // group_size if group_size else 1
+    dev = W.device
+    if out is None:
+        out = {
+            "qcodes": torch.empty(m, d * bits // 32, dtype=torch.int32, device=dev),
+            "scales": torch.empty(m, ng, dtype=torch.float32, device=dev),
+            "zeros": torch.empty(m, ng, dtype=torch.uint8, device=dev),
+            "w_hat": torch.empty(m, d, dtype=torch.float32, device=dev) if want_w_hat else None,
+            "err_sq": torch.empty(m, dtype=torch.float32, device=dev),
+        }
+    ws = _workspace(workspace_bytes(WS_QUANTIZE_LAYER, m, d, 0, cfg), dev, workspace)
+    _check(lib.gptq_quantize_layer(_ptr(W), _DT[W.dtype], m, d, _rowmajor_ld(W, "W"), _ptr(U), _DT[U.dtype],
+                                   _rowmajor_ld(U, "U"), ctypes.byref(cfg), _ptr(out["qcodes"]), _ptr(out["scales"]),
+                                   _ptr(out["zeros"]), _ptr(out["w_hat"]), _ptr(out["err_sq"]), _ptr(ws), ws.numel(),
+                                   _stream(dev)), "gptq_quantize_layer")
+    return out
+
+
+def pack_codes(codes: torch.Tensor, bits: int) -> torch.Tensor:
+    """codes uint8 [m, d] -> int32 storage of the uint32 bitstream [m, d*bits/32]."""
+    lib = load_library()
+    _need_cuda(codes, "codes")
+    if codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError("codes must be contiguous uint8")
+    m, d = codes.shape
+    out = torch.empty(m, d * bits // 32, dtype=torch.int32, device=codes.device)
+    _check(lib.gptq_pack_codes(_ptr(codes), m, d, bits, _ptr(out), _stream(codes.device)), "gptq_pack_codes")
+    return out
+
+
+def quantize(W: torch.Tensor, x_chunks, bits: int, group_size: int = 0, grid: str = "asym", damp: float = 0.01,
+             h_dtype: torch.dtype = torch.float64, u_dtype: torch.dtype = torch.float32, want_w_hat: bool = True):
+    """The whole hot path of one layer: H over the chunks, U, then the column loop.
+    Returns (result dict, H, U, lam). Raises when H + lam I is not positive definite."""
+    if isinstance(x_chunks, torch.Tensor):
+        x_chunks = [x_chunks]
+    d = W.shape[1]
+    H = torch.empty(d, d, dtype=h_dtype, device=W.device)
+    for i, xc in enumerate(x_chunks):
+        accumulate_hessian(H, xc, accumulate=i > 0)
+    U, info, lam = prepare_hinv(H, damp, u_dtype=u_dtype)
+    bad = int(info.item())
+    if bad:
+        raise GPTQError(GPTQ_ERR_INVALID_ARG, f"H + lambda I is not positive definite (reversed minor {bad})")
+    res = quantize_layer(W, U, bits, group_size, grid, want_w_hat=want_w_hat)
+    return res, H, U, lam
