@@ -17,9 +17,14 @@
 //          inverts it (the inverse serves the panel solve and the inverse pass);
 //   trsm:  panel rows A21 <- A21 L11^-T (row-local, fp64 FMA);
 //   syrk:  A22 <- A22 - A21 A21^T on lower 64x64 tiles (v_mfma_f64_16x16x4).
-// Blocked inverse from the last block column to the first:
-//   A21 <- -(L22^-1 A21) L11^-1 (trmm on the matrix cores, then a row-local
-//   product), A11 <- L11^-1.
+// Triangular inverse by recursive doubling: the 64x64 diagonal blocks hold
+// their inverses from potf2; then for s = 64, 128, ... every pair of adjacent
+// inverted s-blocks [[A, 0], [B, C]] is merged with
+//   N21 = -C^-1 (B A^-1)
+// as two batched fp64-MFMA launches per level (log2(d/64) levels), instead of
+// a sequential sweep over the d/64 block columns.
+#include <utility>
+
 #include "common.h"
 
 namespace gptq {
@@ -31,9 +36,16 @@ constexpr int NB = 64;  // panel width
 struct ChainWs {
   double* A;     // d x d
   double* Dinv;  // d x NB: inverse of each diagonal block (rows k0..k0+63)
-  double* T;     // d x NB scratch panel
+  double* T;     // d x smax: B A^-1 of the pairs being merged
   double* lam;   // 1
 };
+
+// Largest merge size s (a power-of-two multiple of NB with s < d).
+int64_t chain_smax(int64_t d) {
+  int64_t s = NB;
+  while (2 * s < d) s *= 2;
+  return s;
+}
 
 ChainWs chain_ws(void* ws, int64_t d) {
   ChainWs w;
@@ -43,7 +55,7 @@ ChainWs chain_ws(void* ws, int64_t d) {
   w.Dinv = (double*)p;
   p += (size_t)d * NB * sizeof(double);
   w.T = (double*)p;
-  p += (size_t)d * NB * sizeof(double);
+  p += (size_t)d * chain_smax(d) * sizeof(double);
   w.lam = (double*)p;
   return w;
 }
@@ -106,87 +118,155 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const void* H, int h
   }
 }
 
-// Factor the diagonal block at k0 in LDS (lower Cholesky), write L11 back with a
-// zero upper triangle, and write L11^-1 to Dinv. info <- first failing order.
-__global__ __launch_bounds__(256) void potf2_kernel(double* A, int64_t d, int64_t k0, double* Dinv,
-                                                    int32_t* info) {
+// Factor the diagonal block at k0 (lower Cholesky) with one wave: lane r holds
+// row r in registers; column values are exchanged through LDS broadcasts.
+// Writes L11 back with a zero upper triangle and L11^-1 to Dinv.
+// info <- first failing order (k0 + c + 1).
+struct Potf2Row {
+  double v[NB];
+};
+
+template <int C>
+__device__ __forceinline__ void potf2_step(Potf2Row& row, double* col, int lane, bool& failed, int nb, int64_t k0,
+                                           int32_t* info) {
+  // broadcast column C of the current matrix
+  col[lane] = row.v[C];
+  __syncthreads();
+  double piv = col[C];
+  if (!(piv > 0.0)) {
+    if (!failed && C < nb && lane == 0 && *info == 0) *info = (int32_t)(k0 + C + 1);
+    failed = true;
+    piv = 1.0;
+  }
+  piv = sqrt(piv);
+  const double l = row.v[C] / piv;  // L[lane][C] for lane > C
+  __syncthreads();
+  col[lane] = l;
+  __syncthreads();
+  if (lane == C) row.v[C] = piv;
+  if (lane > C) row.v[C] = l;
+  // trailing update of this lane's row; entries right of the diagonal are
+  // never read and are zeroed on write-back
+#pragma unroll
+  for (int k = C + 1; k < NB; ++k) row.v[k] = fma(-l, col[k], row.v[k]);
+}
+
+template <int... Cs>
+__device__ __forceinline__ void potf2_all(std::integer_sequence<int, Cs...>, Potf2Row& row, double* col, int lane,
+                                          bool& failed, int nb, int64_t k0, int32_t* info) {
+  (potf2_step<Cs>(row, col, lane, failed, nb, k0, info), ...);
+}
+
+// Li = L^-1, lane j owns column j: Li[r][j] = -(sum_{k<r} L[r][k] Li[k][j]) / L[r][r]
+// (Li[k][j] = 0 for k < j, so every lane runs the same loop).
+template <int R>
+__device__ __forceinline__ void inv_step(Potf2Row& li, const double (*L)[NB + 1], int lane) {
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+#pragma unroll
+  for (int k = 0; k + 3 < R; k += 4) {
+    s0 = fma(L[R][k], li.v[k], s0);
+    s1 = fma(L[R][k + 1], li.v[k + 1], s1);
+    s2 = fma(L[R][k + 2], li.v[k + 2], s2);
+    s3 = fma(L[R][k + 3], li.v[k + 3], s3);
+  }
+#pragma unroll
+  for (int k = R & ~3; k < R; ++k) s0 = fma(L[R][k], li.v[k], s0);
+  const double diag = L[R][R];
+  li.v[R] = (lane == R) ? 1.0 / diag : (lane < R ? -((s0 + s1) + (s2 + s3)) / diag : 0.0);
+}
+
+template <int... Rs>
+__device__ __forceinline__ void inv_all(std::integer_sequence<int, Rs...>, Potf2Row& li, const double (*L)[NB + 1],
+                                        int lane) {
+  (inv_step<Rs>(li, L, lane), ...);
+}
+
+__global__ __launch_bounds__(64) void potf2_kernel(double* A, int64_t d, int64_t k0, double* Dinv,
+                                                   int32_t* info) {
   __shared__ double L[NB][NB + 1];
-  __shared__ double Li[NB][NB + 1];
+  __shared__ double col[NB];
   const int nb = (int)((d - k0) < NB ? (d - k0) : NB);
-  const int tid = threadIdx.x;
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    int r = idx / NB, c = idx % NB;
+  const int lane = threadIdx.x;
+  for (int idx = lane; idx < NB * NB; idx += 64) {
+    const int r = idx / NB, c = idx % NB;
     double v = 0.0;
     if (r < nb && c < nb && c <= r) v = A[(k0 + r) * d + k0 + c];
     if (r >= nb && r == c) v = 1.0;  // identity padding beyond the matrix
     L[r][c] = v;
   }
   __syncthreads();
-  __shared__ int bad;
-  if (tid == 0) bad = 0;
-  for (int c = 0; c < NB; ++c) {
-    __syncthreads();
-    if (tid == 0) {
-      double p = L[c][c];
-      if (!(p > 0.0)) {
-        if (!bad && c < nb) {
-          bad = 1;
-          if (*info == 0) *info = (int32_t)(k0 + c + 1);
-        }
-        p = 1.0;
-      }
-      L[c][c] = sqrt(p);
-    }
-    __syncthreads();
-    const double piv = L[c][c];
-    for (int r = c + 1 + tid; r < NB; r += 256) L[r][c] /= piv;
-    __syncthreads();
-    // trailing update of the lower part: (r, cc) with c < cc <= r
-    const int m = NB - c - 1;
-    for (int idx = tid; idx < m * m; idx += 256) {
-      int r = c + 1 + idx / m, cc = c + 1 + idx % m;
-      if (cc <= r) L[r][cc] -= L[r][c] * L[cc][c];
-    }
-  }
+  Potf2Row row;
+#pragma unroll
+  for (int c = 0; c < NB; ++c) row.v[c] = L[lane][c];
+  bool failed = false;
+  potf2_all(std::make_integer_sequence<int, NB>{}, row, col, lane, failed, nb, k0, info);
   __syncthreads();
-  // inverse of the lower-triangular L: column cc by forward substitution.
-  if (tid < NB) {
-    const int cc = tid;
-    for (int r = 0; r < NB; ++r) Li[r][cc] = 0.0;
-    Li[cc][cc] = 1.0 / L[cc][cc];
-    for (int r = cc + 1; r < NB; ++r) {
-      double s = 0.0;
-      for (int k = cc; k < r; ++k) s += L[r][k] * Li[k][cc];
-      Li[r][cc] = -s / L[r][r];
-    }
-  }
+#pragma unroll
+  for (int c = 0; c < NB; ++c) L[lane][c] = (c <= lane) ? row.v[c] : 0.0;
   __syncthreads();
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    int r = idx / NB, c = idx % NB;
-    if (r < nb && c < nb) A[(k0 + r) * d + k0 + c] = (c <= r) ? L[r][c] : 0.0;
-    if (k0 + r < d) Dinv[(k0 + r) * NB + c] = (c <= r && r < nb && c < nb) ? Li[r][c] : 0.0;
+  Potf2Row li;
+  inv_all(std::make_integer_sequence<int, NB>{}, li, L, lane);
+  for (int idx = lane; idx < NB * NB; idx += 64) {
+    const int r = idx / NB, c = idx % NB;
+    if (r < nb && c < nb) A[(k0 + r) * d + k0 + c] = L[r][c];
+  }
+  // Dinv row r, column lane = li.v[r] (lane owns column lane)
+#pragma unroll
+  for (int r = 0; r < NB; ++r)
+    if (k0 + r < d) Dinv[(k0 + r) * NB + lane] = (r < nb && lane < nb && lane <= r) ? li.v[r] : 0.0;
+}
+
+// One 64x64 fp64 MFMA tile step: acc[2][2] += As[rows][k..k+15] * Bs[k..k+15][cols]
+// for a wave's 32x32 sub-tile. As is [64][KT+1] (row, k); Bs is [KT][64+1] (k, col).
+// v_mfma_f64_16x16x4: A lane l holds A[l%16][l/16], B lane l holds B[l/16][l%16],
+// D lane l, reg r holds D[l/16 + 4r][l%16].
+template <int KT>
+__device__ inline void mfma_f64_block(const double (*As)[KT + 1], const double (*Bs)[64 + 1], int wr, int wc,
+                                      int lane, double4v (&acc)[2][2]) {
+  const int li = lane & 15, lk = lane >> 4;
+#pragma unroll
+  for (int k = 0; k < KT; k += 4) {
+    double av[2], bv[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) av[a] = As[wr + a * 16 + li][k + lk];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) bv[b] = Bs[k + lk][wc + b * 16 + li];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
   }
 }
 
-// Rows i >= k0+NB: A[i][k0:k0+NB] <- A[i][k0:k0+NB] * Linv^T, i.e.
-// x'[c] = sum_{c' <= c} x[c'] Linv[c][c']. 64 rows per workgroup.
+// Rows i >= k0+NB: A[i][k0:k0+NB] <- A[i][k0:k0+NB] Linv^T (fp64 MFMA, K = 64).
 __global__ __launch_bounds__(256) void trsm_rows_kernel(double* A, int64_t d, int64_t k0, const double* Dinv) {
-  __shared__ double Li[NB][NB + 1];
-  __shared__ double X[NB][NB + 1];
-  const int tid = threadIdx.x;
-  const int64_t r0 = k0 + NB + (int64_t)blockIdx.x * NB;
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    int r = idx / NB, c = idx % NB;
-    Li[r][c] = Dinv[(k0 + r) * NB + c];
-    X[r][c] = (r0 + r < d) ? A[(r0 + r) * d + k0 + c] : 0.0;
+  __shared__ double Xs[64][NB + 1];
+  __shared__ double Bs[NB][64 + 1];  // Bs[k][j] = Linv[j][k]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t r0 = k0 + NB + (int64_t)blockIdx.x * 64;
+  for (int idx = tid; idx < 64 * NB; idx += 256) {
+    const int r = idx / NB, c = idx % NB;
+    Xs[r][c] = (r0 + r < d) ? A[(r0 + r) * d + k0 + c] : 0.0;
+    Bs[c][r] = Dinv[(k0 + r) * NB + c];
   }
   __syncthreads();
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    int r = idx / NB, c = idx % NB;
-    double s = 0.0;
-    for (int k = 0; k <= c; ++k) s += X[r][k] * Li[c][k];
-    if (r0 + r < d) A[(r0 + r) * d + k0 + c] = s;
-  }
+  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+  double4v acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = (double4v){0.0, 0.0, 0.0, 0.0};
+  mfma_f64_block<NB>(Xs, Bs, wr, wc, lane, acc);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t i = r0 + wr + a * 16 + (lane >> 4) + 4 * r;
+        const int c = wc + b * 16 + (lane & 15);
+        if (i < d) A[i * d + k0 + c] = acc[a][b][r];
+      }
 }
 
 // C[i][j] -= sum_k P[i][k] P[j][k] for the lower 64x64 tiles of the trailing
@@ -194,42 +274,27 @@ __global__ __launch_bounds__(256) void trsm_rows_kernel(double* A, int64_t d, in
 // Diagonal tiles update only j <= i so the upper triangle stays zero.
 __global__ __launch_bounds__(256) void syrk_f64_kernel(double* A, int64_t d, int64_t k0, int64_t c0) {
   __shared__ double Pi[64][NB + 1];
-  __shared__ double Pj[64][NB + 1];
-  // lower tile index -> (ti, tj), tj <= ti
+  __shared__ double Bs[NB][64 + 1];  // Bs[k][j] = P[j][k]
   const int t = blockIdx.x;
   int ti = (int)((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
   while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
   while (ti * (ti + 1) / 2 > t) --ti;
   const int tj = t - ti * (ti + 1) / 2;
   const int64_t i0 = c0 + (int64_t)ti * 64, j0 = c0 + (int64_t)tj * 64;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int idx = tid; idx < 64 * NB; idx += 256) {
-    int r = idx / NB, c = idx % NB;
+    const int r = idx / NB, c = idx % NB;
     Pi[r][c] = (i0 + r < d) ? A[(i0 + r) * d + k0 + c] : 0.0;
-    Pj[r][c] = (j0 + r < d) ? A[(j0 + r) * d + k0 + c] : 0.0;
+    Bs[c][r] = (j0 + r < d) ? A[(j0 + r) * d + k0 + c] : 0.0;
   }
   __syncthreads();
-  const int lane = tid & 63, w = tid >> 6;
-  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;  // wave sub-tile
+  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
   double4v acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = (double4v){0.0, 0.0, 0.0, 0.0};
-  const int li = lane & 15, lk = lane >> 4;
-#pragma unroll 4
-  for (int k = 0; k < NB; k += 4) {
-    double av[2], bv[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) av[a] = Pi[wr + a * 16 + li][k + lk];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) bv[b] = Pj[wc + b * 16 + li][k + lk];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
-  }
-  // D[i][j]: i = lane/16 + 4*r, j = lane%16
+  mfma_f64_block<NB>(Pi, Bs, wr, wc, lane, acc);
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -242,14 +307,41 @@ __global__ __launch_bounds__(256) void syrk_f64_kernel(double* A, int64_t d, int
       }
 }
 
-// T[i][c] = sum_{c' in [c0, i]} A[i][c'] A[c'][k0 + c] for i >= c0 = k0 + NB:
-// (L22^-1, already inverted in place and lower) x (the L21 panel).
-// One 64-row tile per workgroup; fp64 MFMA with 64-wide K chunks via LDS.
-__global__ __launch_bounds__(256) void trmm_kernel(const double* A, int64_t d, int64_t k0, double* T) {
-  __shared__ double Ai[64][64 + 1];
-  __shared__ double Bp[64][NB + 1];
-  const int64_t c0 = k0 + NB;
-  const int64_t i0 = c0 + (int64_t)blockIdx.x * 64;
+// Every diagonal NB-block of A <- its inverse (lower, zero upper).
+__global__ __launch_bounds__(256) void put_diag_inverse_kernel(double* A, int64_t d, const double* Dinv) {
+  const int64_t k0 = (int64_t)blockIdx.x * NB;
+  const int nb = (int)((d - k0) < NB ? (d - k0) : NB);
+  for (int idx = threadIdx.x; idx < nb * nb; idx += 256) {
+    const int r = idx / nb, c = idx % nb;
+    A[(k0 + r) * d + k0 + c] = Dinv[(k0 + r) * NB + c];
+  }
+}
+
+// Merge step of the triangular inverse at block size s. Pair p covers
+// rows/cols [a0, a0 + 2s): Ainv = A[a0:c0, a0:c0], Cinv = A[c0:c1, c0:c1] (both
+// already inverted, lower), B = A[c0:c1, a0:c0] (still the factor L).
+//   MODE 0: T[r][col - a0] = sum_{k in [col tile, c0)} B[r][k] Ainv[k][col]
+//   MODE 1: A[r][col] = -sum_{k in [c0, r tile end)} Cinv[r][k] T[k][col - a0]
+// grid: x = column tile in [a0, c0), y = row tile in [c0, c1), z = pair.
+template <int MODE>
+__global__ __launch_bounds__(256) void merge_kernel(double* A, int64_t d, double* T, int64_t ldt, int64_t s) {
+  constexpr int KT = 32;
+  __shared__ double As[64][KT + 1];
+  __shared__ double Bs[KT][64 + 1];
+  const int64_t a0 = (int64_t)blockIdx.z * 2 * s, c0 = a0 + s;
+  int64_t c1 = a0 + 2 * s;
+  if (c1 > d) c1 = d;
+  const int64_t r0 = c0 + (int64_t)blockIdx.y * 64;
+  const int64_t col0 = a0 + (int64_t)blockIdx.x * 64;
+  if (c0 >= d || r0 >= c1) return;  // uniform per workgroup
+  int64_t kb, ke;
+  if (MODE == 0) {
+    kb = col0;
+    ke = c0;
+  } else {
+    kb = c0;
+    ke = r0 + 64 < c1 ? r0 + 64 : c1;
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
   double4v acc[2][2];
@@ -257,30 +349,34 @@ __global__ __launch_bounds__(256) void trmm_kernel(const double* A, int64_t d, i
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = (double4v){0.0, 0.0, 0.0, 0.0};
-  const int li = lane & 15, lk = lane >> 4;
-  int64_t kend = i0 + 64;
-  if (kend > d) kend = d;
-  for (int64_t kc = c0; kc < kend; kc += 64) {
+  // each thread stages 8 elements of the A tile (64 x KT) and 8 of the B tile (KT x 64)
+  double pa[8], pb[8];
+  auto fetch = [&](int64_t k) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e;
+      const int ar = idx / KT, ac = idx % KT;
+      const int64_t gr = r0 + ar, gk = k + ac;
+      pa[e] = (gr < c1 && gk < ke) ? A[gr * d + gk] : 0.0;
+      const int br = idx / 64, bc = idx % 64;
+      const int64_t bk = k + br, gc = col0 + bc;
+      double v = 0.0;
+      if (bk < ke && gc < c0) v = (MODE == 0) ? A[bk * d + gc] : T[bk * ldt + (gc - a0)];
+      pb[e] = v;
+    }
+  };
+  fetch(kb);
+  for (int64_t k = kb; k < ke; k += KT) {
     __syncthreads();
-    for (int idx = tid; idx < 64 * 64; idx += 256) {
-      int r = idx / 64, c = idx % 64;
-      Ai[r][c] = (i0 + r < d && kc + c < d) ? A[(i0 + r) * d + kc + c] : 0.0;
-      Bp[r][c] = (kc + r < d) ? A[(kc + r) * d + k0 + c] : 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e;
+      As[idx / KT][idx % KT] = pa[e];
+      Bs[idx / 64][idx % 64] = pb[e];
     }
     __syncthreads();
-#pragma unroll 4
-    for (int k = 0; k < 64; k += 4) {
-      double av[2], bv[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) av[a] = Ai[wr + a * 16 + li][k + lk];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) bv[b] = Bp[k + lk][wc + b * 16 + li];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
-    }
+    if (k + KT < ke) fetch(k + KT);
+    mfma_f64_block<KT>(As, Bs, wr, wc, lane, acc);
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -288,40 +384,15 @@ __global__ __launch_bounds__(256) void trmm_kernel(const double* A, int64_t d, i
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t i = i0 + wr + a * 16 + (lane >> 4) + 4 * r;
-        const int c = wc + b * 16 + (lane & 15);
-        if (i < d) T[i * NB + c] = acc[a][b][r];
+        const int64_t i = r0 + wr + a * 16 + (lane >> 4) + 4 * r;
+        const int64_t j = col0 + wc + b * 16 + (lane & 15);
+        if (i < c1 && j < c0) {
+          if (MODE == 0)
+            T[i * ldt + (j - a0)] = acc[a][b][r];
+          else
+            A[i * d + j] = -acc[a][b][r];
+        }
       }
-}
-
-// Rows i >= k0+NB: A[i][k0+c] = -sum_{c' >= c} T[i][c'] Linv[c'][c].
-__global__ __launch_bounds__(256) void trsm2_rows_kernel(double* A, int64_t d, int64_t k0, const double* T,
-                                                         const double* Dinv) {
-  __shared__ double Li[NB][NB + 1];
-  __shared__ double X[NB][NB + 1];
-  const int tid = threadIdx.x;
-  const int64_t r0 = k0 + NB + (int64_t)blockIdx.x * NB;
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    int r = idx / NB, c = idx % NB;
-    Li[r][c] = Dinv[(k0 + r) * NB + c];
-    X[r][c] = (r0 + r < d) ? T[(r0 + r) * NB + c] : 0.0;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    int r = idx / NB, c = idx % NB;
-    double s = 0.0;
-    for (int k = c; k < NB; ++k) s += X[r][k] * Li[k][c];
-    if (r0 + r < d) A[(r0 + r) * d + k0 + c] = -s;
-  }
-}
-
-// A11 <- L11^-1 (lower, zero upper).
-__global__ __launch_bounds__(256) void put_diag_inverse_kernel(double* A, int64_t d, int64_t k0, const double* Dinv) {
-  const int nb = (int)((d - k0) < NB ? (d - k0) : NB);
-  for (int idx = threadIdx.x; idx < nb * nb; idx += 256) {
-    int r = idx / nb, c = idx % nb;
-    A[(k0 + r) * d + k0 + c] = Dinv[(k0 + r) * NB + c];
-  }
 }
 
 // U[i][j] = A[d-1-i][d-1-j] for j >= i, else 0 (A lower holds L^-1).
@@ -339,12 +410,14 @@ __global__ __launch_bounds__(256) void store_u_kernel(const double* A, int64_t d
 }  // namespace
 
 size_t chain_workspace_bytes(int64_t d) {
-  return (size_t)d * d * sizeof(double) + 2 * (size_t)d * NB * sizeof(double) + 256;
+  return (size_t)d * d * sizeof(double) + (size_t)d * NB * sizeof(double) +
+         (size_t)d * chain_smax(d) * sizeof(double) + 256;
 }
 
 gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, double damp, void* U, int u_f64,
                             int64_t ldu, int32_t* info, double* lambda_out, void* ws, size_t ws_bytes,
                             hipStream_t st) {
+  (void)ws_bytes;
   ChainWs w = chain_ws(ws, d);
   hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(256), 0, st, H, h_f64, d, ldh, damp, w.lam, lambda_out, info);
   GPTQ_CHECK_LAUNCH();
@@ -355,7 +428,7 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
   const int64_t nblk = ceil_div(d, NB);
   for (int64_t k = 0; k < nblk; ++k) {
     const int64_t k0 = k * NB;
-    hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(256), 0, st, w.A, d, k0, w.Dinv, info);
+    hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(64), 0, st, w.A, d, k0, w.Dinv, info);
     GPTQ_CHECK_LAUNCH();
     const int64_t rest = d - k0 - NB;
     if (rest <= 0) break;
@@ -366,18 +439,16 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
                        k0 + NB);
     GPTQ_CHECK_LAUNCH();
   }
-  for (int64_t k = nblk - 1; k >= 0; --k) {
-    const int64_t k0 = k * NB;
-    const int64_t rest = d - k0 - NB;
-    if (rest > 0) {
-      const int64_t rb = ceil_div(rest, 64);
-      hipLaunchKernelGGL(trmm_kernel, dim3((unsigned)rb), dim3(256), 0, st, (const double*)w.A, d, k0, w.T);
-      GPTQ_CHECK_LAUNCH();
-      hipLaunchKernelGGL(trsm2_rows_kernel, dim3((unsigned)rb), dim3(256), 0, st, w.A, d, k0, (const double*)w.T,
-                         (const double*)w.Dinv);
-      GPTQ_CHECK_LAUNCH();
-    }
-    hipLaunchKernelGGL(put_diag_inverse_kernel, dim3(1), dim3(256), 0, st, w.A, d, k0, (const double*)w.Dinv);
+  hipLaunchKernelGGL(put_diag_inverse_kernel, dim3((unsigned)nblk), dim3(256), 0, st, w.A, d,
+                     (const double*)w.Dinv);
+  GPTQ_CHECK_LAUNCH();
+  const int64_t ldt = chain_smax(d);
+  for (int64_t s = NB; s < d; s *= 2) {
+    const int64_t pairs = ceil_div(d, 2 * s);
+    dim3 grid((unsigned)(s / 64), (unsigned)(s / 64), (unsigned)pairs);
+    hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, st, w.A, d, w.T, ldt, s);
+    GPTQ_CHECK_LAUNCH();
+    hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, st, w.A, d, w.T, ldt, s);
     GPTQ_CHECK_LAUNCH();
   }
   hipLaunchKernelGGL(store_u_kernel, dim3((unsigned)ceil_div(d, 256) < 64 ? (unsigned)ceil_div(d, 256) : 64u,

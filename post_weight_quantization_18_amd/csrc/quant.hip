@@ -26,12 +26,13 @@ namespace gptq {
 namespace {
 
 constexpr int BLK = 128;
-constexpr int CL_THREADS = 64;
+constexpr int CL_THREADS = 256;  // 64 rows x 4 lanes
 
 struct QuantWs {
   float* Wk;       // m x d working weights
   float* E;        // m x BLK block errors
   uint8_t* codes;  // m x d
+  float* rdiag;    // d: 1 / U_jj
   float* U32;      // d x d (only when U is fp64)
 };
 
@@ -46,6 +47,8 @@ QuantWs quant_ws(void* ws, int64_t m, int64_t d, int u_f64) {
   p += align256((size_t)m * BLK * sizeof(float));
   w.codes = (uint8_t*)p;
   p += align256((size_t)m * d);
+  w.rdiag = (float*)p;
+  p += align256((size_t)d * sizeof(float));
   w.U32 = u_f64 ? (float*)p : nullptr;
   return w;
 }
@@ -107,9 +110,15 @@ __global__ void f64_to_f32_kernel(const double* U, int64_t d, int64_t ldu, float
     U32[i * d + j] = (float)U[i * ldu + j];
 }
 
+__global__ void rdiag_kernel(const float* U, int64_t d, int64_t ldu, float* rdiag) {
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < d; j += (int64_t)gridDim.x * blockDim.x)
+    rdiag[j] = 1.0f / U[j * ldu + j];
+}
+
 struct ColArgs {
   float* Wk;
   const float* U;
+  const float* rdiag;
   int64_t ldu, m, d, j0;
   int bw;          // block width (multiple of 32, <= 128)
   int ternary;
@@ -124,72 +133,110 @@ struct ColArgs {
   int first;
 };
 
-// Per-lane state of the column loop: the row's 128-column tile, its grid and
-// the packed codes. Every index below is a compile-time constant, so the
-// arrays stay in registers.
-struct RowState {
-  float w[BLK];
-  uint32_t cw[BLK / 4];
+// Layout of the column loop: four lanes (a DPP quad) share one row; lane
+// group g = lane % 4 owns the block's columns [32g, 32g + 32) in registers.
+// At step i the owner group o = i / 32 rounds column i and forms the error e,
+// a quad broadcast hands e to the other three lanes, and every lane updates
+// its 32 columns with the strictly upper part of row i of the block's U, read
+// from LDS (zeros on and below the diagonal make the update branch-free).
+constexpr int QL = 4;            // lanes per row
+constexpr int CPL = BLK / QL;    // columns per lane (32)
+constexpr int UGS = CPL + 4;     // LDS stride of a lane group's slice (floats):
+                                 // the quad's four slices start in different banks
+constexpr int UPITCH = QL * UGS; // LDS row pitch of the U block (floats)
+
+struct LaneState {
+  float w[CPL];         // the lane's 32 working weights, then its 32 errors
+  uint32_t cw[CPL / 4]; // its 32 codes, one byte each
   float s, rs, zf, esum;
 };
 
-template <int I, int K>
-struct Fma {  // w[k] -= e * U[I][k] for k = K .. BLK-1
-  __device__ __forceinline__ static void run(RowState& st, float e, const float* urow) {
-    st.w[K] = fmaf(-e, urow[K], st.w[K]);
-    Fma<I, K + 1>::run(st, e, urow);
-  }
-};
-template <int I>
-struct Fma<I, BLK> {
-  __device__ __forceinline__ static void run(RowState&, float, const float*) {}
-};
+template <int O>
+__device__ __forceinline__ float quad_bcast(float v) {
+  // quad_perm(O, O, O, O)
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), O | (O << 2) | (O << 4) | (O << 6),
+                                                            0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor1(float v) {  // quad_perm(1, 0, 3, 2)
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 1 | (0 << 2) | (3 << 4) | (2 << 6),
+                                                            0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {  // quad_perm(2, 3, 0, 1)
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 2 | (3 << 2) | (0 << 4) | (1 << 6),
+                                                            0xF, 0xF, false));
+}
 
-template <int I, int K, int END>
+template <int K, int END>
 struct MinMax {  // running min/max over w[K .. END-1]
-  __device__ __forceinline__ static void run(const RowState& st, float& lo, float& hi) {
+  __device__ __forceinline__ static void run(const LaneState& st, float& lo, float& hi) {
     lo = fminf(lo, st.w[K]);
     hi = fmaxf(hi, st.w[K]);
-    MinMax<I, K + 1, END>::run(st, lo, hi);
+    MinMax<K + 1, END>::run(st, lo, hi);
   }
 };
-template <int I, int END>
-struct MinMax<I, END, END> {
-  __device__ __forceinline__ static void run(const RowState&, float&, float&) {}
+template <int END>
+struct MinMax<END, END> {
+  __device__ __forceinline__ static void run(const LaneState&, float&, float&) {}
 };
 
 template <int G, int I>
-struct Step {
-  __device__ __forceinline__ static void run(RowState& st, const ColArgs& a, int64_t r, const float (*Us)[BLK],
-                                             const float* rdiag) {
-    if (I < a.bw) {
-      if constexpr (G > 0 && I % (G > 0 ? G : 1) == 0) {
-        float lo = st.w[I], hi = st.w[I];
-        MinMax<I, I + 1, I + (G > 0 ? G : 1)>::run(st, lo, hi);
-        GridFit g = fit_grid(lo, hi, a.ternary, a.maxq);
-        const int64_t gi = (a.j0 + I) / (G > 0 ? G : 1);
-        a.scales[r * a.ngroups + gi] = g.s;
-        a.zeros[r * a.ngroups + gi] = (uint8_t)g.z;
-        st.s = g.s;
-        st.zf = g.z;
-        st.rs = 1.0f / g.s;
-      }
-      const float p = st.w[I] * st.rs + st.zf;
-      const float c = fminf(fmaxf(rintf(p), 0.0f), a.maxq);
-      const float qv = st.s * (c - st.zf);
-      const float e = (st.w[I] - qv) * rdiag[I];
-      st.esum += e * e;
-      st.cw[I >> 2] |= ((uint32_t)c) << (8 * (I & 3));
-      st.w[I] = e;  // the register now carries the error of column I
-      Fma<I, I + 1>::run(st, e, Us[I]);
+__device__ __forceinline__ void col_step(LaneState& st, const ColArgs& a, int64_t r, int g, const float* urow,
+                                         float rd) {
+  constexpr int O = I / CPL, LI = I % CPL;
+  if constexpr (G > 0 && I % (G > 0 ? G : 1) == 0) {
+    // grid of the group [I, I + G): this lane's part, then across the lanes of the group
+    float lo = st.w[LI], hi = st.w[LI];
+    MinMax<LI + 1, (G < CPL ? LI + G : CPL)>::run(st, lo, hi);
+    if constexpr (G >= 2 * CPL) {
+      lo = fminf(lo, quad_xor1(lo));
+      hi = fmaxf(hi, quad_xor1(hi));
+    }
+    if constexpr (G >= 4 * CPL) {
+      lo = fminf(lo, quad_xor2(lo));
+      hi = fmaxf(hi, quad_xor2(hi));
+    }
+    GridFit gf = fit_grid(lo, hi, a.ternary, a.maxq);
+    if (g == O) {
+      const int64_t gi = (a.j0 + I) / (G > 0 ? G : 1);
+      a.scales[r * a.ngroups + gi] = gf.s;
+      a.zeros[r * a.ngroups + gi] = (uint8_t)gf.z;
+    }
+    // groups of 32 or 64 start inside other lanes' ranges too: only the
+    // lanes of this group adopt the new grid
+    const bool mine = (G >= 4 * CPL) || (G == 2 * CPL ? (g >> 1) == (O >> 1) : g == O);
+    if (mine) {
+      st.s = gf.s;
+      st.zf = gf.z;
+      st.rs = 1.0f / gf.s;
     }
   }
-};
+  const bool owner = (g == O);
+  const float wv = st.w[LI];
+  const float p = wv * st.rs + st.zf;
+  const float c = fminf(fmaxf(rintf(p), 0.0f), a.maxq);
+  const float qv = st.s * (c - st.zf);
+  const float e_own = (wv - qv) * rd;
+  if (owner) {
+    st.esum += e_own * e_own;
+    st.cw[LI >> 2] |= ((uint32_t)c) << (8 * (LI & 3));
+    st.w[LI] = e_own;  // the register now carries the error of column I
+  }
+  const float e = quad_bcast<O>(e_own);
+  const float4* u4 = (const float4*)(urow + g * UGS);
+#pragma unroll
+  for (int k4 = 0; k4 < CPL / 4; ++k4) {
+    const float4 u = u4[k4];
+    st.w[4 * k4] = fmaf(-e, u.x, st.w[4 * k4]);
+    st.w[4 * k4 + 1] = fmaf(-e, u.y, st.w[4 * k4 + 1]);
+    st.w[4 * k4 + 2] = fmaf(-e, u.z, st.w[4 * k4 + 2]);
+    st.w[4 * k4 + 3] = fmaf(-e, u.w, st.w[4 * k4 + 3]);
+  }
+}
 
 template <int G, int... Is>
-__device__ __forceinline__ void run_steps(std::integer_sequence<int, Is...>, RowState& st, const ColArgs& a,
-                                          int64_t r, const float (*Us)[BLK], const float* rdiag) {
-  (Step<G, Is>::run(st, a, r, Us, rdiag), ...);
+__device__ __forceinline__ void run_steps(std::integer_sequence<int, Is...>, LaneState& st, const ColArgs& a,
+                                          int64_t r, int g, const float (*Us)[UPITCH], const float* rdiag, int bw) {
+  ((Is < bw ? col_step<G, Is>(st, a, r, g, Us[Is], rdiag[Is]) : void()), ...);
 }
 
 // G = 0: one grid per row (already fitted); G = 32, 64, 128: refit at every
@@ -197,77 +244,98 @@ __device__ __forceinline__ void run_steps(std::integer_sequence<int, Is...>, Row
 // group's first block from the current working weights.
 template <int G>
 __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
-  __shared__ float Us[BLK][BLK];
+  __shared__ __attribute__((aligned(16))) float Us[BLK][UPITCH];
   __shared__ float rdiag[BLK];
   const int tid = threadIdx.x;
   const int bw = a.bw;
+  // strictly upper part of the block's U (zeros on and below the diagonal)
   for (int idx = tid; idx < BLK * BLK / 4; idx += CL_THREADS) {
     const int i = idx / (BLK / 4), k4 = (idx % (BLK / 4)) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (i < bw && k4 < bw) v = *(const float4*)(a.U + (a.j0 + i) * a.ldu + a.j0 + k4);
-    *(float4*)&Us[i][k4] = v;
+    if (k4 + 0 <= i) v.x = 0.f;
+    if (k4 + 1 <= i) v.y = 0.f;
+    if (k4 + 2 <= i) v.z = 0.f;
+    if (k4 + 3 <= i) v.w = 0.f;
+    *(float4*)&Us[i][(k4 / CPL) * UGS + k4 % CPL] = v;
   }
-  __syncthreads();
-  for (int i = tid; i < BLK; i += CL_THREADS) rdiag[i] = i < bw ? 1.0f / Us[i][i] : 0.0f;
+  for (int i = tid; i < BLK; i += CL_THREADS) rdiag[i] = i < bw ? a.rdiag[a.j0 + i] : 0.0f;
   __syncthreads();
 
-  const int64_t r = (int64_t)blockIdx.x * CL_THREADS + tid;
-  if (r >= a.m) return;  // no barrier follows
+  const int g = tid % QL;
+  const int64_t r = (int64_t)blockIdx.x * (CL_THREADS / QL) + tid / QL;
+  const bool live = r < a.m;
+  const int64_t rr = live ? r : a.m - 1;  // dead lanes mirror the last row and store nothing
 
-  RowState st;
-  const float* wrow = a.Wk + r * a.d + a.j0;
+  LaneState st;
+  const float* wrow = a.Wk + rr * a.d + a.j0 + g * CPL;
+  const bool cols_ok = g * CPL < bw;
 #pragma unroll
-  for (int k = 0; k < BLK; k += 4) {
+  for (int k = 0; k < CPL; k += 4) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (k < bw) v = *(const float4*)(wrow + k);
+    if (cols_ok) v = *(const float4*)(wrow + k);
     st.w[k] = v.x;
     st.w[k + 1] = v.y;
     st.w[k + 2] = v.z;
     st.w[k + 3] = v.w;
   }
 #pragma unroll
-  for (int k = 0; k < BLK / 4; ++k) st.cw[k] = 0;
+  for (int k = 0; k < CPL / 4; ++k) st.cw[k] = 0;
   st.esum = 0.0f;
   st.s = 1.0f;
   st.rs = 1.0f;
   st.zf = 0.0f;
   if (G == 0) {
-    st.s = a.scales[r];
-    st.zf = (float)a.zeros[r];
+    st.s = a.scales[rr];
+    st.zf = (float)a.zeros[rr];
     st.rs = 1.0f / st.s;
   } else if (G < 0) {
     const int gi = (int)(a.j0 / a.group);
     if (a.j0 % a.group == 0) {
+      // the group spans whole blocks: each lane scans a quarter of it
       float vmin = INFINITY, vmax = -INFINITY;
-      const float* grow = a.Wk + r * a.d + a.j0;
-      for (int k = 0; k < a.group; k += 4) {
+      const int part = a.group / QL;
+      const float* grow = a.Wk + rr * a.d + a.j0 + g * part;
+      for (int k = 0; k < part; k += 4) {
         float4 v = *(const float4*)(grow + k);
         vmin = fminf(fminf(fminf(vmin, v.x), fminf(v.y, v.z)), v.w);
         vmax = fmaxf(fmaxf(fmaxf(vmax, v.x), fmaxf(v.y, v.z)), v.w);
       }
-      GridFit g = fit_grid(vmin, vmax, a.ternary, a.maxq);
-      a.scales[r * a.ngroups + gi] = g.s;
-      a.zeros[r * a.ngroups + gi] = (uint8_t)g.z;
-      st.s = g.s;
-      st.zf = g.z;
+      vmin = fminf(vmin, quad_xor1(vmin));
+      vmax = fmaxf(vmax, quad_xor1(vmax));
+      vmin = fminf(vmin, quad_xor2(vmin));
+      vmax = fmaxf(vmax, quad_xor2(vmax));
+      GridFit gf = fit_grid(vmin, vmax, a.ternary, a.maxq);
+      if (g == 0 && live) {
+        a.scales[r * a.ngroups + gi] = gf.s;
+        a.zeros[r * a.ngroups + gi] = (uint8_t)gf.z;
+      }
+      st.s = gf.s;
+      st.zf = gf.z;
     } else {
-      st.s = a.scales[r * a.ngroups + gi];
-      st.zf = (float)a.zeros[r * a.ngroups + gi];
+      st.s = a.scales[rr * a.ngroups + gi];
+      st.zf = (float)a.zeros[rr * a.ngroups + gi];
     }
     st.rs = 1.0f / st.s;
   }
 
-  run_steps<G>(std::make_integer_sequence<int, BLK>{}, st, a, r, Us, rdiag);
+  if (live) run_steps<G>(std::make_integer_sequence<int, BLK>{}, st, a, r, g, Us, rdiag, bw);
 
-  float* erow = a.E + r * BLK;
+  if (live) {
+    float* erow = a.E + r * BLK + g * CPL;
+    if (cols_ok) {
 #pragma unroll
-  for (int k = 0; k < BLK; k += 4)
-    if (k < bw) *(float4*)(erow + k) = make_float4(st.w[k], st.w[k + 1], st.w[k + 2], st.w[k + 3]);
-  uint8_t* crow = a.codes + r * a.d + a.j0;
-#pragma unroll
-  for (int k = 0; k < BLK / 4; k += 4)
-    if (4 * k < bw) *(uint4*)(crow + 4 * k) = make_uint4(st.cw[k], st.cw[k + 1], st.cw[k + 2], st.cw[k + 3]);
-  if (a.err_sq) a.err_sq[r] = (a.first ? 0.0f : a.err_sq[r]) + 0.5f * st.esum;
+      for (int k = 0; k < CPL; k += 4) *(float4*)(erow + k) = make_float4(st.w[k], st.w[k + 1], st.w[k + 2], st.w[k + 3]);
+      uint8_t* crow = a.codes + r * a.d + a.j0 + g * CPL;
+      *(uint4*)(crow) = make_uint4(st.cw[0], st.cw[1], st.cw[2], st.cw[3]);
+      *(uint4*)(crow + 16) = make_uint4(st.cw[4], st.cw[5], st.cw[6], st.cw[7]);
+    }
+  }
+  // row sum of err^2 / 2 over the quad
+  float es = st.esum;
+  es += quad_xor1(es);
+  es += quad_xor2(es);
+  if (live && g == 0 && a.err_sq) a.err_sq[r] = (a.first ? 0.0f : a.err_sq[r]) + 0.5f * es;
 }
 
 // W[r][c] -= sum_{k < bw} E[r][k] U[j0 + k][c] for c >= j1.
@@ -363,7 +431,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* codes, int64_t
 
 template <int G>
 gptq_status_t launch_colloop(const ColArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(colloop_kernel<G>, dim3((unsigned)ceil_div(a.m, CL_THREADS)), dim3(CL_THREADS), 0, st, a);
+  hipLaunchKernelGGL(colloop_kernel<G>, dim3((unsigned)ceil_div(a.m, CL_THREADS / 4)), dim3(CL_THREADS), 0, st, a);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
@@ -373,7 +441,7 @@ gptq_status_t launch_colloop(const ColArgs& a, hipStream_t st) {
 size_t quant_workspace_bytes(int64_t m, int64_t d, const gptq_qcfg_t& cfg) {
   (void)cfg;
   size_t b = align256((size_t)m * d * sizeof(float)) + align256((size_t)m * BLK * sizeof(float)) +
-             align256((size_t)m * d);
+             align256((size_t)m * d) + align256((size_t)d * sizeof(float));
   return b;
 }
 
@@ -399,6 +467,8 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
     U32 = w.U32;
     ldu32 = d;
   }
+  hipLaunchKernelGGL(rdiag_kernel, dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, st, U32, d, ldu32, w.rdiag);
+  GPTQ_CHECK_LAUNCH();
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)ceil_div(m, 4)), dim3(256), 0, st, W, w_f32, m, d, ldw, w.Wk,
                      group == 0 ? 1 : 0, ternary, maxq, scales, zeros);
   GPTQ_CHECK_LAUNCH();
@@ -406,6 +476,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   ColArgs a;
   a.Wk = w.Wk;
   a.U = U32;
+  a.rdiag = w.rdiag;
   a.ldu = ldu32;
   a.m = m;
   a.d = d;

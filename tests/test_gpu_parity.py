@@ -103,7 +103,8 @@ def test_hessian_accumulate_and_empty():
 # inverse-Hessian factor
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("d,u_dtype", [(768, torch.float64), (768, torch.float32), (96, torch.float64),
-                                       (200 // 8 * 8, torch.float64)])
+                                       (200, torch.float64), (1000, torch.float64), (4160, torch.float64),
+                                       (64, torch.float64), (40, torch.float64)])
 def test_chain_parity(d, u_dtype):
     say(f"[case] chain d={d} u_dtype={u_dtype}")
     rng = np.random.default_rng(d)
