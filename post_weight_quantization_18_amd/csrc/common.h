@@ -17,6 +17,7 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 typedef double double4v __attribute__((ext_vector_type(4)));
 
 #define GPTQ_LDS __attribute__((address_space(3)))
+#define GPTQ_GLB __attribute__((address_space(1)))
 
 // Returns GPTQ_ERR_HIP from the enclosing function when a launch failed.
 #define GPTQ_CHECK_LAUNCH()                         \

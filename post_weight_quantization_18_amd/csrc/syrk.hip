@@ -5,13 +5,17 @@
 //
 // Design (MI355X):
 //  * Output tiles of 256 (i) x 128 (j) cover the lower triangle only; a
-//    workgroup of 4 waves owns one tile for one token range (split-K when the
-//    tile count alone cannot fill 256 CUs).
-//  * X is token-major fp16; each 64-token stage of the I- and J-feature columns
-//    is copied row-major into LDS with 16-byte loads, and the MFMA operands
-//    (8 consecutive tokens per lane) come out of LDS with the gfx950
-//    transpose read ds_read_b64_tr_b16, so no transpose pass over X is needed.
-//  * v_mfma_f32_32x32x16_f16: fp16 x fp16 products are exact in fp32.
+//    workgroup of 8 waves (64 x 64 each, two per SIMD) owns one tile for one
+//    token range (split-K when the tile count alone cannot fill 256 CUs).
+//  * X is token-major fp16. Each 64-token stage of the tile's I and J feature
+//    columns is copied into LDS by the gfx950 direct global->LDS DMA
+//    (global_load_lds_dwordx4: lane l lands at bytes [16l, 16l+16) of its
+//    wave's 1 KB), row-major with an XOR swizzle of the 16-byte chunks chosen
+//    on the global side, into a 3-deep ring, so two stages are in flight while
+//    the matrix cores work and no registers hold staged data.
+//  * The MFMA operands (8 consecutive tokens per lane) come out of LDS with the
+//    transpose read ds_read_b64_tr_b16; the swizzle keeps these reads free of
+//    bank conflicts. v_mfma_f32_32x32x16_f16: fp16 x fp16 products are exact.
 //  * Accuracy: every 1024 tokens the fp32 accumulators are folded into a
 //    second fp32 register (Fast2Sum) and the rounding error is put back into the
 //    MFMA accumulator, so the partial sum is carried to ~2^-48 relative; the
@@ -26,11 +30,18 @@ namespace {
 constexpr int TI = 256;          // tile rows (i features)
 constexpr int TJ = 128;          // tile cols (j features)
 constexpr int KS = 64;           // tokens per LDS stage
-constexpr int PI = TI + 32;      // LDS row pitch (halves) of the I tile: 576 B
-constexpr int PJ = TJ + 32;      // LDS row pitch (halves) of the J tile: 320 B
 constexpr int FOLD = 16;         // stages between error folds (1024 tokens)
-constexpr int NT = 256;          // threads per workgroup
-constexpr int STAGE_HALVES = KS * PI + KS * PJ;
+constexpr int NT = 512;          // threads per workgroup (8 waves)
+constexpr int NBUF = 3;          // LDS ring depth
+
+// Source of the DMA for rows past the token range or features past d: every
+// lane issues the same number of loads per stage, so vmcnt waits stay exact.
+__device__ const uint4 kZero16[1] = {{0u, 0u, 0u, 0u}};
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt(N), no wait on exp/lgkm.
+constexpr int WAIT_VM0 = 0x0F70;
+constexpr int WAIT_VM4 = 0x0F74;
+constexpr int WAIT_VM6 = 0x0F76;
 
 struct SyrkArgs {
   const half_t* X;
@@ -56,18 +67,38 @@ __device__ inline short4v tr_read(const half_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((GPTQ_LDS short4v*)(p));
 }
 
-__device__ inline half8 frag(const half_t* tile, int pitch, int lane_off) {
-  // lane_off already holds (8*(g>>1) + e) * pitch + 16*(g&1) + 4*q; the second
-  // read takes the next 4 tokens.
-  short4v lo = tr_read(tile + lane_off);
-  short4v hi = tr_read(tile + lane_off + 4 * pitch);
-  // whole-vector reinterpretation: the two 64-bit results are the 8 halves
+// 8 consecutive tokens of one feature per lane: two transpose reads 4 rows apart.
+__device__ inline half8 frag(const half_t* p, int pitch) {
+  short4v lo = tr_read(p);
+  short4v hi = tr_read(p + 4 * pitch);
   short8v both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(half8, both);
 }
 
+// LDS chunk (16 B) position of feature chunk c in row r: c ^ 4 (r mod 4).
+__device__ inline int swz(int row, int chunk) { return chunk ^ (4 * (row & 3)); }
+
+// global -> LDS DMA of 16 bytes per lane: lane l writes LDS bytes
+// [lds + 16 l, lds + 16 l + 16). Issued through asm so that the compiler does
+// not insert its conservative "wait for every LDS DMA" before unrelated LDS
+// reads; the kernel waits on vmcnt itself. The instruction has no register
+// result, and M0 is set and consumed inside the same asm block.
+__device__ inline void dma16(const void* src, const half_t* lds) {
+  // wave-uniform by construction (it depends on the wave index only)
+  const uint32_t lds_off = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GPTQ_LDS const void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(src)
+               : "memory", "m0");
+}
+
+__device__ inline void lds_barrier() {
+  // LDS writes of this wave are complete; the asm keeps the compiler from
+  // moving memory operations across the barrier.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
-  __shared__ __attribute__((aligned(16))) half_t lds[2 * STAGE_HALVES];
+  // ring of NBUF stages; stage buffer b holds the I tile then the J tile
+  __shared__ __attribute__((aligned(1024))) half_t ring[NBUF * KS * (TI + TJ)];
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int split = logical / a.ntiles;
@@ -83,59 +114,59 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   const int nstages = tok1 > tok0 ? (int)((tok1 - tok0 + KS - 1) / KS) : 0;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wi = w >> 1, wj = w & 1;
+  const int wi = w >> 1, wj = w & 1;  // wave tile: rows 64 wi .. +63, cols 64 wj .. +63
   const bool j_in_i = (J0 >= I0) && (J0 < I0 + TI);
 
-  // ---- global -> register staging map ----
-  // I tile: 64 rows x 32 chunks of 8 halves; thread: chunk tid%32, rows tid/32 + 8r.
-  // J tile: 64 rows x 16 chunks; thread: chunk tid%16, rows tid/16 + 16r.
-  const int ci = tid & 31, ri = tid >> 5;
-  const int cj = tid & 15, rj = tid >> 4;
-  const int64_t fi = I0 + 8 * ci, fj = J0 + 8 * cj;
-  const bool fi_ok = fi < a.d, fj_ok = (!j_in_i) && (fj < a.d);
-
-  uint4 pa[8], pb[4];
-  auto load_stage = [&](int64_t k0) {
+  // ---- DMA of one stage (tokens t0 .. t0+63) into (bI, bJ) ----
+  // I tile: wave w, instruction e covers rows 8w + 2e + {0, 1} (1 KB); lane l
+  // takes row 8w + 2e + l/32 and LDS chunk position l%32, holding feature
+  // chunk (l%32) ^ 4 (row mod 4). The swizzle depends on e only through e&1.
+  // J tile: instruction e covers rows 8w + 4e + {0..3}; lane l takes row
+  // 8w + 4e + l/16 and position l%16 (swizzle independent of e).
+  auto issue = [&](int64_t t0, half_t* bI, half_t* bJ) {
+    const half_t* xs = a.X + t0 * a.ldx;
+    const int rows = (int)((tok1 - t0) < KS ? (tok1 - t0) : KS);
+    // recompute the per-lane parts here rather than keep 64-bit copies live
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
+    const int rI_ = lane_v >> 5, pI_ = lane_v & 31, rJ_ = lane_v >> 4, pJ_ = lane_v & 15;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      int64_t tok = k0 + ri + 8 * r;
-      if (fi_ok && tok < tok1)
-        pa[r] = *(const uint4*)(a.X + tok * a.ldx + fi);
-      else
-        pa[r] = make_uint4(0, 0, 0, 0);
+    for (int e = 0; e < 4; ++e) {
+      const int row = 8 * w + 2 * e + rI_;
+      const int c = pI_ ^ (4 * (row & 3));
+      const bool ok = (I0 + 8 * c < a.d) && row < rows;
+      const half_t* src = xs + (int64_t)row * a.ldx + I0 + 8 * c;
+      dma16(ok ? (const void*)src : (const void*)kZero16, bI + (8 * w + 2 * e) * TI);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int64_t tok = k0 + rj + 16 * r;
-      if (fj_ok && tok < tok1)
-        pb[r] = *(const uint4*)(a.X + tok * a.ldx + fj);
-      else
-        pb[r] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_stage = [&](half_t* buf) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) *(uint4*)(buf + (ri + 8 * r) * PI + 8 * ci) = pa[r];
     if (!j_in_i) {
-      half_t* bj_buf = buf + KS * PI;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) *(uint4*)(bj_buf + (rj + 16 * r) * PJ + 8 * cj) = pb[r];
+      for (int e = 0; e < 2; ++e) {
+        const int row = 8 * w + 4 * e + rJ_;
+        const int c = pJ_ ^ (4 * (row & 3));
+        const bool ok = (J0 + 8 * c < a.d) && row < rows;
+        const half_t* src = xs + (int64_t)row * a.ldx + J0 + 8 * c;
+        dma16(ok ? (const void*)src : (const void*)kZero16, bJ + (8 * w + 4 * e) * TJ);
+      }
     }
   };
 
-  // ---- per-lane transpose-read offsets ----
-  const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
-  const int tokoff = 8 * (g >> 1) + e;
-  const int featoff = 16 * (g & 1) + 4 * q;
-  // A operand: I features wi*128 + f*32 ; B operand: J features wj*64 + f*32.
-  const int a_off = tokoff * PI + wi * 128 + featoff;
-  const int b_pitch = j_in_i ? PI : PJ;
-  const int b_feat0 = j_in_i ? (int)(J0 - I0) : 0;
-  const int b_off = tokoff * b_pitch + b_feat0 + wj * 64 + featoff;
-
-  float16v acc[4][2], outer[4][2];
+  // ---- per-lane transpose-read offsets (halves) ----
+  // lane: g = lane/16, e = (lane/4)%4, q = lane%4 reads token row 8(g/2) + e and
+  // features base + 16(g%2) + 4q; the row's swizzle is 4e.
+  const int g = lane >> 4, e4 = (lane >> 2) & 3, q = lane & 3;
+  const int tokoff = 8 * (g >> 1) + e4;
+  const int sub = 2 * (g & 1) + (q >> 1), halfsel = 4 * (q & 1);
+  int offA[2], offB[2];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < 2; ++f) offA[f] = tokoff * TI + (swz(tokoff, wi * 8 + 4 * f + sub) << 3) + halfsel;
+  const int bpitch = j_in_i ? TI : TJ;
+  const int bchunk0 = j_in_i ? (int)((J0 - I0) / 8) : 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) offB[h] = tokoff * bpitch + (swz(tokoff, bchunk0 + wj * 8 + 4 * h + sub) << 3) + halfsel;
+
+  float16v acc[2][2], outer[2][2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -144,58 +175,88 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
         outer[f][h][r] = 0.0f;
       }
 
-  if (nstages > 0) {
-    load_stage(tok0);
-    store_stage(lds);
-  }
-  __syncthreads();
-
-  for (int s = 0; s < nstages; ++s) {
-    const bool more = s + 1 < nstages;
-    if (more) load_stage(tok0 + (int64_t)(s + 1) * KS);
-    const half_t* buf = lds + (s & 1) * STAGE_HALVES;
-    const half_t* bbuf = j_in_i ? buf : buf + KS * PI;
+  // B operand from bB (the I buffer itself on diagonal tiles): the two cases
+  // are separate code paths so every LDS read has one known LDS object.
+  auto compute_from = [&](const half_t* bI, const half_t* bB, int bp) {
+    // one 16-token slice ahead: the fragments of slice kk+1 are read while the
+    // matrix cores work on slice kk (scheduling barriers keep it to one slice,
+    // which bounds the registers the reads occupy)
+    half8 af[2][2], bf[2][2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) af[0][f] = frag(bI + offA[f], TI);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) bf[0][h] = frag(bB + offB[h], bp);
 #pragma unroll
     for (int kk = 0; kk < KS / 16; ++kk) {
-      half8 af[4], bf[2];
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk + 1 < KS / 16) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) af[f] = frag(buf, PI, a_off + kk * 16 * PI + f * 32);
+        for (int f = 0; f < 2; ++f) af[nxt][f] = frag(bI + offA[f] + (kk + 1) * 16 * TI, TI);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) bf[h] = frag(bbuf, b_pitch, b_off + kk * 16 * b_pitch + h * 32);
+        for (int h = 0; h < 2; ++h) bf[nxt][h] = frag(bB + offB[h] + (kk + 1) * 16 * bp, bp);
+      }
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          acc[f][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[f], bf[h], acc[f][h], 0, 0, 0);
-    }
-    if ((s + 1) % FOLD == 0) {
-      // Fast2Sum(outer, acc): outer <- fl(outer + acc), acc <- exact residual.
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float o = outer[f][h][r], c = acc[f][h][r];
-            float sum = o + c;
-            float z = sum - o;
-            acc[f][h][r] = c - z;
-            outer[f][h][r] = sum;
-          }
+          acc[f][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][f], bf[cur][h], acc[f][h], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) store_stage(lds + ((s + 1) & 1) * STAGE_HALVES);
-    __syncthreads();
+  };
+  auto compute = [&](const half_t* bI, const half_t* bJ) {
+    if (j_in_i)
+      compute_from(bI, bI, TI);
+    else
+      compute_from(bI, bJ, TJ);
+  };
+  auto fold = [&]() {
+    // Fast2Sum(outer, acc): outer <- fl(outer + acc), acc <- exact residual.
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float o = outer[f][h][r], c = acc[f][h][r];
+          float sum = o + c;
+          float z = sum - o;
+          acc[f][h][r] = c - z;
+          outer[f][h][r] = sum;
+        }
+  };
+  auto stage_i = [&](int b) { return ring + b * KS * (TI + TJ); };
+  auto stage_j = [&](int b) { return ring + b * KS * (TI + TJ) + KS * TI; };
+
+  if (nstages > 0) issue(tok0, stage_i(0), stage_j(0));
+  if (nstages > 1) issue(tok0 + KS, stage_i(1), stage_j(1));
+  int cur = 0;
+  for (int s = 0; s < nstages; ++s) {
+    // wait for this stage's DMA (the next stage's 4 or 6 loads per thread may
+    // stay in flight), barrier, refill the buffer freed by the previous stage,
+    // then run the matrix cores.
+    if (s + 1 >= nstages)
+      __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    else if (j_in_i)
+      __builtin_amdgcn_s_waitcnt(WAIT_VM4);
+    else
+      __builtin_amdgcn_s_waitcnt(WAIT_VM6);
+    lds_barrier();
+    const int nxt = cur == 0 ? NBUF - 1 : cur - 1;  // (cur + 2) mod 3
+    if (s + 2 < nstages) issue(tok0 + (int64_t)(s + 2) * KS, stage_i(nxt), stage_j(nxt));
+    compute(stage_i(cur), stage_j(cur));
+    if ((s + 1) % FOLD == 0) fold();
+    cur = cur == NBUF - 1 ? 0 : cur + 1;
   }
 
   // ---- epilogue ----
   const int hl = lane >> 5, col = lane & 31;
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int li = wi * 128 + f * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const int li = wi * 64 + f * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
         const int lj = wj * 64 + h * 32 + col;
         const double v = 2.0 * ((double)outer[f][h][r] + (double)acc[f][h][r]);
         if (a.direct) {
