@@ -27,12 +27,19 @@ namespace gptq {
 
 namespace {
 
-constexpr int TI = 256;          // tile rows (i features)
-constexpr int TJ = 128;          // tile cols (j features)
-constexpr int KS = 64;           // tokens per LDS stage
-constexpr int FOLD = 16;         // stages between error folds (1024 tokens)
-constexpr int NT = 512;          // threads per workgroup (8 waves)
-constexpr int NBUF = 3;          // LDS ring depth
+#ifndef GPTQ_SYRK_KS
+#define GPTQ_SYRK_KS 64
+#endif
+#ifndef GPTQ_SYRK_NBUF
+#define GPTQ_SYRK_NBUF 3
+#endif
+constexpr int TI = 256;            // tile rows (i features)
+constexpr int TJ = 128;            // tile cols (j features)
+constexpr int KS = GPTQ_SYRK_KS;   // tokens per LDS stage
+constexpr int FOLD = 1024 / KS;    // stages between error folds (1024 tokens)
+constexpr int NT = 512;            // threads per workgroup (8 waves)
+constexpr int NBUF = GPTQ_SYRK_NBUF;  // LDS ring depth
+
 
 // Source of the DMA for rows past the token range or features past d: every
 // lane issues the same number of loads per stage, so vmcnt waits stay exact.
@@ -53,14 +60,16 @@ struct SyrkArgs {
   int h_f64, accumulate, direct;
 };
 
-__device__ inline void tile_coords(int t, int& bi, int& bj) {
-  // tiles of I-block bi are bj = 0 .. 2*bi+1, so tile t lies in
-  // [bi(bi+1), (bi+1)(bi+2)).
+// Tile t -> (bi, bj): the tiles of I-block bi are bj = 0 .. 2 bi + 1, so t lies
+// in [bi (bi + 1), (bi + 1)(bi + 2)). Consecutive tiles (which one XCD runs
+// together) share their I columns. Tiles past d are empty.
+__device__ inline bool tile_coords(int t, int64_t d, int& bi, int& bj) {
   int b = (int)((sqrtf(4.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
   while ((b + 1) * (b + 2) <= t) ++b;
   while (b * (b + 1) > t) --b;
   bi = b;
   bj = t - b * (b + 1);
+  return (int64_t)bj * TJ < d;
 }
 
 __device__ inline short4v tr_read(const half_t* p) {
@@ -83,9 +92,7 @@ __device__ inline int swz(int row, int chunk) { return chunk ^ (4 * (row & 3)); 
 // not insert its conservative "wait for every LDS DMA" before unrelated LDS
 // reads; the kernel waits on vmcnt itself. The instruction has no register
 // result, and M0 is set and consumed inside the same asm block.
-__device__ inline void dma16(const void* src, const half_t* lds) {
-  // wave-uniform by construction (it depends on the wave index only)
-  const uint32_t lds_off = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GPTQ_LDS const void*)lds);
+__device__ inline void dma16(const void* src, uint32_t lds_off) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(src)
                : "memory", "m0");
 }
@@ -104,9 +111,8 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   const int split = logical / a.ntiles;
   const int t = logical - split * a.ntiles;
   int bi, bj;
-  tile_coords(t, bi, bj);
+  if (!tile_coords(t, a.d, bi, bj)) return;  // empty slot: the workgroup exits (uniform)
   const int64_t I0 = (int64_t)bi * TI, J0 = (int64_t)bj * TJ;
-  if (J0 >= a.d) return;  // whole workgroup exits together (uniform)
 
   const int64_t tok0 = (int64_t)split * a.tokens_per_split;
   int64_t tok1 = tok0 + a.tokens_per_split;
@@ -117,36 +123,52 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   const int wi = w >> 1, wj = w & 1;  // wave tile: rows 64 wi .. +63, cols 64 wj .. +63
   const bool j_in_i = (J0 >= I0) && (J0 < I0 + TI);
 
-  // ---- DMA of one stage (tokens t0 .. t0+63) into (bI, bJ) ----
+  // ---- DMA of one stage (tokens t0 .. t0+63) into ring buffer b ----
   // I tile: wave w, instruction e covers rows 8w + 2e + {0, 1} (1 KB); lane l
   // takes row 8w + 2e + l/32 and LDS chunk position l%32, holding feature
   // chunk (l%32) ^ 4 (row mod 4). The swizzle depends on e only through e&1.
   // J tile: instruction e covers rows 8w + 4e + {0..3}; lane l takes row
   // 8w + 4e + l/16 and position l%16 (swizzle independent of e).
-  auto issue = [&](int64_t t0, half_t* bI, half_t* bJ) {
-    const half_t* xs = a.X + t0 * a.ldx;
-    const int rows = (int)((tok1 - t0) < KS ? (tok1 - t0) : KS);
-    // recompute the per-lane parts here rather than keep 64-bit copies live
-    int lane_v = lane;
-    asm volatile("" : "+v"(lane_v));
-    const int rI_ = lane_v >> 5, pI_ = lane_v & 31, rJ_ = lane_v >> 4, pJ_ = lane_v & 15;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 8 * w + 2 * e + rI_;
-      const int c = pI_ ^ (4 * (row & 3));
-      const bool ok = (I0 + 8 * c < a.d) && row < rows;
-      const half_t* src = xs + (int64_t)row * a.ldx + I0 + 8 * c;
-      dma16(ok ? (const void*)src : (const void*)kZero16, bI + (8 * w + 2 * e) * TI);
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index, in an SGPR
+  const int rI = lane >> 5, pI = lane & 31, rJ = lane >> 4, pJ = lane & 15;
+  const int cI0 = pI ^ (4 * (rI & 3)), cI1 = pI ^ (4 * ((2 + rI) & 3));
+  const int cJ = pJ ^ (4 * (rJ & 3));
+  const bool okI0 = I0 + 8 * cI0 < a.d, okI1 = I0 + 8 * cI1 < a.d, okJ = J0 + 8 * cJ < a.d;
+  const int64_t offI0 = (int64_t)(8 * w + rI) * a.ldx + I0 + 8 * cI0;
+  const int64_t offI1 = (int64_t)(8 * w + rI) * a.ldx + I0 + 8 * cI1;
+  const int64_t offJ = (int64_t)(8 * w + rJ) * a.ldx + J0 + 8 * cJ;
+  const bool tile_inside = (I0 + TI <= a.d) && (J0 + TJ <= a.d);
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GPTQ_LDS void*)ring);
+  constexpr uint32_t STAGE_BYTES = KS * (TI + TJ) * 2;
+  // instruction e (0..3) of the I tile and (0..1) of the J tile for the stage
+  // starting at token t0 into ring buffer b
+  auto issue_I = [&](int e, int64_t t0, int b, bool full) {
+    // row 8w + 2e + l/32; offI0 / offI1 carry row 8w + l/32 and the chunk swizzle of
+    // the row's parity class (e even / odd)
+    const half_t* src = a.X + t0 * a.ldx + (int64_t)(2 * e) * a.ldx + ((e & 1) ? offI1 : offI0);
+    if (!full) {
+      const int rows = (int)((tok1 - t0) < KS ? (tok1 - t0) : KS);
+      const bool ok = ((e & 1) ? okI1 : okI0) && (8 * w + 2 * e + rI) < rows;
+      if (!ok) src = (const half_t*)kZero16;
     }
+    dma16(src, ring_lds + b * STAGE_BYTES + (uint32_t)((8 * wu + 2 * e) * TI * 2));
+  };
+  auto issue_J = [&](int e, int64_t t0, int b, bool full) {
+    const half_t* src = a.X + t0 * a.ldx + (int64_t)(4 * e) * a.ldx + offJ;
+    if (!full) {
+      const int rows = (int)((tok1 - t0) < KS ? (tok1 - t0) : KS);
+      const bool ok = okJ && (8 * w + 4 * e + rJ) < rows;
+      if (!ok) src = (const half_t*)kZero16;
+    }
+    dma16(src, ring_lds + b * STAGE_BYTES + KS * TI * 2 + (uint32_t)((8 * wu + 4 * e) * TJ * 2));
+  };
+  auto issue = [&](int64_t t0, int b) {
+    const bool full = tile_inside && t0 + KS <= tok1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) issue_I(e, t0, b, full);
     if (!j_in_i) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int row = 8 * w + 4 * e + rJ_;
-        const int c = pJ_ ^ (4 * (row & 3));
-        const bool ok = (J0 + 8 * c < a.d) && row < rows;
-        const half_t* src = xs + (int64_t)row * a.ldx + J0 + 8 * c;
-        dma16(ok ? (const void*)src : (const void*)kZero16, bJ + (8 * w + 4 * e) * TJ);
-      }
+      for (int e = 0; e < 2; ++e) issue_J(e, t0, b, full);
     }
   };
 
@@ -177,10 +199,12 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
 
   // B operand from bB (the I buffer itself on diagonal tiles): the two cases
   // are separate code paths so every LDS read has one known LDS object.
-  auto compute_from = [&](const half_t* bI, const half_t* bB, int bp) {
-    // one 16-token slice ahead: the fragments of slice kk+1 are read while the
-    // matrix cores work on slice kk (scheduling barriers keep it to one slice,
-    // which bounds the registers the reads occupy)
+  // The DMA of stage s+2 (into the buffer stage s-1 used) is spread over the
+  // four 16-token slices of stage s so that its address arithmetic overlaps the
+  // matrix cores. Fragments run one slice ahead; scheduling barriers keep it to
+  // one slice, which bounds the registers the reads occupy.
+  auto compute_from = [&](const half_t* bI, const half_t* bB, int bp, bool refill, int64_t t_next, int b_next) {
+    const bool full = tile_inside && t_next + KS <= tok1;
     half8 af[2][2], bf[2][2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) af[0][f] = frag(bI + offA[f], TI);
@@ -189,6 +213,10 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KS / 16; ++kk) {
       const int cur = kk & 1, nxt = cur ^ 1;
+      if (refill) {
+        issue_I(kk, t_next, b_next, full);
+        if (!j_in_i && kk < 2) issue_J(kk, t_next, b_next, full);
+      }
       if (kk + 1 < KS / 16) {
 #pragma unroll
         for (int f = 0; f < 2; ++f) af[nxt][f] = frag(bI + offA[f] + (kk + 1) * 16 * TI, TI);
@@ -203,11 +231,11 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto compute = [&](const half_t* bI, const half_t* bJ) {
+  auto compute = [&](const half_t* bI, const half_t* bJ, bool refill, int64_t t_next, int b_next) {
     if (j_in_i)
-      compute_from(bI, bI, TI);
+      compute_from(bI, bI, TI, refill, t_next, b_next);
     else
-      compute_from(bI, bJ, TJ);
+      compute_from(bI, bJ, TJ, refill, t_next, b_next);
   };
   auto fold = [&]() {
     // Fast2Sum(outer, acc): outer <- fl(outer + acc), acc <- exact residual.
@@ -227,13 +255,13 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   auto stage_i = [&](int b) { return ring + b * KS * (TI + TJ); };
   auto stage_j = [&](int b) { return ring + b * KS * (TI + TJ) + KS * TI; };
 
-  if (nstages > 0) issue(tok0, stage_i(0), stage_j(0));
-  if (nstages > 1) issue(tok0 + KS, stage_i(1), stage_j(1));
+  if (nstages > 0) issue(tok0, 0);
+  if (nstages > 1) issue(tok0 + KS, 1);
   int cur = 0;
   for (int s = 0; s < nstages; ++s) {
     // wait for this stage's DMA (the next stage's 4 or 6 loads per thread may
-    // stay in flight), barrier, refill the buffer freed by the previous stage,
-    // then run the matrix cores.
+    // stay in flight), barrier, then run the matrix cores while refilling the
+    // buffer the previous stage used.
     if (s + 1 >= nstages)
       __builtin_amdgcn_s_waitcnt(WAIT_VM0);
     else if (j_in_i)
@@ -242,8 +270,7 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
       __builtin_amdgcn_s_waitcnt(WAIT_VM6);
     lds_barrier();
     const int nxt = cur == 0 ? NBUF - 1 : cur - 1;  // (cur + 2) mod 3
-    if (s + 2 < nstages) issue(tok0 + (int64_t)(s + 2) * KS, stage_i(nxt), stage_j(nxt));
-    compute(stage_i(cur), stage_j(cur));
+    compute(stage_i(cur), stage_j(cur), s + 2 < nstages, tok0 + (int64_t)(s + 2) * KS, nxt);
     if ((s + 1) % FOLD == 0) fold();
     cur = cur == NBUF - 1 ? 0 : cur + 1;
   }
@@ -288,7 +315,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const double* __restri
     const int t = (int)(idx / per_tile);
     const int64_t within = idx - (int64_t)t * per_tile;
     int bi, bj;
-    tile_coords(t, bi, bj);
+    if (!tile_coords(t, d, bi, bj)) continue;
     const int64_t i = (int64_t)bi * TI + within / TJ, j = (int64_t)bj * TJ + within % TJ;
     if (i >= d || j > i) continue;
     double s = 0.0;
@@ -317,27 +344,38 @@ __global__ void syrk_zero_kernel(void* H, int64_t d, int64_t ldh, int h_f64) {
 }
 
 int syrk_ntiles(int64_t d) {
-  int64_t T = ceil_div(d, TI);
+  const int64_t T = ceil_div(d, TI);
   return (int)(T * (T + 1));
 }
 
-// Token split: enough workgroups to fill 256 CUs with a small tail, token
-// ranges a multiple of the stage, bounded by the stages available.
-int syrk_choose_split(int ntiles, int64_t n) {
+// Real (non-empty) tiles of the lower triangle at width d.
+int syrk_real_tiles(int64_t d) {
+  const int64_t ti = ceil_div(d, TI), tj = ceil_div(d, TJ);
+  int64_t n = 0;
+  for (int64_t bi = 0; bi < ti; ++bi) n += (2 * bi + 2 < tj ? 2 * bi + 2 : tj);
+  return (int)n;
+}
+
+// Token split S: minimises an estimate of the call's time,
+//   ceil(tiles * S / 256) rounds x (stages per split + 4) stage times
+//   + the fp64 partial tiles written and read back (S > 1),
+// with one workgroup per CU (the LDS ring takes most of a CU's LDS).
+int syrk_choose_split(int64_t d, int64_t n) {
   const int64_t stages = ceil_div(n, KS);
-  if (stages <= 1 || ntiles >= 1024) return 1;
+  const int tiles = syrk_real_tiles(d);
+  if (stages <= 1) return 1;
+  const double stage_us = 0.45 * KS / 64.0;
+  const double partial_us_per_tile = 2.0 * TI * TJ * 8 / 4.0e6;  // write + read at ~4 TB/s
   int best = 1;
-  double best_eff = 0.0;
+  double best_t = 1e30;
   for (int s = 1; s <= 64 && s <= stages; ++s) {
-    const int64_t wgs = (int64_t)ntiles * s;
-    const int64_t waves = ceil_div(wgs, 256);
-    const double eff = (double)wgs / (double)(waves * 256);
-    const double score = eff * (wgs >= 256 ? 1.0 : (double)wgs / 256.0);
-    if (score > best_eff + 1e-9) {
-      best_eff = score;
+    const int64_t rounds = ceil_div((int64_t)tiles * s, 256);
+    const double t = (double)rounds * ((double)ceil_div(stages, s) + 4.0) * stage_us +
+                     (s > 1 ? (double)s * tiles * partial_us_per_tile : 0.0);
+    if (t < best_t * 0.98) {
+      best_t = t;
       best = s;
     }
-    if (wgs >= 512 && eff >= 0.9) break;
   }
   return best;
 }
@@ -346,7 +384,7 @@ int syrk_choose_split(int ntiles, int64_t n) {
 
 size_t syrk_workspace_bytes(int64_t d, int64_t n) {
   const int nt = syrk_ntiles(d);
-  const int s = syrk_choose_split(nt, n);
+  const int s = syrk_choose_split(d, n);
   if (s <= 1) return 0;
   return (size_t)s * (size_t)nt * TI * TJ * sizeof(double);
 }
@@ -361,7 +399,7 @@ gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const hal
     }
     return GPTQ_OK;
   }
-  int split = syrk_choose_split(nt, n);
+  int split = syrk_choose_split(d, n);
   const size_t per_split = (size_t)nt * TI * TJ * sizeof(double);
   if (split > 1 && (ws == nullptr || ws_bytes < (size_t)split * per_split)) {
     split = ws ? (int)(ws_bytes / per_split) : 1;
