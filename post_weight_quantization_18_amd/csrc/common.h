@@ -37,6 +37,25 @@ __device__ inline int xcd_logical_block(int id, int nblocks) {
   return x * base + (x < rem ? x : rem) + local;
 }
 
+// gfx950 direct global -> LDS DMA of 16 bytes per lane: lane l writes LDS bytes
+// [lds_off + 16 l, lds_off + 16 l + 16) (lds_off wave-uniform). Issued through
+// asm so that the compiler does not insert its conservative "wait for every LDS
+// DMA" before unrelated LDS reads; callers wait on vmcnt themselves. The
+// instruction has no register result, and M0 is set and consumed inside the
+// same asm block.
+__device__ inline void dma16(const void* src, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(src)
+               : "memory", "m0");
+}
+
+// Workgroup barrier after this wave's LDS accesses completed; the asm keeps the
+// compiler from moving memory operations across it.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt(N), no wait on exp/lgkm.
+constexpr int WAIT_VM0 = 0x0F70;
+constexpr int WAIT_VM4 = 0x0F74;
+constexpr int WAIT_VM6 = 0x0F76;
 
 // Entry points of the individual kernel families (implemented in the .hip files).
 gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const half_t* X, int64_t n,
@@ -53,6 +72,26 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
                             float* scales, uint8_t* zeros, float* W_hat, float* err_sq, void* ws,
                             size_t ws_bytes, hipStream_t st);
 size_t quant_workspace_bytes(int64_t m, int64_t d, const gptq_qcfg_t& cfg);
+
+// C[i][j] -= rowscale[i] * cscale * sum_k A[i][k] B[k][j] for i < M, j < N, with
+// A = Ah + Al and B = Bh + Bl given as fp16 pairs and the product taken as
+// Ah Bh + Ah Bl + Al Bh on the fp16 matrix cores (fp32 accumulate).
+// A is row-major [M][lda]; B is stored transposed in 128-deep K slabs: element
+// (k, j) at (k / 128) * bstride + j * 128 + k % 128. K % 32 == 0.
+struct TgemmArgs {
+  float* C;
+  int64_t ldc;
+  const half_t* Ah;
+  const half_t* Al;
+  int64_t lda;
+  const float* rowscale;
+  const half_t* Bh;
+  const half_t* Bl;
+  int64_t bstride;
+  const float* cscale;  // device scalar (power of two), multiplies every row
+  int64_t M, N, K;
+};
+gptq_status_t tgemm_enqueue(const TgemmArgs& a, hipStream_t st);
 
 gptq_status_t pack_enqueue(const uint8_t* codes, int64_t ldc, int64_t m, int64_t d, int bits,
                            uint32_t* out, hipStream_t st);

@@ -11,10 +11,14 @@
 //    (128 x 128 fp32) in LDS, read as wave-uniform broadcasts. Step 3 inside
 //    the block is a chain of register FMAs; the group grid (min/max) is a
 //    per-lane reduction over registers, no cross-lane traffic at all.
-//  * The block's errors E [m, 128] go to the workspace; the far columns are
-//    then updated by one GEMM W[:, end:] -= E U[blk, end:] on the matrix cores
-//    (v_mfma_f32_32x32x2f32: fp32 operands, because single-pass fp16 operands
-//    move the pre-round values by more than the 1e-3 grid-unit band).
+//  * The block's errors E [m, 128] go to the workspace. The columns not yet
+//    quantized are updated on the matrix cores (trail.hip) in two levels, so
+//    that the fp32 weights are not re-read and re-written once per 128-column
+//    block: inside a super-block of S columns (a multiple of 128 near
+//    sqrt(128 d)) every block updates the rest of its super-block; at the end
+//    of a super-block one GEMM with K = S updates every later column. The sum
+//    applied to each column is the same as with one update per block; only the
+//    order in which its terms are added differs.
 //  * Codes are kept one byte per weight in the workspace and packed (with the
 //    dequantized W_hat) by a final kernel.
 #include <utility>
@@ -29,28 +33,75 @@ constexpr int BLK = 128;
 constexpr int CL_THREADS = 256;  // 64 rows x 4 lanes
 
 struct QuantWs {
-  float* Wk;       // m x d working weights
-  float* E;        // m x BLK block errors
-  uint8_t* codes;  // m x d
-  float* rdiag;    // d: 1 / U_jj
-  float* U32;      // d x d (only when U is fp64)
+  float* Wk;        // m x d working weights
+  float* Esb;       // m x S errors of the current super-block
+  half_t* Ehb;      // m x BLK errors of one block, scaled, fp16 high part
+  half_t* Elb;      //                                    fp16 low part
+  half_t* Ehs;      // m x S errors of one super-block, scaled, fp16 high part
+  half_t* Els;      //                                          fp16 low part
+  float* einv_b;    // m: inverse of the row scale of Ehb / Elb
+  float* einv_s;    // m: inverse of the row scale of Ehs / Els
+  uint8_t* codes;   // m x d
+  float* rdiag;     // d: 1 / U_jj
+  uint32_t* umax;   // [0]: bits of max |U| over the far part of every block row
+  float* uinv;      // [0]: inverse of the power-of-two scale of U's fp16 pairs
+  half_t* Uth;      // nblocks x d x BLK: U[blk, c] transposed (c, k), scaled, fp16 high
+  half_t* Utl;      //                                                         fp16 low
+  float* U32;       // d x d (only when U is fp64)
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-QuantWs quant_ws(void* ws, int64_t m, int64_t d, int u_f64) {
+int64_t nblocks_of(int64_t d) { return (d + BLK - 1) / BLK; }
+
+// Super-block width: the multiple of 128 nearest sqrt(128 d), within [256, 2048]
+// (balances the weight traffic of the in-super-block updates, ~ d S, against
+// that of the super-block GEMMs, ~ d^2 / S). Groups wider than a block are
+// fitted at their first block on the weights of the whole group, which must by
+// then carry every earlier update: S is rounded up to a multiple of such a
+// group, so that no group straddles two super-blocks.
+int64_t sb_width(int64_t d, int group) {
+  int64_t s = (int64_t)(sqrt(128.0 * (double)d) / BLK + 0.5) * BLK;
+  if (s < 2 * BLK) s = 2 * BLK;
+  if (s > 16 * BLK) s = 16 * BLK;
+  if (group > BLK) s = ceil_div(s, group) * group;
+  return s;
+}
+
+QuantWs quant_ws(void* ws, int64_t m, int64_t d, int group, int u_f64) {
   QuantWs w;
   char* p = (char*)ws;
-  w.Wk = (float*)p;
-  p += align256((size_t)m * d * sizeof(float));
-  w.E = (float*)p;
-  p += align256((size_t)m * BLK * sizeof(float));
-  w.codes = (uint8_t*)p;
-  p += align256((size_t)m * d);
-  w.rdiag = (float*)p;
-  p += align256((size_t)d * sizeof(float));
-  w.U32 = u_f64 ? (float*)p : nullptr;
+  const int64_t nb = nblocks_of(d), S = sb_width(d, group);
+  auto take = [&](size_t bytes) {
+    char* q = p;
+    p += align256(bytes);
+    return q;
+  };
+  w.Wk = (float*)take((size_t)m * d * sizeof(float));
+  w.Esb = (float*)take((size_t)m * S * sizeof(float));
+  w.Ehb = (half_t*)take((size_t)m * BLK * sizeof(half_t));
+  w.Elb = (half_t*)take((size_t)m * BLK * sizeof(half_t));
+  w.Ehs = (half_t*)take((size_t)m * S * sizeof(half_t));
+  w.Els = (half_t*)take((size_t)m * S * sizeof(half_t));
+  w.einv_b = (float*)take((size_t)m * sizeof(float));
+  w.einv_s = (float*)take((size_t)m * sizeof(float));
+  w.codes = (uint8_t*)take((size_t)m * d);
+  w.rdiag = (float*)take((size_t)d * sizeof(float));
+  w.umax = (uint32_t*)take(sizeof(uint32_t));
+  w.uinv = (float*)take(sizeof(float));
+  w.Uth = (half_t*)take((size_t)nb * d * BLK * sizeof(half_t));
+  w.Utl = (half_t*)take((size_t)nb * d * BLK * sizeof(half_t));
+  w.U32 = u_f64 ? (float*)take((size_t)d * d * sizeof(float)) : nullptr;
   return w;
+}
+
+size_t quant_ws_total(int64_t m, int64_t d, int group, int u_f64) {
+  const int64_t nb = nblocks_of(d), S = sb_width(d, group);
+  size_t b = align256((size_t)m * d * 4) + align256((size_t)m * S * 4) + 2 * align256((size_t)m * BLK * 2) +
+             2 * align256((size_t)m * S * 2) + 2 * align256((size_t)m * 4) + align256((size_t)m * d) +
+             align256((size_t)d * 4) + 2 * align256(4) + 2 * align256((size_t)nb * d * BLK * 2);
+  if (u_f64) b += align256((size_t)d * d * 4);
+  return b;
 }
 
 struct GridFit {
@@ -125,7 +176,8 @@ struct ColArgs {
   float maxq;
   int group;       // runtime group size (used when G < 0)
   int ngroups;
-  float* E;
+  float* E;        // errors out: E[r * lde + ecol + k] for the block's columns k
+  int64_t lde, ecol;
   uint8_t* codes;
   float* scales;
   uint8_t* zeros;
@@ -321,15 +373,13 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
 
   if (live) run_steps<G>(std::make_integer_sequence<int, BLK>{}, st, a, r, g, Us, rdiag, bw);
 
-  if (live) {
-    float* erow = a.E + r * BLK + g * CPL;
-    if (cols_ok) {
+  if (live && cols_ok) {
+    float* erow = a.E + r * a.lde + a.ecol + g * CPL;
 #pragma unroll
-      for (int k = 0; k < CPL; k += 4) *(float4*)(erow + k) = make_float4(st.w[k], st.w[k + 1], st.w[k + 2], st.w[k + 3]);
-      uint8_t* crow = a.codes + r * a.d + a.j0 + g * CPL;
-      *(uint4*)(crow) = make_uint4(st.cw[0], st.cw[1], st.cw[2], st.cw[3]);
-      *(uint4*)(crow + 16) = make_uint4(st.cw[4], st.cw[5], st.cw[6], st.cw[7]);
-    }
+    for (int k = 0; k < CPL; k += 4) *(float4*)(erow + k) = make_float4(st.w[k], st.w[k + 1], st.w[k + 2], st.w[k + 3]);
+    uint8_t* crow = a.codes + r * a.d + a.j0 + g * CPL;
+    *(uint4*)(crow) = make_uint4(st.cw[0], st.cw[1], st.cw[2], st.cw[3]);
+    *(uint4*)(crow + 16) = make_uint4(st.cw[4], st.cw[5], st.cw[6], st.cw[7]);
   }
   // row sum of err^2 / 2 over the quad
   float es = st.esum;
@@ -338,65 +388,98 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
   if (live && g == 0 && a.err_sq) a.err_sq[r] = (a.first ? 0.0f : a.err_sq[r]) + 0.5f * es;
 }
 
-// W[r][c] -= sum_{k < bw} E[r][k] U[j0 + k][c] for c >= j1.
-// 128 x 128 output tile per workgroup, 4 waves of 64 x 64, fp32 MFMA 32x32x2.
-__global__ __launch_bounds__(256) void trail_kernel(float* Wk, int64_t m, int64_t d, const float* E,
-                                                    const float* U, int64_t ldu, int64_t j0, int bw, int64_t j1) {
-  __shared__ float As[128][33];
-  __shared__ float Bs[32][132];
-  const int64_t row0 = (int64_t)blockIdx.y * 128, col0 = j1 + (int64_t)blockIdx.x * 128;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wr = (w >> 1) * 64, wc = (w & 1) * 64;
-  float16v acc[2][2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
-  const int li = lane & 31, lk = lane >> 5;
-  for (int kc = 0; kc < bw; kc += 32) {
-    for (int idx = tid; idx < 128 * 8; idx += 256) {
-      const int r = idx >> 3, c4 = (idx & 7) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (row0 + r < m) v = *(const float4*)(E + (row0 + r) * BLK + kc + c4);
-      As[r][c4] = v.x;
-      As[r][c4 + 1] = v.y;
-      As[r][c4 + 2] = v.z;
-      As[r][c4 + 3] = v.w;
-    }
-    for (int idx = tid; idx < 32 * 32; idx += 256) {
-      const int r = idx >> 5, c4 = (idx & 31) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (col0 + c4 < d) v = *(const float4*)(U + (j0 + kc + r) * ldu + col0 + c4);
-      *(float4*)&Bs[r][c4] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 32; k += 2) {
-      float av[2], bv[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) av[x] = As[wr + x * 32 + li][k + lk];
-#pragma unroll
-      for (int y = 0; y < 2; ++y) bv[y] = Bs[k + lk][wc + y * 32 + li];
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[x], bv[y], acc[x][y], 0, 0, 0);
-    }
-    __syncthreads();
+// Errors E[r][0 .. kw) (fp32, leading dimension lde) -> fp16 pairs with one
+// power-of-two scale per row that puts max |e| in [2^14, 2^15):
+//   Eh = fp16(e * 2^k), El = fp16(e * 2^k - Eh), einv[r] = 2^-k.
+// One wave per row.
+__global__ __launch_bounds__(256) void esplit_kernel(const float* E, int64_t lde, int64_t m, int kw, half_t* Eh,
+                                                     half_t* El, int64_t ldo, float* einv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= m) return;
+  const float* erow = E + r * lde;
+  float mx = 0.0f;
+  for (int k = 4 * lane; k < kw; k += 256) {
+    const float4 v = *(const float4*)(erow + k);
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
   }
-  const int hl = lane >> 5;
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  int ex = 0;
+  if (mx > 0.0f) frexpf(mx, &ex);
+  const float sc = mx > 0.0f ? ldexpf(1.0f, 15 - ex) : 1.0f;
+  for (int k = 4 * lane; k < kw; k += 256) {
+    const float4 v = *(const float4*)(erow + k);
+    const float x[4] = {v.x * sc, v.y * sc, v.z * sc, v.w * sc};
+    half_t h[4], l[4];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+    for (int t = 0; t < 4; ++t) {
+      h[t] = (half_t)x[t];
+      l[t] = (half_t)(x[t] - (float)h[t]);
+    }
+    typedef half_t half4 __attribute__((ext_vector_type(4)));
+    *(half4*)(Eh + r * ldo + k) = half4{h[0], h[1], h[2], h[3]};
+    *(half4*)(El + r * ldo + k) = half4{l[0], l[1], l[2], l[3]};
+  }
+  if (lane == 0) einv[r] = 1.0f / sc;
+}
+
+// max |U[j0 + k][c]| over k < BLK, c >= j0 + BLK, over every block but the
+// last: float bits of non-negative values order like integers, so atomicMax on
+// the bits is exact and order-independent.
+__global__ __launch_bounds__(256) void umax_zero_kernel(uint32_t* umax) {
+  if (threadIdx.x == 0) umax[0] = 0u;
+}
+
+__global__ __launch_bounds__(256) void umax_kernel(const float* U, int64_t ldu, int64_t d, uint32_t* umax) {
+  const int64_t b = blockIdx.y, j0 = b * BLK, j1 = j0 + BLK;
+  float mx = 0.0f;
+  for (int64_t c = j1 + (int64_t)blockIdx.x * 256 + threadIdx.x; c < d; c += (int64_t)gridDim.x * 256)
+    for (int k = 0; k < BLK; ++k) mx = fmaxf(mx, fabsf(U[(j0 + k) * ldu + c]));
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((threadIdx.x & 63) == 0 && mx > 0.0f) atomicMax(&umax[0], __float_as_uint(mx));
+}
+
+__device__ inline float u_scale(const uint32_t* umax) {
+  const float mx = __uint_as_float(umax[0]);
+  int ex = 0;
+  if (mx > 0.0f) frexpf(mx, &ex);
+  return mx > 0.0f ? ldexpf(1.0f, 15 - ex) : 1.0f;
+}
+
+// Transposed, scaled fp16 hi/lo panels of the far part of each block row of U:
+//   Ut{h,l}[b][c][k] = split(U[j0 + k][c] * 2^s),  c >= j0 + BLK, k < BLK,
+// with 2^s the power of two that puts max |U| of all far parts in [2^14, 2^15)
+// (uinv = 2^-s). One 64-column chunk per workgroup, transposed through LDS.
+__global__ __launch_bounds__(256) void usplit_kernel(const float* U, int64_t ldu, int64_t d, const uint32_t* umax,
+                                                     half_t* Uth, half_t* Utl, float* uinv) {
+  __shared__ float tile[BLK][64 + 1];
+  const int64_t b = blockIdx.y, j0 = b * BLK, j1 = j0 + BLK;
+  const int64_t c0 = j1 + (int64_t)blockIdx.x * 64;
+  const float sc = u_scale(umax);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) uinv[0] = 1.0f / sc;
+  if (c0 >= d) return;
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < BLK * 64; idx += 256) {
+    const int k = idx / 64, c = idx % 64;
+    tile[k][c] = (c0 + c < d) ? U[(j0 + k) * ldu + c0 + c] * sc : 0.0f;
+  }
+  __syncthreads();
+  // each thread writes 8 consecutive k of one column: 64 cols x 16 chunks
+  for (int idx = tid; idx < 64 * (BLK / 8); idx += 256) {
+    const int c = idx / (BLK / 8), k8 = (idx % (BLK / 8)) * 8;
+    if (c0 + c >= d) continue;
+    half8 hv, lv;
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t i = row0 + wr + x * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const int64_t j = col0 + wc + y * 32 + li;
-        if (i < m && j < d) Wk[i * d + j] -= acc[x][y][r];
-      }
+    for (int t = 0; t < 8; ++t) {
+      const float v = tile[k8 + t][c];
+      const half_t h = (half_t)v;
+      hv[t] = h;
+      lv[t] = (half_t)(v - (float)h);
+    }
+    const int64_t o = (b * d + c0 + c) * BLK + k8;
+    *(half8*)(Uth + o) = hv;
+    *(half8*)(Utl + o) = lv;
+  }
 }
 
 // Packs one row per workgroup into the LSB-first bitstream and, when W_hat is
@@ -439,20 +522,15 @@ gptq_status_t launch_colloop(const ColArgs& a, hipStream_t st) {
 }  // namespace
 
 size_t quant_workspace_bytes(int64_t m, int64_t d, const gptq_qcfg_t& cfg) {
-  (void)cfg;
-  size_t b = align256((size_t)m * d * sizeof(float)) + align256((size_t)m * BLK * sizeof(float)) +
-             align256((size_t)m * d) + align256((size_t)d * sizeof(float));
-  return b;
+  return quant_ws_total(m, d, cfg.group_size, 0);
 }
-
-static size_t quant_u32_bytes(int64_t d) { return align256((size_t)d * d * sizeof(float)); }
 
 gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int64_t ldw, const void* U, int u_f64,
                             int64_t ldu, const gptq_qcfg_t& cfg, uint32_t* qcodes, float* scales, uint8_t* zeros,
                             float* W_hat, float* err_sq, void* ws, size_t ws_bytes, hipStream_t st) {
-  const size_t need = quant_workspace_bytes(m, d, cfg) + (u_f64 ? quant_u32_bytes(d) : 0);
+  const size_t need = quant_ws_total(m, d, cfg.group_size, u_f64);
   if (ws == nullptr || ws_bytes < need) return GPTQ_ERR_WORKSPACE;
-  QuantWs w = quant_ws(ws, m, d, u_f64);
+  QuantWs w = quant_ws(ws, m, d, cfg.group_size, u_f64);
   const int ternary = cfg.grid == GPTQ_GRID_TERNARY;
   const float maxq = ternary ? 2.0f : (float)((1 << cfg.bits) - 1);
   const int group = cfg.group_size;
@@ -469,6 +547,17 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   }
   hipLaunchKernelGGL(rdiag_kernel, dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, st, U32, d, ldu32, w.rdiag);
   GPTQ_CHECK_LAUNCH();
+  const int64_t nblk = nblocks_of(d);
+  if (nblk > 1) {
+    hipLaunchKernelGGL(umax_zero_kernel, dim3(1), dim3(64), 0, st, w.umax);
+    GPTQ_CHECK_LAUNCH();
+    const unsigned cgroups = (unsigned)(ceil_div(d, 256) < 16 ? ceil_div(d, 256) : 16);
+    hipLaunchKernelGGL(umax_kernel, dim3(cgroups, (unsigned)(nblk - 1)), dim3(256), 0, st, U32, ldu32, d, w.umax);
+    GPTQ_CHECK_LAUNCH();
+    hipLaunchKernelGGL(usplit_kernel, dim3((unsigned)ceil_div(d, 64), (unsigned)(nblk - 1)), dim3(256), 0, st, U32,
+                       ldu32, d, (const uint32_t*)w.umax, w.Uth, w.Utl, w.uinv);
+    GPTQ_CHECK_LAUNCH();
+  }
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)ceil_div(m, 4)), dim3(256), 0, st, W, w_f32, m, d, ldw, w.Wk,
                      group == 0 ? 1 : 0, ternary, maxq, scales, zeros);
   GPTQ_CHECK_LAUNCH();
@@ -484,16 +573,30 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   a.maxq = maxq;
   a.group = group;
   a.ngroups = ngroups;
-  a.E = w.E;
   a.codes = w.codes;
   a.scales = scales;
   a.zeros = zeros;
   a.err_sq = err_sq;
+  const int64_t S = sb_width(d, group);
+  a.E = w.Esb;
+  a.lde = S;
   const int64_t nblocks = ceil_div(d, BLK);
+  TgemmArgs t;
+  t.C = nullptr;
+  t.ldc = d;
+  t.Bh = w.Uth;
+  t.Bl = w.Utl;
+  t.bstride = d * BLK;
+  t.cscale = w.uinv;
+  t.M = m;
+  const unsigned egrid = (unsigned)ceil_div(m, 4);
   for (int64_t b = 0; b < nblocks; ++b) {
     a.j0 = b * BLK;
     a.bw = (int)((d - a.j0) < BLK ? (d - a.j0) : BLK);
     a.first = b == 0;
+    const int64_t sb0 = (a.j0 / S) * S;
+    const int64_t sb1 = (sb0 + S) < d ? (sb0 + S) : d;
+    a.ecol = a.j0 - sb0;
     gptq_status_t s;
     switch (group) {
       case 0: s = launch_colloop<0>(a, st); break;
@@ -504,11 +607,36 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
     }
     if (s != GPTQ_OK) return s;
     const int64_t j1 = a.j0 + a.bw;
-    if (j1 < d) {
-      dim3 grid((unsigned)ceil_div(d - j1, 128), (unsigned)ceil_div(m, 128));
-      hipLaunchKernelGGL(trail_kernel, grid, dim3(256), 0, st, w.Wk, m, d, (const float*)w.E, U32, ldu32, a.j0,
-                         a.bw, j1);
+    if (j1 < sb1) {
+      // the rest of the super-block: K = this block
+      hipLaunchKernelGGL(esplit_kernel, dim3(egrid), dim3(256), 0, st, (const float*)(w.Esb + a.ecol), S, m, a.bw,
+                         w.Ehb, w.Elb, (int64_t)BLK, w.einv_b);
       GPTQ_CHECK_LAUNCH();
+      t.C = w.Wk + j1;
+      t.Ah = w.Ehb;
+      t.Al = w.Elb;
+      t.lda = BLK;
+      t.rowscale = w.einv_b;
+      t.Bh = w.Uth + (b * d + j1) * BLK;
+      t.Bl = w.Utl + (b * d + j1) * BLK;
+      t.N = sb1 - j1;
+      t.K = a.bw;
+      if ((s = tgemm_enqueue(t, st)) != GPTQ_OK) return s;
+    } else if (j1 == sb1 && sb1 < d) {
+      // every later column: K = the whole super-block
+      hipLaunchKernelGGL(esplit_kernel, dim3(egrid), dim3(256), 0, st, (const float*)w.Esb, S, m, (int)(sb1 - sb0),
+                         w.Ehs, w.Els, S, w.einv_s);
+      GPTQ_CHECK_LAUNCH();
+      t.C = w.Wk + sb1;
+      t.Ah = w.Ehs;
+      t.Al = w.Els;
+      t.lda = S;
+      t.rowscale = w.einv_s;
+      t.Bh = w.Uth + ((sb0 / BLK) * d + sb1) * BLK;
+      t.Bl = w.Utl + ((sb0 / BLK) * d + sb1) * BLK;
+      t.N = d - sb1;
+      t.K = sb1 - sb0;
+      if ((s = tgemm_enqueue(t, st)) != GPTQ_OK) return s;
     }
   }
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)m), dim3(256), 0, st, (const uint8_t*)w.codes, d, m, d, cfg.bits,
@@ -526,7 +654,7 @@ gptq_status_t pack_enqueue(const uint8_t* codes, int64_t ldc, int64_t m, int64_t
 }
 
 size_t quant_workspace_bytes_u64(int64_t m, int64_t d, const gptq_qcfg_t& cfg) {
-  return quant_workspace_bytes(m, d, cfg) + quant_u32_bytes(d);
+  return quant_ws_total(m, d, cfg.group_size, 1);
 }
 
 }  // namespace gptq

@@ -45,11 +45,6 @@ constexpr int NBUF = GPTQ_SYRK_NBUF;  // LDS ring depth
 // lane issues the same number of loads per stage, so vmcnt waits stay exact.
 __device__ const uint4 kZero16[1] = {{0u, 0u, 0u, 0u}};
 
-// s_waitcnt immediates (gfx9 encoding): vmcnt(N), no wait on exp/lgkm.
-constexpr int WAIT_VM0 = 0x0F70;
-constexpr int WAIT_VM4 = 0x0F74;
-constexpr int WAIT_VM6 = 0x0F76;
-
 struct SyrkArgs {
   const half_t* X;
   int64_t ldx, n, d;
@@ -86,22 +81,6 @@ __device__ inline half8 frag(const half_t* p, int pitch) {
 
 // LDS chunk (16 B) position of feature chunk c in row r: c ^ 4 (r mod 4).
 __device__ inline int swz(int row, int chunk) { return chunk ^ (4 * (row & 3)); }
-
-// global -> LDS DMA of 16 bytes per lane: lane l writes LDS bytes
-// [lds + 16 l, lds + 16 l + 16). Issued through asm so that the compiler does
-// not insert its conservative "wait for every LDS DMA" before unrelated LDS
-// reads; the kernel waits on vmcnt itself. The instruction has no register
-// result, and M0 is set and consumed inside the same asm block.
-__device__ inline void dma16(const void* src, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(src)
-               : "memory", "m0");
-}
-
-__device__ inline void lds_barrier() {
-  // LDS writes of this wave are complete; the asm keeps the compiler from
-  // moving memory operations across the barrier.
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   // ring of NBUF stages; stage buffer b holds the I tile then the J tile

@@ -1,0 +1,202 @@
+// Trailing update of the lazy-block scheme on the gfx950 matrix cores:
+//   W[:, far] -= E U[blocks, far]
+// FDE Interviews breakdown of GPTQ, figure "Quantize a column, correct the
+// rest", steps 3-4: the errors of a finished block of columns are pushed onto
+// the columns not yet quantized as one matrix product.
+//
+// Precision: a single fp16 product moves the pre-round values by about 2^-11 of
+// the update, which is more than the rounding-boundary band the codes must
+// respect, so both operands are split into fp16 pairs (x = hi + lo, each with
+// a power-of-two scale that puts the largest |x| just under 2^15) and the
+// product is taken in three passes, hi*hi + hi*lo + lo*hi, accumulated in fp32
+// (about 2^-22 relative; lo*lo is below fp32 rounding).
+//
+// Design (MI355X):
+//  * 256 x 128 output tile per workgroup of 8 waves (64 x 64 each, two per
+//    SIMD); v_mfma_f32_32x32x16_f16, 12 per wave per 16-deep K step.
+//  * Both operands are K-contiguous (A row-major, B stored transposed), so each
+//    32-deep K stage is four row-major LDS panels (A hi/lo 256 x 32, B hi/lo
+//    128 x 32, 48 KB) filled by the direct global->LDS DMA into a 3-deep ring;
+//    the 16-byte chunks of a row are XOR-swizzled by (row / 4) mod 4, chosen on
+//    the global side, which makes the fragment reads (ds_read_b128, 32 rows x 2
+//    chunks per wave) free of bank conflicts.
+//  * Workgroups run in groups of 8 row tiles per column tile, and the groups
+//    are laid out contiguously per XCD, so that the tiles resident on one XCD
+//    share their A and B panels in its L2.
+#include "common.h"
+
+namespace gptq {
+
+namespace {
+
+constexpr int TM = 256, TN = 128, KS = 32, NT = 512, NBUF = 3;
+constexpr int ROWB = KS * 2;                       // bytes per LDS panel row (32 halves)
+constexpr uint32_t OFF_AH = 0, OFF_AL = TM * ROWB, OFF_BH = 2 * TM * ROWB, OFF_BL = 2 * TM * ROWB + TN * ROWB;
+constexpr uint32_t STAGE_BYTES = (2 * TM + 2 * TN) * ROWB;  // 48 KB
+constexpr int GROUP_M = 8;
+
+__device__ const uint4 kZeroT[1] = {{0u, 0u, 0u, 0u}};
+
+__device__ inline half8 lds_frag(const char* ring, uint32_t byte_off) {
+  return *(const half8*)(ring + byte_off);
+}
+
+__global__ __launch_bounds__(NT, 1) void tgemm_kernel(TgemmArgs a, int ntm, int ntn) {
+  __shared__ __attribute__((aligned(1024))) char ring[NBUF * STAGE_BYTES];
+
+  // grouped tile order inside each XCD's contiguous range of logical ids
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int per_group = GROUP_M * ntn;
+  const int grp = logical / per_group, first_m = grp * GROUP_M;
+  const int gm = (ntm - first_m) < GROUP_M ? (ntm - first_m) : GROUP_M;
+  const int within = logical - grp * per_group;
+  const int tm = first_m + within % gm, tn = within / gm;
+  const int64_t I0 = (int64_t)tm * TM, J0 = (int64_t)tn * TN;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int wi = w >> 1, wj = w & 1;
+  const int nst = (int)(a.K / KS);
+
+  // ---- DMA plan: wave w moves A rows 32w .. 32w+31 (hi and lo) and B rows
+  // 16w .. 16w+15 (hi and lo): six 1 KB instructions per stage. Lane l covers
+  // row (l / 4) of the instruction's 16 rows and LDS chunk position l % 4,
+  // which holds global chunk (l % 4) ^ ((row / 4) % 4) = (l % 4) ^ ((l / 16) % 4).
+  const int lrow = lane >> 2;
+  const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  int64_t srcA[2], srcB;
+  bool okA[2], okB;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int64_t r = I0 + 32 * w + 16 * e + lrow;
+    okA[e] = r < a.M;
+    srcA[e] = (okA[e] ? r : 0) * a.lda + 8 * chunk;
+  }
+  {
+    const int64_t c = J0 + 16 * w + lrow;
+    okB = c < a.N;
+    srcB = (okB ? c : 0) * 128 + 8 * chunk;
+  }
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GPTQ_LDS void*)ring);
+  // instruction e (0..5) of stage s into ring buffer b
+  auto issue = [&](int e, int s, int b) {
+    const int64_t k0 = (int64_t)s * KS;
+    const void* src;
+    uint32_t off;
+    if (e < 4) {
+      const int h = e & 1;  // which 16-row half of the wave's 32 A rows
+      const half_t* base = (e < 2) ? a.Ah : a.Al;
+      src = okA[h] ? (const void*)(base + srcA[h] + k0) : (const void*)kZeroT;
+      off = ((e < 2) ? OFF_AH : OFF_AL) + (uint32_t)((32 * wu + 16 * h) * ROWB);
+    } else {
+      const half_t* base = (e == 4) ? a.Bh : a.Bl;
+      src = okB ? (const void*)(base + (k0 >> 7) * a.bstride + srcB + (k0 & 127)) : (const void*)kZeroT;
+      off = ((e == 4) ? OFF_BH : OFF_BL) + (uint32_t)(16 * wu * ROWB);
+    }
+    dma16(src, ring_lds + (uint32_t)b * STAGE_BYTES + off);
+  };
+
+  // ---- fragment offsets: subtile row (l % 32), K chunk 2 kk + l / 32, stored
+  // at position chunk ^ ((row / 4) % 4) = chunk ^ ((l / 4) % 4)
+  const int frow = lane & 31, fsw = (lane >> 2) & 3, fhi = lane >> 5;
+  uint32_t offA[2][2], offB[2][2];  // [subtile][kk]
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint32_t pos = (uint32_t)(((2 * kk + fhi) ^ fsw) * 16);
+      offA[x][kk] = (uint32_t)((64 * wi + 32 * x + frow) * ROWB) + pos;
+      offB[x][kk] = (uint32_t)((64 * wj + 32 * x + frow) * ROWB) + pos;
+    }
+
+  float16v acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
+
+  auto compute = [&](int b, bool refill, int s_next, int b_next) {
+    const char* st = ring + (size_t)b * STAGE_BYTES;
+    half8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        ah[x] = lds_frag(st, OFF_AH + offA[x][kk]);
+        al[x] = lds_frag(st, OFF_AL + offA[x][kk]);
+        bh[x] = lds_frag(st, OFF_BH + offB[x][kk]);
+        bl[x] = lds_frag(st, OFF_BL + offB[x][kk]);
+      }
+      if (refill) {
+#pragma unroll
+        for (int e = 3 * kk; e < 3 * kk + 3; ++e) issue(e, s_next, b_next);
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[x], bh[y], acc[x][y], 0, 0, 0);
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[x], bl[y], acc[x][y], 0, 0, 0);
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[x], bh[y], acc[x][y], 0, 0, 0);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (nst > 0) {
+#pragma unroll
+    for (int e = 0; e < 6; ++e) issue(e, 0, 0);
+  }
+  if (nst > 1) {
+#pragma unroll
+    for (int e = 0; e < 6; ++e) issue(e, 1, 1);
+  }
+  int cur = 0;
+  for (int s = 0; s < nst; ++s) {
+    // this stage's six loads are done once at most the next stage's six remain
+    if (s + 1 >= nst)
+      __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    else
+      __builtin_amdgcn_s_waitcnt(WAIT_VM6);
+    lds_barrier();
+    const int nxt = cur == 0 ? NBUF - 1 : cur - 1;  // (cur + 2) mod 3: the buffer stage s-1 used
+    compute(cur, s + 2 < nst, s + 2, nxt);
+    cur = cur == NBUF - 1 ? 0 : cur + 1;
+  }
+
+  // ---- epilogue: C -= acc * rowscale[i] * cscale ----
+  const float cs = *a.cscale;
+  const int hl = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t i = I0 + 64 * wi + 32 * x + 8 * (r >> 2) + 4 * hl + (r & 3);
+      if (i >= a.M) continue;
+      const float sc = a.rowscale[i] * cs;
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        const int64_t j = J0 + 64 * wj + 32 * y + col;
+        if (j < a.N) {
+          float* c = a.C + i * a.ldc + j;
+          *c = fmaf(-acc[x][y][r], sc, *c);
+        }
+      }
+    }
+}
+
+}  // namespace
+
+gptq_status_t tgemm_enqueue(const TgemmArgs& a, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0 || a.K <= 0) return GPTQ_OK;
+  if (a.K % KS) return GPTQ_ERR_INVALID_ARG;
+  const int64_t ntm = ceil_div(a.M, TM), ntn = ceil_div(a.N, TN);
+  if (ntm * ntn > 0x7fffffff) return GPTQ_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(tgemm_kernel, dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a, (int)ntm, (int)ntn);
+  GPTQ_CHECK_LAUNCH();
+  return GPTQ_OK;
+}
+
+}  // namespace gptq
