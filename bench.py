@@ -37,8 +37,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--config", default="opt2.7b-fc1", choices=sorted(S.CONFIGS))
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=512)
-    p.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    p.add_argument("--cpu-sample-rows", type=int, default=None)
+    p.add_argument("--cpu-sample-tokens", type=int, default=None)
     return p.parse_args()
 
 
@@ -96,42 +96,63 @@ class LayerRun:
         return [self.ev_h[2 * i].elapsed_time(self.ev_h[2 * i + 1]) for i in range(self.n_chunks())]
 
 
-def cpu_baseline(cfg, w, x, rows, tokens):
-    """The fp64 oracle, as it stands, on a bounded sample of the same layer:
-    H over `tokens` calibration tokens (scaled by N / tokens), the full chain on
-    d, and the column loop on `rows` rows (scaled by m / rows)."""
+def _say(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, w, x, rows=None, tokens=None):
+    """The fp64 oracle, as it stands, on a bounded sample of the same layer
+    (about 10-30 s of CPU work), extrapolated to the whole layer:
+      * H over `tokens` calibration tokens, scaled by N / tokens;
+      * the chain (damp, Cholesky, inverse) on the leading d_s x d_s block of
+        that H (at most 6144), scaled by (d / d_s)^3;
+      * the column loop on `rows` rows at full width, scaled by m / rows. Its
+        cost does not depend on U's values, so at d > d_s it runs on a stand-in
+        upper-triangular U (unit diagonal, 1e-3 above it)."""
     import numpy as np
 
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
-        threads = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else os.cpu_count()
+        info = threadpool_info()
+        threads = max(i.get("num_threads", 1) for i in info) if info else os.cpu_count()
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
+    d = cfg.d
+    if tokens is None:
+        tokens = int(min(16384, max(256, 1.2e12 / d ** 2)) // 256 * 256)
+    if rows is None:
+        rows = int(min(512, max(16, 2e11 / d ** 2)))
     rows = min(rows, cfg.m)
     tokens = min(tokens, cfg.n_tokens)
+    d_s = min(d, 6144)
     xs = x[:tokens].cpu().numpy()
     ws = w[:rows].double().cpu().numpy()
     t0 = time.perf_counter()
     h = O.hessian([xs[i:i + 4096] for i in range(0, tokens, 4096)])
     t1 = time.perf_counter()
-    hd, _ = O.damp(h, cfg.damp)
+    hd, _ = O.damp(h[:d_s, :d_s], cfg.damp)
     u = O.inverse_hessian_factor(hd)
     t2 = time.perf_counter()
-    O.gptq_quantize(ws, u, cfg.bits, cfg.grid, cfg.group)
+    if d_s < d:
+        u = np.triu(np.full((d, d), 1e-3))
+        np.fill_diagonal(u, 1.0)
     t3 = time.perf_counter()
+    O.gptq_quantize(ws, u, cfg.bits, cfg.grid, cfg.group)
+    t4 = time.perf_counter()
     t_h = (t1 - t0) * cfg.n_tokens / tokens
-    t_chain = t2 - t1
-    t_loop = (t3 - t2) * cfg.m / rows
+    t_chain = (t2 - t1) * (d / d_s) ** 3
+    t_loop = (t4 - t3) * cfg.m / rows
     total = t_h + t_chain + t_loop
     return {
         "value": cfg.n_weights / total,
         "unit": "weights/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{cfg.name}: H over {tokens} of {cfg.n_tokens} tokens (x{cfg.n_tokens / tokens:g}), full fp64 "
-                   f"chain at d={cfg.d}, column loop on {rows} of {cfg.m} rows (x{cfg.m / rows:g}); measured "
-                   f"{t3 - t0:.1f} s, extrapolated {total:.1f} s per layer"),
+        "sample": (f"{cfg.name}: H over {tokens} of {cfg.n_tokens} tokens (x{cfg.n_tokens / tokens:g}); chain on "
+                   f"the leading {d_s}x{d_s} block (x{(d / d_s) ** 3:g}); column loop on {rows} of {cfg.m} rows "
+                   f"(x{cfg.m / rows:g}); measured {t1 - t0 + t2 - t1 + t4 - t3:.1f} s, extrapolated "
+                   f"{total:.1f} s per layer"),
         "stage_s": {"hessian": t_h, "chain": t_chain, "loop": t_loop},
         "cpu": platform.processor() or platform.machine(),
     }
@@ -146,12 +167,16 @@ def main():
     cfg = S.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     G.load_library()
+    _say(f"{cfg.name}: drawing W {cfg.m}x{cfg.d} and X {cfg.n_tokens}x{cfg.d}")
     w = S.make_weights(cfg, dev)
     x = S.make_activations(cfg, dev)
     torch.cuda.synchronize()
+    _say("inputs resident; allocating buffers")
     run = LayerRun(cfg, w, x)
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
         run.step()
+        torch.cuda.synchronize()
+        _say(f"warmup step {i + 1}/{args.warmup} done")
     torch.cuda.synchronize()
     if run.info is not None and int(run.info.item()) != 0:
         raise RuntimeError("H + lambda I not positive definite")
@@ -166,6 +191,7 @@ def main():
         for k, v in run.stage_ms().items():
             stage_acc[k] = stage_acc.get(k, 0.0) + v
         syrk_calls += run.syrk_call_ms()
+        _say(f"timed step done: {run.stage_ms()}")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage = {k: v / args.steps for k, v in stage_acc.items()}
@@ -204,6 +230,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
+        _say("timing the oracle on a bounded sample (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(cfg, w, x, args.cpu_sample_rows, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)
 

@@ -19,6 +19,10 @@ Recipe (all seeds derive from (config, layer, stream, chunk)):
   A = diag(s) Q^T with Q Haar-orthogonal (QR of a Gaussian, sign-fixed),
   s_k = c / k (k = 1..d) with c chosen so the mean channel variance is 1, and
   6 distinct channels (columns of A) scaled x20.
+  For d > 16384 (the OPT-175B fc2 input width) a dense Haar Q costs more than
+  the rest of the run, so Q = P2 B2 P1 B1 instead: B1, B2 block-diagonal with
+  Haar blocks of 4096, P1, P2 random permutations. The spectrum s is the same,
+  so the conditioning of H is too; only the mixing pattern is structured.
 
 Small configurations are drawn on the CPU (fp64, torch's CPU generator);
 large ones on the GPU (fp32 GEMM), which is fast and deterministic for a given
@@ -114,30 +118,86 @@ def make_weights(cfg: LayerConfig, device="cpu") -> torch.Tensor:
     return w.to(torch.float32 if cfg.w_dtype == "fp32" else torch.float16)
 
 
+STRUCTURED_D = 16384
+BLOCK_Q = 4096
+
+
+def _haar(n, gen, dev, work):
+    g = torch.randn(n, n, generator=gen, device=dev, dtype=work)
+    q, r = torch.linalg.qr(g)
+    return q * torch.sign(torch.diagonal(r)).unsqueeze(0)
+
+
+def _spectrum(d, dev, work):
+    k = torch.arange(1, d + 1, device=dev, dtype=work)
+    c = math.sqrt(d / float(torch.sum(1.0 / (k.double().cpu() ** 2))))
+    return c / k
+
+
+def _outlier_channels(cfg, dev):
+    gi = _gen(torch.device("cpu"), _seed(cfg, 3))
+    return torch.randperm(cfg.d, generator=gi)[:min(6, cfg.d)].to(dev)
+
+
 def mixing_matrix(cfg: LayerConfig, device="cpu") -> torch.Tensor:
-    """A = diag(s) Q^T with 6 outlier channels x20 (fp64 on CPU, fp32 on GPU)."""
+    """A = diag(s) Q^T with 6 outlier channels x20 (fp64 on CPU, fp32 on GPU);
+    dense Haar Q (d <= 16384 only)."""
     dev = torch.device(device)
     work = torch.float64 if dev.type == "cpu" else torch.float32
     d = cfg.d
-    g = torch.randn(d, d, generator=_gen(dev, _seed(cfg, 2)), device=dev, dtype=work)
-    q, r = torch.linalg.qr(g)
-    q = q * torch.sign(torch.diagonal(r)).unsqueeze(0)
-    k = torch.arange(1, d + 1, device=dev, dtype=work)
-    c = math.sqrt(d / float(torch.sum(1.0 / (k.double().cpu() ** 2))))
-    s = c / k
-    a = s.unsqueeze(1) * q.t()
-    gi = _gen(torch.device("cpu"), _seed(cfg, 3))
-    n_out = min(6, d)
-    chans = torch.randperm(d, generator=gi)[:n_out].to(dev)
-    a[:, chans] *= 20.0
+    assert d <= STRUCTURED_D, "the dense mixing matrix is only drawn up to d = 16384"
+    q = _haar(d, _gen(dev, _seed(cfg, 2)), dev, work)
+    a = _spectrum(d, dev, work).unsqueeze(1) * q.t()
+    a[:, _outlier_channels(cfg, dev)] *= 20.0
     return a.contiguous()
+
+
+class _StructuredMix:
+    """x -> x diag(s) Q^T with Q = P2 B2 P1 B1 (see the module docstring), then
+    the outlier channels x20; applied to row blocks of Z."""
+
+    def __init__(self, cfg, dev, work):
+        d = cfg.d
+        assert d % BLOCK_Q == 0
+        nb = d // BLOCK_Q
+        gq = _gen(dev, _seed(cfg, 2))
+        self.b1 = torch.stack([_haar(BLOCK_Q, gq, dev, work) for _ in range(nb)])
+        self.b2 = torch.stack([_haar(BLOCK_Q, gq, dev, work) for _ in range(nb)])
+        gp = _gen(torch.device("cpu"), _seed(cfg, 5))
+        self.p1 = torch.randperm(d, generator=gp).to(dev)
+        self.p2 = torch.randperm(d, generator=gp).to(dev)
+        self.s = _spectrum(d, dev, work)
+        self.chans = _outlier_channels(cfg, dev)
+        self.nb = nb
+
+    def _blockmul_t(self, y, b):
+        # y [t, d] times blockdiag(b)^T
+        t = y.shape[0]
+        yb = y.view(t, self.nb, BLOCK_Q).transpose(0, 1)           # [nb, t, 4096]
+        out = torch.bmm(yb, b.transpose(1, 2).contiguous())         # [nb, t, 4096]
+        return out.transpose(0, 1).reshape(t, -1)
+
+    def __call__(self, z):
+        # Q^T = B1^T P1^T B2^T P2^T; a permutation P (x P = x[:, perm]) acts
+        # on the right as a column gather
+        y = z * self.s
+        y = self._blockmul_t(y, self.b1)
+        y = y[:, torch.argsort(self.p1)]
+        y = self._blockmul_t(y, self.b2)
+        y = y[:, torch.argsort(self.p2)]
+        y[:, self.chans] *= 20.0
+        return y
 
 
 def make_activations(cfg: LayerConfig, device="cpu", out=None) -> torch.Tensor:
     """X [N, d] fp16, token-major, drawn sequence by sequence."""
     dev = torch.device(device)
     work = torch.float64 if dev.type == "cpu" else torch.float32
-    a = mixing_matrix(cfg, dev)
+    if cfg.d > STRUCTURED_D:
+        mix = _StructuredMix(cfg, dev, work)
+    else:
+        a = mixing_matrix(cfg, dev)
+        mix = lambda z: z @ a  # noqa: E731
     n = cfg.n_tokens
     if out is None:
         out = torch.empty(n, cfg.d, dtype=torch.float16, device=dev)
@@ -146,7 +206,7 @@ def make_activations(cfg: LayerConfig, device="cpu", out=None) -> torch.Tensor:
         t1 = min(t0 + seq, n)
         z = torch.randn(t1 - t0, cfg.d, generator=_gen(dev, _seed(cfg, 4, t0 // seq)),
                         device=dev, dtype=work)
-        out[t0:t1] = (z @ a).to(torch.float16)
+        out[t0:t1] = mix(z).to(torch.float16)
     return out
 
 
