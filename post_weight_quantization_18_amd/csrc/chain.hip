@@ -40,6 +40,13 @@ struct ChainWs {
   double* lam;   // 1
 };
 
+// Outer panel width of the Cholesky: 8 NB panels (512 columns) per delayed
+// trailing update.
+int64_t chain_outer_panel(int64_t d) {
+  (void)d;
+  return 8 * NB;
+}
+
 // Largest merge size s (a power-of-two multiple of NB with s < d).
 int64_t chain_smax(int64_t d) {
   int64_t s = NB;
@@ -269,41 +276,72 @@ __global__ __launch_bounds__(256) void trsm_rows_kernel(double* A, int64_t d, in
       }
 }
 
-// C[i][j] -= sum_k P[i][k] P[j][k] for the lower 64x64 tiles of the trailing
-// matrix (rows/cols >= c0), P = A[:, k0:k0+NB]. fp64 MFMA 16x16x4.
-// Diagonal tiles update only j <= i so the upper triangle stays zero.
-__global__ __launch_bounds__(256) void syrk_f64_kernel(double* A, int64_t d, int64_t k0, int64_t c0) {
-  __shared__ double Pi[64][NB + 1];
-  __shared__ double Bs[NB][64 + 1];  // Bs[k][j] = P[j][k]
-  const int t = blockIdx.x;
-  int ti = (int)((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
-  while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-  while (ti * (ti + 1) / 2 > t) --ti;
-  const int tj = t - ti * (ti + 1) / 2;
+// Delayed Cholesky update: A[i][j] -= sum_{k in [ka, ka + K)} A[i][k] A[j][k]
+// for i in [c0, d), j in [c0, c1), j <= i (the strictly upper triangle stays
+// zero). 64 x 64 tiles (4 waves of 32 x 32, fp64 MFMA 16x16x4), K staged 32
+// columns at a time through LDS with the next slice prefetched into registers.
+// tri = 1: c1 = d and blockIdx.x enumerates the lower triangle of tiles;
+// tri = 0: grid (column tiles, row tiles), tiles above the diagonal exit.
+__global__ __launch_bounds__(256) void update_f64_kernel(double* A, int64_t d, int64_t ka, int64_t K, int64_t c0,
+                                                         int64_t c1, int tri) {
+  constexpr int KT = 32;
+  __shared__ double As[64][KT + 1];
+  __shared__ double Bs[KT][64 + 1];
+  int ti, tj;
+  if (tri) {
+    const int t = blockIdx.x;
+    ti = (int)((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
+    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+    while (ti * (ti + 1) / 2 > t) --ti;
+    tj = t - ti * (ti + 1) / 2;
+  } else {
+    tj = blockIdx.x;
+    ti = blockIdx.y;
+    if (ti < tj) return;  // uniform per workgroup
+  }
   const int64_t i0 = c0 + (int64_t)ti * 64, j0 = c0 + (int64_t)tj * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int idx = tid; idx < 64 * NB; idx += 256) {
-    const int r = idx / NB, c = idx % NB;
-    Pi[r][c] = (i0 + r < d) ? A[(i0 + r) * d + k0 + c] : 0.0;
-    Bs[c][r] = (j0 + r < d) ? A[(j0 + r) * d + k0 + c] : 0.0;
-  }
-  __syncthreads();
   const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
   double4v acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = (double4v){0.0, 0.0, 0.0, 0.0};
-  mfma_f64_block<NB>(Pi, Bs, wr, wc, lane, acc);
+    for (int y = 0; y < 2; ++y) acc[x][y] = (double4v){0.0, 0.0, 0.0, 0.0};
+  const int64_t ke = ka + K;
+  // each thread stages 8 elements of each 64 x KT panel, rows idx / KT, columns idx % KT
+  double pa[8], pb[8];
+  auto fetch = [&](int64_t k) __attribute__((always_inline)) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e;
+      const int r = idx / KT, c = idx % KT;
+      const int64_t gk = k + c;
+      pa[e] = (i0 + r < d && gk < ke) ? A[(i0 + r) * d + gk] : 0.0;
+      pb[e] = (j0 + r < c1 && gk < ke) ? A[(j0 + r) * d + gk] : 0.0;
+    }
+  };
+  fetch(ka);
+  for (int64_t k = ka; k < ke; k += KT) {
+    __syncthreads();
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e;
+      As[idx / KT][idx % KT] = pa[e];
+      Bs[idx % KT][idx / KT] = pb[e];
+    }
+    __syncthreads();
+    if (k + KT < ke) fetch(k + KT);
+    mfma_f64_block<KT>(As, Bs, wr, wc, lane, acc);
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t i = i0 + wr + a * 16 + (lane >> 4) + 4 * r;
-        const int64_t j = j0 + wc + b * 16 + (lane & 15);
-        if (i < d && j < d && j <= i) A[i * d + j] -= acc[a][b][r];
+        const int64_t i = i0 + wr + x * 16 + (lane >> 4) + 4 * r;
+        const int64_t j = j0 + wc + y * 16 + (lane & 15);
+        if (i < d && j < c1 && j <= i) A[i * d + j] -= acc[x][y][r];
       }
 }
 
@@ -425,19 +463,36 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
   hipLaunchKernelGGL(load_reversed_kernel, dim3((unsigned)nt32, (unsigned)nt32), dim3(256), 0, st, H, h_f64, d,
                      ldh, (const double*)w.lam, w.A);
   GPTQ_CHECK_LAUNCH();
+  // Blocked right-looking Cholesky in two levels: NB-wide panels are factored
+  // (potf2 + trsm) inside outer panels of CP columns, each NB panel updating
+  // only the rest of its outer panel; the trailing matrix receives one update
+  // of depth CP per outer panel, so it is read and written d / CP times instead
+  // of d / NB times.
   const int64_t nblk = ceil_div(d, NB);
-  for (int64_t k = 0; k < nblk; ++k) {
-    const int64_t k0 = k * NB;
-    hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(64), 0, st, w.A, d, k0, w.Dinv, info);
-    GPTQ_CHECK_LAUNCH();
-    const int64_t rest = d - k0 - NB;
-    if (rest <= 0) break;
-    const int64_t rb = ceil_div(rest, 64);
-    hipLaunchKernelGGL(trsm_rows_kernel, dim3((unsigned)rb), dim3(256), 0, st, w.A, d, k0, (const double*)w.Dinv);
-    GPTQ_CHECK_LAUNCH();
-    hipLaunchKernelGGL(syrk_f64_kernel, dim3((unsigned)(rb * (rb + 1) / 2)), dim3(256), 0, st, w.A, d, k0,
-                       k0 + NB);
-    GPTQ_CHECK_LAUNCH();
+  const int64_t CP = chain_outer_panel(d);
+  for (int64_t p0 = 0; p0 < d; p0 += CP) {
+    const int64_t pe = p0 + CP < d ? p0 + CP : d;
+    for (int64_t k0 = p0; k0 < pe; k0 += NB) {
+      hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(64), 0, st, w.A, d, k0, w.Dinv, info);
+      GPTQ_CHECK_LAUNCH();
+      const int64_t rest = d - k0 - NB;
+      if (rest <= 0) break;
+      const int64_t rb = ceil_div(rest, 64);
+      hipLaunchKernelGGL(trsm_rows_kernel, dim3((unsigned)rb), dim3(256), 0, st, w.A, d, k0, (const double*)w.Dinv);
+      GPTQ_CHECK_LAUNCH();
+      if (k0 + NB < pe) {
+        const int64_t c0 = k0 + NB;
+        dim3 grid((unsigned)ceil_div(pe - c0, 64), (unsigned)ceil_div(d - c0, 64));
+        hipLaunchKernelGGL(update_f64_kernel, grid, dim3(256), 0, st, w.A, d, k0, (int64_t)NB, c0, pe, 0);
+        GPTQ_CHECK_LAUNCH();
+      }
+    }
+    if (pe < d) {
+      const int64_t rb = ceil_div(d - pe, 64);
+      hipLaunchKernelGGL(update_f64_kernel, dim3((unsigned)(rb * (rb + 1) / 2)), dim3(256), 0, st, w.A, d, p0,
+                         pe - p0, pe, d, 1);
+      GPTQ_CHECK_LAUNCH();
+    }
   }
   hipLaunchKernelGGL(put_diag_inverse_kernel, dim3((unsigned)nblk), dim3(256), 0, st, w.A, d,
                      (const double*)w.Dinv);

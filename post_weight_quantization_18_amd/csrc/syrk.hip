@@ -37,8 +37,17 @@ constexpr int TI = 256;            // tile rows (i features)
 constexpr int TJ = 128;            // tile cols (j features)
 constexpr int KS = GPTQ_SYRK_KS;   // tokens per LDS stage
 constexpr int FOLD = 1024 / KS;    // stages between error folds (1024 tokens)
-constexpr int NT = 512;            // threads per workgroup (8 waves)
+#ifndef GPTQ_SYRK_WAVES
+#define GPTQ_SYRK_WAVES 8
+#endif
+constexpr int NW = GPTQ_SYRK_WAVES;   // waves per workgroup: 2 columns of 64 x (NW/2) row bands
+constexpr int NT = 64 * NW;           // threads per workgroup
+constexpr int FI = TI / (NW / 2) / 32;  // 32-row subtiles per wave (2 or 4)
+constexpr int RW = KS / NW;           // token rows each wave moves per stage
+constexpr int EI = RW / 2;            // I-tile DMA instructions per wave per stage (2 rows each)
+constexpr int EJ = RW / 4;            // J-tile DMA instructions per wave per stage (4 rows each)
 constexpr int NBUF = GPTQ_SYRK_NBUF;  // LDS ring depth
+static_assert(EI % (KS / 16) == 0 && (EJ % (KS / 16) == 0 || EJ < KS / 16), "DMA spread over the slices");
 
 
 // Source of the DMA for rows past the token range or features past d: every
@@ -99,55 +108,55 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   const int nstages = tok1 > tok0 ? (int)((tok1 - tok0 + KS - 1) / KS) : 0;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wi = w >> 1, wj = w & 1;  // wave tile: rows 64 wi .. +63, cols 64 wj .. +63
+  const int wi = w >> 1, wj = w & 1;  // wave tile: rows 32 FI wi .. + 32 FI - 1, cols 64 wj .. +63
   const bool j_in_i = (J0 >= I0) && (J0 < I0 + TI);
 
   // ---- DMA of one stage (tokens t0 .. t0+63) into ring buffer b ----
-  // I tile: wave w, instruction e covers rows 8w + 2e + {0, 1} (1 KB); lane l
-  // takes row 8w + 2e + l/32 and LDS chunk position l%32, holding feature
+  // I tile: wave w, instruction e covers rows RW w + 2e + {0, 1} (1 KB); lane l
+  // takes row RW w + 2e + l/32 and LDS chunk position l%32, holding feature
   // chunk (l%32) ^ 4 (row mod 4). The swizzle depends on e only through e&1.
-  // J tile: instruction e covers rows 8w + 4e + {0..3}; lane l takes row
-  // 8w + 4e + l/16 and position l%16 (swizzle independent of e).
+  // J tile: instruction e covers rows RW w + 4e + {0..3}; lane l takes row
+  // RW w + 4e + l/16 and position l%16 (swizzle independent of e).
   const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index, in an SGPR
   const int rI = lane >> 5, pI = lane & 31, rJ = lane >> 4, pJ = lane & 15;
   const int cI0 = pI ^ (4 * (rI & 3)), cI1 = pI ^ (4 * ((2 + rI) & 3));
   const int cJ = pJ ^ (4 * (rJ & 3));
   const bool okI0 = I0 + 8 * cI0 < a.d, okI1 = I0 + 8 * cI1 < a.d, okJ = J0 + 8 * cJ < a.d;
-  const int64_t offI0 = (int64_t)(8 * w + rI) * a.ldx + I0 + 8 * cI0;
-  const int64_t offI1 = (int64_t)(8 * w + rI) * a.ldx + I0 + 8 * cI1;
-  const int64_t offJ = (int64_t)(8 * w + rJ) * a.ldx + J0 + 8 * cJ;
+  const int64_t offI0 = (int64_t)(RW * w + rI) * a.ldx + I0 + 8 * cI0;
+  const int64_t offI1 = (int64_t)(RW * w + rI) * a.ldx + I0 + 8 * cI1;
+  const int64_t offJ = (int64_t)(RW * w + rJ) * a.ldx + J0 + 8 * cJ;
   const bool tile_inside = (I0 + TI <= a.d) && (J0 + TJ <= a.d);
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GPTQ_LDS void*)ring);
   constexpr uint32_t STAGE_BYTES = KS * (TI + TJ) * 2;
-  // instruction e (0..3) of the I tile and (0..1) of the J tile for the stage
-  // starting at token t0 into ring buffer b
-  auto issue_I = [&](int e, int64_t t0, int b, bool full) {
-    // row 8w + 2e + l/32; offI0 / offI1 carry row 8w + l/32 and the chunk swizzle of
-    // the row's parity class (e even / odd)
+  // instruction e (0 .. EI-1) of the I tile and (0 .. EJ-1) of the J tile for
+  // the stage starting at token t0 into ring buffer b
+  auto issue_I = [&](int e, int64_t t0, int b, bool full) __attribute__((always_inline)) {
+    // row RW w + 2e + l/32; offI0 / offI1 carry row RW w + l/32 and the chunk
+    // swizzle of the row's parity class (e even / odd)
     const half_t* src = a.X + t0 * a.ldx + (int64_t)(2 * e) * a.ldx + ((e & 1) ? offI1 : offI0);
     if (!full) {
       const int rows = (int)((tok1 - t0) < KS ? (tok1 - t0) : KS);
-      const bool ok = ((e & 1) ? okI1 : okI0) && (8 * w + 2 * e + rI) < rows;
+      const bool ok = ((e & 1) ? okI1 : okI0) && (RW * w + 2 * e + rI) < rows;
       if (!ok) src = (const half_t*)kZero16;
     }
-    dma16(src, ring_lds + b * STAGE_BYTES + (uint32_t)((8 * wu + 2 * e) * TI * 2));
+    dma16(src, ring_lds + b * STAGE_BYTES + (uint32_t)((RW * wu + 2 * e) * TI * 2));
   };
-  auto issue_J = [&](int e, int64_t t0, int b, bool full) {
+  auto issue_J = [&](int e, int64_t t0, int b, bool full) __attribute__((always_inline)) {
     const half_t* src = a.X + t0 * a.ldx + (int64_t)(4 * e) * a.ldx + offJ;
     if (!full) {
       const int rows = (int)((tok1 - t0) < KS ? (tok1 - t0) : KS);
-      const bool ok = okJ && (8 * w + 4 * e + rJ) < rows;
+      const bool ok = okJ && (RW * w + 4 * e + rJ) < rows;
       if (!ok) src = (const half_t*)kZero16;
     }
-    dma16(src, ring_lds + b * STAGE_BYTES + KS * TI * 2 + (uint32_t)((8 * wu + 4 * e) * TJ * 2));
+    dma16(src, ring_lds + b * STAGE_BYTES + KS * TI * 2 + (uint32_t)((RW * wu + 4 * e) * TJ * 2));
   };
-  auto issue = [&](int64_t t0, int b) {
+  auto issue = [&](int64_t t0, int b) __attribute__((always_inline)) {
     const bool full = tile_inside && t0 + KS <= tok1;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) issue_I(e, t0, b, full);
+    for (int e = 0; e < EI; ++e) issue_I(e, t0, b, full);
     if (!j_in_i) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) issue_J(e, t0, b, full);
+      for (int e = 0; e < EJ; ++e) issue_J(e, t0, b, full);
     }
   };
 
@@ -157,17 +166,17 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   const int g = lane >> 4, e4 = (lane >> 2) & 3, q = lane & 3;
   const int tokoff = 8 * (g >> 1) + e4;
   const int sub = 2 * (g & 1) + (q >> 1), halfsel = 4 * (q & 1);
-  int offA[2], offB[2];
+  int offA[FI], offB[2];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) offA[f] = tokoff * TI + (swz(tokoff, wi * 8 + 4 * f + sub) << 3) + halfsel;
+  for (int f = 0; f < FI; ++f) offA[f] = tokoff * TI + (swz(tokoff, wi * 4 * FI + 4 * f + sub) << 3) + halfsel;
   const int bpitch = j_in_i ? TI : TJ;
   const int bchunk0 = j_in_i ? (int)((J0 - I0) / 8) : 0;
 #pragma unroll
   for (int h = 0; h < 2; ++h) offB[h] = tokoff * bpitch + (swz(tokoff, bchunk0 + wj * 8 + 4 * h + sub) << 3) + halfsel;
 
-  float16v acc[2][2], outer[2][2];
+  float16v acc[FI][2], outer[FI][2];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < FI; ++f)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -182,46 +191,51 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   // four 16-token slices of stage s so that its address arithmetic overlaps the
   // matrix cores. Fragments run one slice ahead; scheduling barriers keep it to
   // one slice, which bounds the registers the reads occupy.
-  auto compute_from = [&](const half_t* bI, const half_t* bB, int bp, bool refill, int64_t t_next, int b_next) {
+  auto compute_from = [&](const half_t* bI, const half_t* bB, int bp, bool refill, int64_t t_next, int b_next) __attribute__((always_inline)) {
     const bool full = tile_inside && t_next + KS <= tok1;
-    half8 af[2][2], bf[2][2];
+    half8 af[2][FI], bf[2][2];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) af[0][f] = frag(bI + offA[f], TI);
+    for (int f = 0; f < FI; ++f) af[0][f] = frag(bI + offA[f], TI);
 #pragma unroll
     for (int h = 0; h < 2; ++h) bf[0][h] = frag(bB + offB[h], bp);
 #pragma unroll
     for (int kk = 0; kk < KS / 16; ++kk) {
       const int cur = kk & 1, nxt = cur ^ 1;
       if (refill) {
-        issue_I(kk, t_next, b_next, full);
-        if (!j_in_i && kk < 2) issue_J(kk, t_next, b_next, full);
+        constexpr int PI = EI / (KS / 16), PJ = EJ >= KS / 16 ? EJ / (KS / 16) : 1;
+#pragma unroll
+        for (int e = 0; e < PI; ++e) issue_I(kk * PI + e, t_next, b_next, full);
+        if (!j_in_i && kk * PJ < EJ) {
+#pragma unroll
+          for (int e = 0; e < PJ; ++e) issue_J(kk * PJ + e, t_next, b_next, full);
+        }
       }
       if (kk + 1 < KS / 16) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) af[nxt][f] = frag(bI + offA[f] + (kk + 1) * 16 * TI, TI);
+        for (int f = 0; f < FI; ++f) af[nxt][f] = frag(bI + offA[f] + (kk + 1) * 16 * TI, TI);
 #pragma unroll
         for (int h = 0; h < 2; ++h) bf[nxt][h] = frag(bB + offB[h] + (kk + 1) * 16 * bp, bp);
       }
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < FI; ++f)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           acc[f][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][f], bf[cur][h], acc[f][h], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto compute = [&](const half_t* bI, const half_t* bJ, bool refill, int64_t t_next, int b_next) {
+  auto compute = [&](const half_t* bI, const half_t* bJ, bool refill, int64_t t_next, int b_next) __attribute__((always_inline)) {
     if (j_in_i)
       compute_from(bI, bI, TI, refill, t_next, b_next);
     else
       compute_from(bI, bJ, TJ, refill, t_next, b_next);
   };
-  auto fold = [&]() {
+  auto fold = [&]() __attribute__((always_inline)) {
     // Fast2Sum(outer, acc): outer <- fl(outer + acc), acc <- exact residual.
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < FI; ++f)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float o = outer[f][h][r], c = acc[f][h][r];
@@ -230,9 +244,12 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
           acc[f][h][r] = c - z;
           outer[f][h][r] = sum;
         }
+        // one 32 x 32 sub-tile at a time keeps the temporaries to 16 registers
+        __builtin_amdgcn_sched_barrier(0);
+      }
   };
-  auto stage_i = [&](int b) { return ring + b * KS * (TI + TJ); };
-  auto stage_j = [&](int b) { return ring + b * KS * (TI + TJ) + KS * TI; };
+  auto stage_i = [&](int b) __attribute__((always_inline)) { return ring + b * KS * (TI + TJ); };
+  auto stage_j = [&](int b) __attribute__((always_inline)) { return ring + b * KS * (TI + TJ) + KS * TI; };
 
   if (nstages > 0) issue(tok0, 0);
   if (nstages > 1) issue(tok0 + KS, 1);
@@ -244,9 +261,9 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
     if (s + 1 >= nstages)
       __builtin_amdgcn_s_waitcnt(WAIT_VM0);
     else if (j_in_i)
-      __builtin_amdgcn_s_waitcnt(WAIT_VM4);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | EI);  // vmcnt(EI)
     else
-      __builtin_amdgcn_s_waitcnt(WAIT_VM6);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (EI + EJ));  // vmcnt(EI + EJ)
     lds_barrier();
     const int nxt = cur == 0 ? NBUF - 1 : cur - 1;  // (cur + 2) mod 3
     compute(stage_i(cur), stage_j(cur), s + 2 < nstages, tok0 + (int64_t)(s + 2) * KS, nxt);
@@ -257,12 +274,12 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   // ---- epilogue ----
   const int hl = lane >> 5, col = lane & 31;
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < FI; ++f)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int li = wi * 64 + f * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const int li = wi * 32 * FI + f * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
         const int lj = wj * 64 + h * 32 + col;
         const double v = 2.0 * ((double)outer[f][h][r] + (double)acc[f][h][r]);
         if (a.direct) {
