@@ -125,102 +125,160 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const void* H, int h
   }
 }
 
-// Factor the diagonal block at k0 (lower Cholesky) with one wave: lane r holds
-// row r in registers; column values are exchanged through LDS broadcasts.
+// Factor the 64 x 64 diagonal block at k0 (lower Cholesky) and invert the
+// factor, in one workgroup of 4 waves, blocked by 16 columns so that only the
+// 16-column leaves are serial:
+//   for each 16-block kb: (1) one wave factors the 16 x 16 diagonal leaf, a row
+//   per lane in registers; each step broadcasts the current column through LDS
+//   (one write, one batch of reads) and takes the pivot's inverse square root
+//   (v_rsq_f64 + two Newton steps), then the same wave inverts the leaf by
+//   forward substitution; (2) all threads solve the rows below against the
+//   leaf's inverse; (3) all threads apply the rank-16 update to the rest.
+// The off-diagonal 16-blocks of L^-1 follow from the diagonal ones block-row by
+// block-row: Li[I][J] = -Li[I][I] sum_{K=J}^{I-1} L[I][K] Li[K][J].
 // Writes L11 back with a zero upper triangle and L11^-1 to Dinv.
 // info <- first failing order (k0 + c + 1).
-struct Potf2Row {
-  double v[NB];
-};
+constexpr int LEAF = 16;
 
-template <int C>
-__device__ __forceinline__ void potf2_step(Potf2Row& row, double* col, int lane, bool& failed, int nb, int64_t k0,
-                                           int32_t* info) {
-  // broadcast column C of the current matrix
-  col[lane] = row.v[C];
-  __syncthreads();
-  double piv = col[C];
-  if (!(piv > 0.0)) {
-    if (!failed && C < nb && lane == 0 && *info == 0) *info = (int32_t)(k0 + C + 1);
-    failed = true;
-    piv = 1.0;
-  }
-  piv = sqrt(piv);
-  const double l = row.v[C] / piv;  // L[lane][C] for lane > C
-  __syncthreads();
-  col[lane] = l;
-  __syncthreads();
-  if (lane == C) row.v[C] = piv;
-  if (lane > C) row.v[C] = l;
-  // trailing update of this lane's row; entries right of the diagonal are
-  // never read and are zeroed on write-back
-#pragma unroll
-  for (int k = C + 1; k < NB; ++k) row.v[k] = fma(-l, col[k], row.v[k]);
+// 1 / sqrt(p) to fp64 accuracy for p > 0 (hardware estimate + two Newton steps).
+__device__ __forceinline__ double rsqrt_f64(double p) {
+  double y = __builtin_amdgcn_rsq(p);
+  y = y * (1.5 - 0.5 * p * y * y);
+  y = y * (1.5 - 0.5 * p * y * y);
+  return y;
 }
 
-template <int... Cs>
-__device__ __forceinline__ void potf2_all(std::integer_sequence<int, Cs...>, Potf2Row& row, double* col, int lane,
-                                          bool& failed, int nb, int64_t k0, int32_t* info) {
-  (potf2_step<Cs>(row, col, lane, failed, nb, k0, info), ...);
-}
-
-// Li = L^-1, lane j owns column j: Li[r][j] = -(sum_{k<r} L[r][k] Li[k][j]) / L[r][r]
-// (Li[k][j] = 0 for k < j, so every lane runs the same loop).
-template <int R>
-__device__ __forceinline__ void inv_step(Potf2Row& li, const double (*L)[NB + 1], int lane) {
-  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-#pragma unroll
-  for (int k = 0; k + 3 < R; k += 4) {
-    s0 = fma(L[R][k], li.v[k], s0);
-    s1 = fma(L[R][k + 1], li.v[k + 1], s1);
-    s2 = fma(L[R][k + 2], li.v[k + 2], s2);
-    s3 = fma(L[R][k + 3], li.v[k + 3], s3);
-  }
-#pragma unroll
-  for (int k = R & ~3; k < R; ++k) s0 = fma(L[R][k], li.v[k], s0);
-  const double diag = L[R][R];
-  li.v[R] = (lane == R) ? 1.0 / diag : (lane < R ? -((s0 + s1) + (s2 + s3)) / diag : 0.0);
-}
-
-template <int... Rs>
-__device__ __forceinline__ void inv_all(std::integer_sequence<int, Rs...>, Potf2Row& li, const double (*L)[NB + 1],
-                                        int lane) {
-  (inv_step<Rs>(li, L, lane), ...);
-}
-
-__global__ __launch_bounds__(64) void potf2_kernel(double* A, int64_t d, int64_t k0, double* Dinv,
+__global__ __launch_bounds__(256) void potf2_kernel(double* A, int64_t d, int64_t k0, double* Dinv,
                                                    int32_t* info) {
   __shared__ double L[NB][NB + 1];
+  __shared__ double Li[NB][NB + 1];
+  __shared__ double tmp[3][LEAF][LEAF + 1];
   __shared__ double col[NB];
+  __shared__ double rdiag[NB];
   const int nb = (int)((d - k0) < NB ? (d - k0) : NB);
-  const int lane = threadIdx.x;
-  for (int idx = lane; idx < NB * NB; idx += 64) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int idx = tid; idx < NB * NB; idx += 256) {
     const int r = idx / NB, c = idx % NB;
     double v = 0.0;
     if (r < nb && c < nb && c <= r) v = A[(k0 + r) * d + k0 + c];
     if (r >= nb && r == c) v = 1.0;  // identity padding beyond the matrix
     L[r][c] = v;
+    Li[r][c] = 0.0;
   }
   __syncthreads();
-  Potf2Row row;
-#pragma unroll
-  for (int c = 0; c < NB; ++c) row.v[c] = L[lane][c];
   bool failed = false;
-  potf2_all(std::make_integer_sequence<int, NB>{}, row, col, lane, failed, nb, k0, info);
-  __syncthreads();
+  for (int b0 = 0; b0 < NB; b0 += LEAF) {
+    // ---- (1) leaf: factor and invert the 16 x 16 diagonal block (wave 0) ----
+    if (w == 0) {
+      const int i = lane & (LEAF - 1);
+      double r[LEAF];
 #pragma unroll
-  for (int c = 0; c < NB; ++c) L[lane][c] = (c <= lane) ? row.v[c] : 0.0;
-  __syncthreads();
-  Potf2Row li;
-  inv_all(std::make_integer_sequence<int, NB>{}, li, L, lane);
-  for (int idx = lane; idx < NB * NB; idx += 64) {
-    const int r = idx / NB, c = idx % NB;
-    if (r < nb && c < nb) A[(k0 + r) * d + k0 + c] = L[r][c];
+      for (int j = 0; j < LEAF; ++j) r[j] = L[b0 + i][b0 + j];  // zeros above the diagonal
+#pragma unroll
+      for (int c = 0; c < LEAF; ++c) {
+        col[lane] = r[c];  // column c of the current leaf: lane j holds A[j][c]
+        double cv[LEAF];
+#pragma unroll
+        for (int j = c; j < LEAF; ++j) cv[j] = col[j];
+        double p = cv[c];
+        if (!(p > 0.0)) {
+          if (!failed && b0 + c < nb && lane == 0 && *info == 0) *info = (int32_t)(k0 + b0 + c + 1);
+          failed = true;
+          p = 1.0;
+        }
+        const double rs = rsqrt_f64(p);
+        const double lc = r[c] * rs;  // L[i][c]
+        r[c] = lc;
+        if (lane == 0) rdiag[b0 + c] = rs;
+#pragma unroll
+        for (int j = c + 1; j < LEAF; ++j) r[j] = fma(-lc, cv[j] * rs, r[j]);
+      }
+      if (lane < LEAF) {
+#pragma unroll
+        for (int j = 0; j < LEAF; ++j) L[b0 + i][b0 + j] = (j <= i) ? r[j] : 0.0;
+      }
+      // forward substitution, lane j owning column j of the leaf's inverse:
+      // x[rr] = (delta(rr, j) - sum_{k < rr} L[rr][k] x[k]) / L[rr][rr]
+      double x[LEAF];
+#pragma unroll
+      for (int rr = 0; rr < LEAF; ++rr) {
+        double lr[LEAF];
+#pragma unroll
+        for (int k = 0; k < rr; ++k) lr[k] = L[b0 + rr][b0 + k];
+        double s0 = (rr == i) ? 1.0 : 0.0, s1 = 0.0;
+#pragma unroll
+        for (int k = 0; k < rr; ++k) {
+          if (k & 1)
+            s1 = fma(-lr[k], x[k], s1);
+          else
+            s0 = fma(-lr[k], x[k], s0);
+        }
+        x[rr] = (s0 + s1) * rdiag[b0 + rr];
+      }
+      if (lane < LEAF) {
+#pragma unroll
+        for (int rr = 0; rr < LEAF; ++rr) Li[b0 + rr][b0 + i] = (rr >= i) ? x[rr] : 0.0;
+      }
+    }
+    __syncthreads();
+    const int rows = NB - b0 - LEAF;  // rows below the leaf
+    if (rows <= 0) break;
+    // ---- (2) rows below: L[R][b0 + c] = sum_{k <= c} A[R][b0 + k] Li[b0 + c][b0 + k] ----
+    double out[3];
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      const int idx = tid + 256 * e;
+      out[e] = 0.0;
+      if (idx < rows * LEAF) {
+        const int R = b0 + LEAF + idx / LEAF, c = idx % LEAF;
+        double s = 0.0;
+#pragma unroll
+        for (int k = 0; k < LEAF; ++k) s = fma(L[R][b0 + k], Li[b0 + c][b0 + k], s);
+        out[e] = s;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      const int idx = tid + 256 * e;
+      if (idx < rows * LEAF) L[b0 + LEAF + idx / LEAF][b0 + idx % LEAF] = out[e];
+    }
+    __syncthreads();
+    // ---- (3) rank-16 update of the lower part of the rest ----
+    for (int idx = tid; idx < rows * rows; idx += 256) {
+      const int R = b0 + LEAF + idx / rows, C = b0 + LEAF + idx % rows;
+      if (C > R) continue;
+      double s = 0.0;
+#pragma unroll
+      for (int k = 0; k < LEAF; ++k) s = fma(L[R][b0 + k], L[C][b0 + k], s);
+      L[R][C] -= s;
+    }
+    __syncthreads();
   }
-  // Dinv row r, column lane = li.v[r] (lane owns column lane)
+  // ---- off-diagonal blocks of L^-1, block-row by block-row ----
+  for (int I = 1; I < NB / LEAF; ++I) {
+    // tmp[J] = sum_{K=J}^{I-1} L[I][K] Li[K][J] for J < I
+    for (int idx = tid; idx < I * LEAF * LEAF; idx += 256) {
+      const int J = idx / (LEAF * LEAF), r = (idx / LEAF) % LEAF, c = idx % LEAF;
+      double s = 0.0;
+      for (int k = J * LEAF; k < I * LEAF; ++k) s = fma(L[I * LEAF + r][k], Li[k][J * LEAF + c], s);
+      tmp[J][r][c] = s;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < I * LEAF * LEAF; idx += 256) {
+      const int J = idx / (LEAF * LEAF), r = (idx / LEAF) % LEAF, c = idx % LEAF;
+      double s = 0.0;
 #pragma unroll
-  for (int r = 0; r < NB; ++r)
-    if (k0 + r < d) Dinv[(k0 + r) * NB + lane] = (r < nb && lane < nb && lane <= r) ? li.v[r] : 0.0;
+      for (int k = 0; k < LEAF; ++k) s = fma(Li[I * LEAF + r][I * LEAF + k], tmp[J][k][c], s);
+      Li[I * LEAF + r][J * LEAF + c] = -s;
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < NB * NB; idx += 256) {
+    const int r = idx / NB, c = idx % NB;
+    if (r < nb && c < nb) A[(k0 + r) * d + k0 + c] = (c <= r) ? L[r][c] : 0.0;
+    if (k0 + r < d) Dinv[(k0 + r) * NB + c] = (r < nb && c < nb && c <= r) ? Li[r][c] : 0.0;
+  }
 }
 
 // One 64x64 fp64 MFMA tile step: acc[2][2] += As[rows][k..k+15] * Bs[k..k+15][cols]
@@ -473,7 +531,7 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
   for (int64_t p0 = 0; p0 < d; p0 += CP) {
     const int64_t pe = p0 + CP < d ? p0 + CP : d;
     for (int64_t k0 = p0; k0 < pe; k0 += NB) {
-      hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(64), 0, st, w.A, d, k0, w.Dinv, info);
+      hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(256), 0, st, w.A, d, k0, w.Dinv, info);
       GPTQ_CHECK_LAUNCH();
       const int64_t rest = d - k0 - NB;
       if (rest <= 0) break;
