@@ -21,6 +21,8 @@
 //    MFMA accumulator, so the partial sum is carried to ~2^-48 relative; the
 //    final value is outer + acc in fp64, and split-K partials are summed in a
 //    fixed order in fp64 (deterministic).
+#include <type_traits>
+
 #include "common.h"
 
 namespace gptq {
@@ -224,12 +226,6 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto compute = [&](const half_t* bI, const half_t* bJ, bool refill, int64_t t_next, int b_next) __attribute__((always_inline)) {
-    if (j_in_i)
-      compute_from(bI, bI, TI, refill, t_next, b_next);
-    else
-      compute_from(bI, bJ, TJ, refill, t_next, b_next);
-  };
   auto fold = [&]() __attribute__((always_inline)) {
     // Fast2Sum(outer, acc): outer <- fl(outer + acc), acc <- exact residual.
 #pragma unroll
@@ -253,23 +249,36 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
 
   if (nstages > 0) issue(tok0, 0);
   if (nstages > 1) issue(tok0 + KS, 1);
-  int cur = 0;
-  for (int s = 0; s < nstages; ++s) {
-    // wait for this stage's DMA (the next stage's 4 or 6 loads per thread may
-    // stay in flight), barrier, then run the matrix cores while refilling the
-    // buffer the previous stage used.
-    if (s + 1 >= nstages)
-      __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-    else if (j_in_i)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | EI);  // vmcnt(EI)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (EI + EJ));  // vmcnt(EI + EJ)
-    lds_barrier();
-    const int nxt = cur == 0 ? NBUF - 1 : cur - 1;  // (cur + 2) mod 3
-    compute(stage_i(cur), stage_j(cur), s + 2 < nstages, tok0 + (int64_t)(s + 2) * KS, nxt);
-    if ((s + 1) % FOLD == 0) fold();
-    cur = cur == NBUF - 1 ? 0 : cur + 1;
-  }
+  // The stage loop is instantiated once per tile kind (diagonal tiles read B
+  // from the I buffer): a branch inside the loop would make the compiler merge
+  // the accumulators of the two paths with register copies on every stage.
+  auto stage_loop = [&](auto diag_tag) __attribute__((always_inline)) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
+    int cur = 0;
+    for (int s = 0; s < nstages; ++s) {
+      // wait for this stage's DMA (the next stage's loads may stay in flight),
+      // barrier, then run the matrix cores while refilling the buffer the
+      // previous stage used.
+      if (s + 1 >= nstages)
+        __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+      else if (DIAG)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | EI);  // vmcnt(EI)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (EI + EJ));  // vmcnt(EI + EJ)
+      lds_barrier();
+      const int nxt = cur == 0 ? NBUF - 1 : cur - 1;  // (cur + 2) mod 3
+      if (DIAG)
+        compute_from(stage_i(cur), stage_i(cur), TI, s + 2 < nstages, tok0 + (int64_t)(s + 2) * KS, nxt);
+      else
+        compute_from(stage_i(cur), stage_j(cur), TJ, s + 2 < nstages, tok0 + (int64_t)(s + 2) * KS, nxt);
+      if ((s + 1) % FOLD == 0) fold();
+      cur = cur == NBUF - 1 ? 0 : cur + 1;
+    }
+  };
+  if (j_in_i)
+    stage_loop(std::true_type{});
+  else
+    stage_loop(std::false_type{});
 
   // ---- epilogue ----
   const int hl = lane >> 5, col = lane & 31;
