@@ -76,18 +76,21 @@ size_t quant_workspace_bytes(int64_t m, int64_t d, const gptq_qcfg_t& cfg);
 // C[i][j] -= rowscale[i] * cscale * sum_k A[i][k] B[k][j] for i < M, j < N, with
 // A = Ah + Al and B = Bh + Bl given as fp16 pairs and the product taken as
 // Ah Bh + Ah Bl + Al Bh on the fp16 matrix cores (fp32 accumulate).
-// A is row-major [M][lda]; B is stored transposed in 128-deep K slabs: element
-// (k, j) at (k / 128) * bstride + j * 128 + k % 128. K % 32 == 0.
+// Both operands are stored K-tiled in slabs of 32 (so that one slab of 16 rows
+// is 1 KB of contiguous memory):
+//   A(i, k) at (k / 32) * a_kslab + i * 32 + k % 32   (a_kslab >= 32 * M)
+//   B(k, j) at (k / 128) * b_block + ((k % 128) / 32) * b_kslab + j * 32 + k % 32
+// K % 32 == 0.
 struct TgemmArgs {
   float* C;
   int64_t ldc;
   const half_t* Ah;
   const half_t* Al;
-  int64_t lda;
+  int64_t a_kslab;
   const float* rowscale;
   const half_t* Bh;
   const half_t* Bl;
-  int64_t bstride;
+  int64_t b_block, b_kslab;
   const float* cscale;  // device scalar (power of two), multiplies every row
   int64_t M, N, K;
 };

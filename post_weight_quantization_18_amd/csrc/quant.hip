@@ -35,9 +35,9 @@ constexpr int CL_THREADS = 256;  // 64 rows x 4 lanes
 struct QuantWs {
   float* Wk;        // m x d working weights
   float* Esb;       // m x S errors of the current super-block
-  half_t* Ehb;      // m x BLK errors of one block, scaled, fp16 high part
+  half_t* Ehb;      // m x BLK errors of one block, scaled, fp16 high part (K-tiled by 32)
   half_t* Elb;      //                                    fp16 low part
-  half_t* Ehs;      // m x S errors of one super-block, scaled, fp16 high part
+  half_t* Ehs;      // m x S errors of one super-block, scaled, fp16 high part (K-tiled by 32)
   half_t* Els;      //                                          fp16 low part
   float* einv_b;    // m: inverse of the row scale of Ehb / Elb
   float* einv_s;    // m: inverse of the row scale of Ehs / Els
@@ -45,7 +45,7 @@ struct QuantWs {
   float* rdiag;     // d: 1 / U_jj
   uint32_t* umax;   // [0]: bits of max |U| over the far part of every block row
   float* uinv;      // [0]: inverse of the power-of-two scale of U's fp16 pairs
-  half_t* Uth;      // nblocks x d x BLK: U[blk, c] transposed (c, k), scaled, fp16 high
+  half_t* Uth;      // nblocks x d x BLK: U[blk, c] transposed, K-tiled by 32, scaled, fp16 high
   half_t* Utl;      //                                                         fp16 low
   float* U32;       // d x d (only when U is fp64)
 };
@@ -390,10 +390,11 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
 
 // Errors E[r][0 .. kw) (fp32, leading dimension lde) -> fp16 pairs with one
 // power-of-two scale per row that puts max |e| in [2^14, 2^15):
-//   Eh = fp16(e * 2^k), El = fp16(e * 2^k - Eh), einv[r] = 2^-k.
+//   Eh = fp16(e * 2^k), El = fp16(e * 2^k - Eh), einv[r] = 2^-k,
+// stored K-tiled for the trailing GEMM: (r, k) at (k / 32) * kslab + r * 32 + k % 32.
 // One wave per row.
 __global__ __launch_bounds__(256) void esplit_kernel(const float* E, int64_t lde, int64_t m, int kw, half_t* Eh,
-                                                     half_t* El, int64_t ldo, float* einv) {
+                                                     half_t* El, int64_t kslab, float* einv) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= m) return;
@@ -417,8 +418,9 @@ __global__ __launch_bounds__(256) void esplit_kernel(const float* E, int64_t lde
       l[t] = (half_t)(x[t] - (float)h[t]);
     }
     typedef half_t half4 __attribute__((ext_vector_type(4)));
-    *(half4*)(Eh + r * ldo + k) = half4{h[0], h[1], h[2], h[3]};
-    *(half4*)(El + r * ldo + k) = half4{l[0], l[1], l[2], l[3]};
+    const int64_t o = (int64_t)(k >> 5) * kslab + r * 32 + (k & 31);
+    *(half4*)(Eh + o) = half4{h[0], h[1], h[2], h[3]};
+    *(half4*)(El + o) = half4{l[0], l[1], l[2], l[3]};
   }
   if (lane == 0) einv[r] = 1.0f / sc;
 }
@@ -446,8 +448,9 @@ __device__ inline float u_scale(const uint32_t* umax) {
   return mx > 0.0f ? ldexpf(1.0f, 15 - ex) : 1.0f;
 }
 
-// Transposed, scaled fp16 hi/lo panels of the far part of each block row of U:
-//   Ut{h,l}[b][c][k] = split(U[j0 + k][c] * 2^s),  c >= j0 + BLK, k < BLK,
+// Transposed, scaled fp16 hi/lo panels of the far part of each block row of U,
+// K-tiled in slabs of 32 for the trailing GEMM:
+//   Ut{h,l}[b][k / 32][c][k % 32] = split(U[j0 + k][c] * 2^s),  c >= j0 + BLK, k < BLK,
 // with 2^s the power of two that puts max |U| of all far parts in [2^14, 2^15)
 // (uinv = 2^-s). One 64-column chunk per workgroup, transposed through LDS.
 __global__ __launch_bounds__(256) void usplit_kernel(const float* U, int64_t ldu, int64_t d, const uint32_t* umax,
@@ -476,7 +479,7 @@ __global__ __launch_bounds__(256) void usplit_kernel(const float* U, int64_t ldu
       hv[t] = h;
       lv[t] = (half_t)(v - (float)h);
     }
-    const int64_t o = (b * d + c0 + c) * BLK + k8;
+    const int64_t o = b * d * BLK + (int64_t)(k8 >> 5) * d * 32 + (c0 + c) * 32 + (k8 & 31);
     *(half8*)(Uth + o) = hv;
     *(half8*)(Utl + o) = lv;
   }
@@ -586,7 +589,9 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   t.ldc = d;
   t.Bh = w.Uth;
   t.Bl = w.Utl;
-  t.bstride = d * BLK;
+  t.b_block = d * BLK;
+  t.b_kslab = d * 32;
+  t.a_kslab = m * 32;
   t.cscale = w.uinv;
   t.M = m;
   const unsigned egrid = (unsigned)ceil_div(m, 4);
@@ -610,30 +615,28 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
     if (j1 < sb1) {
       // the rest of the super-block: K = this block
       hipLaunchKernelGGL(esplit_kernel, dim3(egrid), dim3(256), 0, st, (const float*)(w.Esb + a.ecol), S, m, a.bw,
-                         w.Ehb, w.Elb, (int64_t)BLK, w.einv_b);
+                         w.Ehb, w.Elb, m * 32, w.einv_b);
       GPTQ_CHECK_LAUNCH();
       t.C = w.Wk + j1;
       t.Ah = w.Ehb;
       t.Al = w.Elb;
-      t.lda = BLK;
       t.rowscale = w.einv_b;
-      t.Bh = w.Uth + (b * d + j1) * BLK;
-      t.Bl = w.Utl + (b * d + j1) * BLK;
+      t.Bh = w.Uth + b * d * BLK + j1 * 32;
+      t.Bl = w.Utl + b * d * BLK + j1 * 32;
       t.N = sb1 - j1;
       t.K = a.bw;
       if ((s = tgemm_enqueue(t, st)) != GPTQ_OK) return s;
     } else if (j1 == sb1 && sb1 < d) {
       // every later column: K = the whole super-block
       hipLaunchKernelGGL(esplit_kernel, dim3(egrid), dim3(256), 0, st, (const float*)w.Esb, S, m, (int)(sb1 - sb0),
-                         w.Ehs, w.Els, S, w.einv_s);
+                         w.Ehs, w.Els, m * 32, w.einv_s);
       GPTQ_CHECK_LAUNCH();
       t.C = w.Wk + sb1;
       t.Ah = w.Ehs;
       t.Al = w.Els;
-      t.lda = S;
       t.rowscale = w.einv_s;
-      t.Bh = w.Uth + ((sb0 / BLK) * d + sb1) * BLK;
-      t.Bl = w.Utl + ((sb0 / BLK) * d + sb1) * BLK;
+      t.Bh = w.Uth + (sb0 / BLK) * d * BLK + sb1 * 32;
+      t.Bl = w.Utl + (sb0 / BLK) * d * BLK + sb1 * 32;
       t.N = d - sb1;
       t.K = sb1 - sb0;
       if ((s = tgemm_enqueue(t, st)) != GPTQ_OK) return s;

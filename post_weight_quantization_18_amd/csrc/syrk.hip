@@ -56,6 +56,20 @@ static_assert(EI % (KS / 16) == 0 && (EJ % (KS / 16) == 0 || EJ < KS / 16), "DMA
 // lane issues the same number of loads per stage, so vmcnt waits stay exact.
 __device__ const uint4 kZero16[1] = {{0u, 0u, 0u, 0u}};
 
+// s_waitcnt vmcnt(PER * later) for a wave-uniform later in [0, MAXL]; the
+// immediate must be a constant, so the count is chosen by a uniform switch.
+template <int PER, int MAXL>
+__device__ __forceinline__ void wait_vm_stages(int later) {
+  static_assert(PER * MAXL < 64, "vmcnt holds at most 63");
+  if constexpr (MAXL >= 0) {
+    if (later >= MAXL) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((PER * MAXL) & 15) | (((PER * MAXL) >> 4) << 14));
+      return;
+    }
+    if constexpr (MAXL > 0) wait_vm_stages<PER, MAXL - 1>(later);
+  }
+}
+
 struct SyrkArgs {
   const half_t* X;
   int64_t ldx, n, d;
@@ -247,8 +261,10 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   auto stage_i = [&](int b) __attribute__((always_inline)) { return ring + b * KS * (TI + TJ); };
   auto stage_j = [&](int b) __attribute__((always_inline)) { return ring + b * KS * (TI + TJ) + KS * TI; };
 
-  if (nstages > 0) issue(tok0, 0);
-  if (nstages > 1) issue(tok0 + KS, 1);
+  // prologue: the first NBUF - 1 stages in flight
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nstages) issue(tok0 + (int64_t)p * KS, p);
   // The stage loop is instantiated once per tile kind (diagonal tiles read B
   // from the I buffer): a branch inside the loop would make the compiler merge
   // the accumulators of the two paths with register copies on every stage.
@@ -259,18 +275,21 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
       // wait for this stage's DMA (the next stage's loads may stay in flight),
       // barrier, then run the matrix cores while refilling the buffer the
       // previous stage used.
-      if (s + 1 >= nstages)
-        __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-      else if (DIAG)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | EI);  // vmcnt(EI)
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (EI + EJ));  // vmcnt(EI + EJ)
+      // this stage's loads are complete once at most the later stages' loads
+      // (up to NBUF - 2 stages of PER loads each) remain in flight
+      {
+        constexpr int PER = DIAG ? EI : EI + EJ;
+        const int later = (nstages - 1 - s) < (NBUF - 2) ? (nstages - 1 - s) : (NBUF - 2);
+        wait_vm_stages<PER, NBUF - 2>(later);
+      }
       lds_barrier();
-      const int nxt = cur == 0 ? NBUF - 1 : cur - 1;  // (cur + 2) mod 3
+      const int nxt = cur == 0 ? NBUF - 1 : cur - 1;  // the buffer stage s - 1 used
+      const bool refill = s + NBUF - 1 < nstages;
+      const int64_t t_next = tok0 + (int64_t)(s + NBUF - 1) * KS;
       if (DIAG)
-        compute_from(stage_i(cur), stage_i(cur), TI, s + 2 < nstages, tok0 + (int64_t)(s + 2) * KS, nxt);
+        compute_from(stage_i(cur), stage_i(cur), TI, refill, t_next, nxt);
       else
-        compute_from(stage_i(cur), stage_j(cur), TJ, s + 2 < nstages, tok0 + (int64_t)(s + 2) * KS, nxt);
+        compute_from(stage_i(cur), stage_j(cur), TJ, refill, t_next, nxt);
       if ((s + 1) % FOLD == 0) fold();
       cur = cur == NBUF - 1 ? 0 : cur + 1;
     }
@@ -281,32 +300,48 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
     stage_loop(std::false_type{});
 
   // ---- epilogue ----
+  // One 32 x 32 sub-tile at a time: all old H values of the sub-tile are read
+  // before any is written, so the read-modify-write costs one memory round
+  // trip per sub-tile instead of one per element.
   const int hl = lane >> 5, col = lane & 31;
 #pragma unroll
   for (int f = 0; f < FI; ++f)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      double v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = 2.0 * ((double)outer[f][h][r] + (double)acc[f][h][r]);
+      const int li0 = wi * 32 * FI + f * 32 + 4 * hl, lj = wj * 64 + h * 32 + col;
+      if (!a.direct) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ((double*)a.out)[((int64_t)logical * TI + li0 + 8 * (r >> 2) + (r & 3)) * TJ + lj] = v[r];
+        continue;
+      }
+      const int64_t j = J0 + lj;
+      if (a.accumulate) {
+        double old[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t i = I0 + li0 + 8 * (r >> 2) + (r & 3);
+          const bool ok = i < a.d && j <= i;
+          old[r] = !ok ? 0.0 : a.h_f64 ? ((const double*)a.out)[i * a.ldh + j]
+                                        : (double)((const float*)a.out)[i * a.ldh + j];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] += old[r];
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int li = wi * 32 * FI + f * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const int lj = wj * 64 + h * 32 + col;
-        const double v = 2.0 * ((double)outer[f][h][r] + (double)acc[f][h][r]);
-        if (a.direct) {
-          const int64_t i = I0 + li, j = J0 + lj;
-          if (i < a.d && j <= i) {
-            if (a.h_f64) {
-              double* H = (double*)a.out + i * a.ldh + j;
-              *H = a.accumulate ? *H + v : v;
-            } else {
-              float* H = (float*)a.out + i * a.ldh + j;
-              *H = (float)(a.accumulate ? (double)*H + v : v);
-            }
-          }
-        } else {
-          double* P = (double*)a.out + ((int64_t)logical * TI + li) * TJ + lj;
-          *P = v;
+        const int64_t i = I0 + li0 + 8 * (r >> 2) + (r & 3);
+        if (i < a.d && j <= i) {
+          if (a.h_f64)
+            ((double*)a.out)[i * a.ldh + j] = v[r];
+          else
+            ((float*)a.out)[i * a.ldh + j] = (float)v[r];
         }
       }
+    }
 }
 
 // Sums the split-K partial tiles in split order and adds them to H.

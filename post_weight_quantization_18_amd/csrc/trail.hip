@@ -14,9 +14,10 @@
 // Design (MI355X):
 //  * 256 x 128 output tile per workgroup of 8 waves (64 x 64 each, two per
 //    SIMD); v_mfma_f32_32x32x16_f16, 12 per wave per 16-deep K step.
-//  * Both operands are K-contiguous (A row-major, B stored transposed), so each
-//    32-deep K stage is four row-major LDS panels (A hi/lo 256 x 32, B hi/lo
-//    128 x 32, 48 KB) filled by the direct global->LDS DMA into a 3-deep ring;
+//  * Both operands are stored K-tiled in slabs of 32 (a 32-deep slab of 16
+//    rows is 1 KB of contiguous memory), so each 32-deep K stage is four
+//    row-major LDS panels (A hi/lo 256 x 32, B hi/lo 128 x 32, 48 KB) filled by
+//    fully coalesced direct global->LDS DMA into a 3-deep ring;
 //    the 16-byte chunks of a row are XOR-swizzled by (row / 4) mod 4, chosen on
 //    the global side, which makes the fragment reads (ds_read_b128, 32 rows x 2
 //    chunks per wave) free of bank conflicts.
@@ -70,12 +71,12 @@ __global__ __launch_bounds__(NT, 1) void tgemm_kernel(TgemmArgs a, int ntm, int 
   for (int e = 0; e < 2; ++e) {
     const int64_t r = I0 + 32 * w + 16 * e + lrow;
     okA[e] = r < a.M;
-    srcA[e] = (okA[e] ? r : 0) * a.lda + 8 * chunk;
+    srcA[e] = (okA[e] ? r : 0) * 32 + 8 * chunk;
   }
   {
     const int64_t c = J0 + 16 * w + lrow;
     okB = c < a.N;
-    srcB = (okB ? c : 0) * 128 + 8 * chunk;
+    srcB = (okB ? c : 0) * 32 + 8 * chunk;
   }
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GPTQ_LDS void*)ring);
   // instruction e (0..5) of stage s into ring buffer b
@@ -86,11 +87,12 @@ __global__ __launch_bounds__(NT, 1) void tgemm_kernel(TgemmArgs a, int ntm, int 
     if (e < 4) {
       const int h = e & 1;  // which 16-row half of the wave's 32 A rows
       const half_t* base = (e < 2) ? a.Ah : a.Al;
-      src = okA[h] ? (const void*)(base + srcA[h] + k0) : (const void*)kZeroT;
+      src = okA[h] ? (const void*)(base + (k0 >> 5) * a.a_kslab + srcA[h]) : (const void*)kZeroT;
       off = ((e < 2) ? OFF_AH : OFF_AL) + (uint32_t)((32 * wu + 16 * h) * ROWB);
     } else {
       const half_t* base = (e == 4) ? a.Bh : a.Bl;
-      src = okB ? (const void*)(base + (k0 >> 7) * a.bstride + srcB + (k0 & 127)) : (const void*)kZeroT;
+      src = okB ? (const void*)(base + (k0 >> 7) * a.b_block + ((k0 & 127) >> 5) * a.b_kslab + srcB)
+                : (const void*)kZeroT;
       off = ((e == 4) ? OFF_BH : OFF_BL) + (uint32_t)(16 * wu * ROWB);
     }
     dma16(src, ring_lds + (uint32_t)b * STAGE_BYTES + off);
@@ -133,14 +135,20 @@ __global__ __launch_bounds__(NT, 1) void tgemm_kernel(TgemmArgs a, int ntm, int 
 #pragma unroll
         for (int e = 3 * kk; e < 3 * kk + 3; ++e) issue(e, s_next, b_next);
       }
+      // the three passes sweep all four sub-tiles in turn, so consecutive
+      // MFMAs never accumulate into the same registers
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[x], bh[y], acc[x][y], 0, 0, 0);
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[x], bl[y], acc[x][y], 0, 0, 0);
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[x], bh[y], acc[x][y], 0, 0, 0);
-        }
+        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[x], bh[y], acc[x][y], 0, 0, 0);
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[x], bl[y], acc[x][y], 0, 0, 0);
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[x], bh[y], acc[x][y], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -167,24 +175,51 @@ __global__ __launch_bounds__(NT, 1) void tgemm_kernel(TgemmArgs a, int ntm, int 
   }
 
   // ---- epilogue: C -= acc * rowscale[i] * cscale ----
+  // All loads of a sub-tile row group are issued before any store, so the
+  // read-modify-write costs one memory round trip per 16 rows instead of one
+  // per element (the compiler cannot reorder loads across possibly aliasing
+  // stores by itself).
   const float cs = *a.cscale;
   const int hl = lane >> 5, col = lane & 31;
+  const bool full = (I0 + TM <= a.M) && (J0 + TN <= a.N);
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < 2; ++x) {
+    const int64_t ib = I0 + 64 * wi + 32 * x + 4 * hl;
+    float sc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t i = I0 + 64 * wi + 32 * x + 8 * (r >> 2) + 4 * hl + (r & 3);
-      if (i >= a.M) continue;
-      const float sc = a.rowscale[i] * cs;
+      const int64_t i = ib + 8 * (r >> 2) + (r & 3);
+      sc[r] = (i < a.M) ? a.rowscale[i] : 0.0f;
+    }
+    if (full) {
+      float cv[2][16];
 #pragma unroll
-      for (int y = 0; y < 2; ++y) {
-        const int64_t j = J0 + 64 * wj + 32 * y + col;
-        if (j < a.N) {
-          float* c = a.C + i * a.ldc + j;
-          *c = fmaf(-acc[x][y][r], sc, *c);
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          cv[y][r] = a.C[(ib + 8 * (r >> 2) + (r & 3)) * a.ldc + J0 + 64 * wj + 32 * y + col];
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          a.C[(ib + 8 * (r >> 2) + (r & 3)) * a.ldc + J0 + 64 * wj + 32 * y + col] =
+              fmaf(-acc[x][y][r], sc[r] * cs, cv[y][r]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = ib + 8 * (r >> 2) + (r & 3);
+        if (i >= a.M) continue;
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const int64_t j = J0 + 64 * wj + 32 * y + col;
+          if (j < a.N) {
+            float* c = a.C + i * a.ldc + j;
+            *c = fmaf(-acc[x][y][r], sc[r] * cs, *c);
+          }
         }
       }
     }
+  }
 }
 
 }  // namespace
