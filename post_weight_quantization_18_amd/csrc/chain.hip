@@ -391,6 +391,9 @@ __global__ __launch_bounds__(256) void update_f64_kernel(double* A, int64_t d, i
     if (k + KT < ke) fetch(k + KT);
     mfma_f64_block<KT>(As, Bs, wr, wc, lane, acc);
   }
+  // all 16 old values are read before any is written: one memory round trip
+  // for the read-modify-write instead of one per element
+  double old[2][2][4];
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -399,7 +402,17 @@ __global__ __launch_bounds__(256) void update_f64_kernel(double* A, int64_t d, i
       for (int r = 0; r < 4; ++r) {
         const int64_t i = i0 + wr + x * 16 + (lane >> 4) + 4 * r;
         const int64_t j = j0 + wc + y * 16 + (lane & 15);
-        if (i < d && j < c1 && j <= i) A[i * d + j] -= acc[x][y][r];
+        old[x][y][r] = (i < d && j < c1 && j <= i) ? A[i * d + j] : 0.0;
+      }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t i = i0 + wr + x * 16 + (lane >> 4) + 4 * r;
+        const int64_t j = j0 + wc + y * 16 + (lane & 15);
+        if (i < d && j < c1 && j <= i) A[i * d + j] = old[x][y][r] - acc[x][y][r];
       }
 }
 

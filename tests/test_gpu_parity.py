@@ -104,7 +104,9 @@ def test_hessian_accumulate_and_empty():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("d,u_dtype", [(768, torch.float64), (768, torch.float32), (96, torch.float64),
                                        (200, torch.float64), (1000, torch.float64), (4160, torch.float64),
-                                       (64, torch.float64), (40, torch.float64)])
+                                       (64, torch.float64), (40, torch.float64),
+                                       # large enough for the 128-tile trailing updates, ragged at 128
+                                       (8256, torch.float64)])
 def test_chain_parity(d, u_dtype):
     say(f"[case] chain d={d} u_dtype={u_dtype}")
     rng = np.random.default_rng(d)
