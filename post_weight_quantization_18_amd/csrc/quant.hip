@@ -231,9 +231,23 @@ struct MinMax<END, END> {
   __device__ __forceinline__ static void run(const LaneState&, float&, float&) {}
 };
 
+// The lane's 32 entries of one row of the block's U and that row's 1 / U_ii,
+// loaded one step ahead of their use.
+struct URow {
+  float4 u[CPL / 4];
+  float rd;
+};
+
+__device__ __forceinline__ void load_urow(URow& ur, const float (*Us)[UPITCH], const float* rdiag, int i, int g) {
+  const float4* u4 = (const float4*)(Us[i] + g * UGS);
+#pragma unroll
+  for (int k4 = 0; k4 < CPL / 4; ++k4) ur.u[k4] = u4[k4];
+  ur.rd = rdiag[i];
+}
+
 template <int G, int I>
-__device__ __forceinline__ void col_step(LaneState& st, const ColArgs& a, int64_t r, int g, const float* urow,
-                                         float rd) {
+__device__ __forceinline__ void col_step(LaneState& st, const ColArgs& a, int64_t r, int g, const URow& ur) {
+  const float rd = ur.rd;
   constexpr int O = I / CPL, LI = I % CPL;
   if constexpr (G > 0 && I % (G > 0 ? G : 1) == 0) {
     // grid of the group [I, I + G): this lane's part, then across the lanes of the group
@@ -274,10 +288,9 @@ __device__ __forceinline__ void col_step(LaneState& st, const ColArgs& a, int64_
     st.w[LI] = e_own;  // the register now carries the error of column I
   }
   const float e = quad_bcast<O>(e_own);
-  const float4* u4 = (const float4*)(urow + g * UGS);
 #pragma unroll
   for (int k4 = 0; k4 < CPL / 4; ++k4) {
-    const float4 u = u4[k4];
+    const float4 u = ur.u[k4];
     st.w[4 * k4] = fmaf(-e, u.x, st.w[4 * k4]);
     st.w[4 * k4 + 1] = fmaf(-e, u.y, st.w[4 * k4 + 1]);
     st.w[4 * k4 + 2] = fmaf(-e, u.z, st.w[4 * k4 + 2]);
@@ -285,11 +298,19 @@ __device__ __forceinline__ void col_step(LaneState& st, const ColArgs& a, int64_
   }
 }
 
-template <int G, int... Is>
-__device__ __forceinline__ void run_steps(std::integer_sequence<int, Is...>, LaneState& st, const ColArgs& a,
-                                          int64_t r, int g, const float (*Us)[UPITCH], const float* rdiag, int bw) {
-  ((Is < bw ? col_step<G, Is>(st, a, r, g, Us[Is], rdiag[Is]) : void()), ...);
-}
+// Steps I .. BLK-1 of the block: row I + 1 of U is read from LDS before step I
+// runs, so its latency hides behind the step's arithmetic.
+template <int G, int I>
+struct Steps {
+  __device__ __forceinline__ static void run(LaneState& st, const ColArgs& a, int64_t r, int g,
+                                             const float (*Us)[UPITCH], const float* rdiag, int bw, const URow& cur) {
+    if (I >= bw) return;
+    URow nxt;
+    if constexpr (I + 1 < BLK) load_urow(nxt, Us, rdiag, I + 1, g);
+    col_step<G, I>(st, a, r, g, cur);
+    if constexpr (I + 1 < BLK) Steps<G, I + 1>::run(st, a, r, g, Us, rdiag, bw, nxt);
+  }
+};
 
 // G = 0: one grid per row (already fitted); G = 32, 64, 128: refit at every
 // group start inside the block; G = -1: groups span whole blocks, refit at the
@@ -371,7 +392,11 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
     st.rs = 1.0f / st.s;
   }
 
-  if (live) run_steps<G>(std::make_integer_sequence<int, BLK>{}, st, a, r, g, Us, rdiag, bw);
+  if (live) {
+    URow first;
+    load_urow(first, Us, rdiag, 0, g);
+    Steps<G, 0>::run(st, a, r, g, Us, rdiag, bw, first);
+  }
 
   if (live && cols_ok) {
     float* erow = a.E + r * a.lde + a.ecol + g * CPL;
