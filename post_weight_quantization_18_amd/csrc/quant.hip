@@ -307,6 +307,7 @@ struct Steps {
     if (I >= bw) return;
     URow nxt;
     if constexpr (I + 1 < BLK) load_urow(nxt, Us, rdiag, I + 1, g);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this step's work
     col_step<G, I>(st, a, r, g, cur);
     if constexpr (I + 1 < BLK) Steps<G, I + 1>::run(st, a, r, g, Us, rdiag, bw, nxt);
   }
