@@ -131,9 +131,9 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const void* H, int h
 //   for each 16-block kb: (1) one wave factors the 16 x 16 diagonal leaf, a row
 //   per lane in registers; each step broadcasts the current column through LDS
 //   (one write, one batch of reads) and takes the pivot's inverse square root
-//   (v_rsq_f64 + two Newton steps), then the same wave inverts the leaf by
-//   forward substitution; (2) all threads solve the rows below against the
-//   leaf's inverse; (3) all threads apply the rank-16 update to the rest.
+//   (v_rsq_f64 + two Newton steps); (2) that wave inverts the leaf by forward
+//   substitution while the other three solve the rows below against the leaf,
+//   one row per thread; (3) all threads apply the rank-16 update to the rest.
 // The off-diagonal 16-blocks of L^-1 follow from the diagonal ones block-row by
 // block-row: Li[I][J] = -Li[I][I] sum_{K=J}^{I-1} L[I][K] Li[K][J].
 // Writes L11 back with a zero upper triangle and L11^-1 to Dinv.
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void potf2_kernel(double* A, int64_t d, int64_
   __syncthreads();
   bool failed = false;
   for (int b0 = 0; b0 < NB; b0 += LEAF) {
-    // ---- (1) leaf: factor and invert the 16 x 16 diagonal block (wave 0) ----
+    // ---- (1) leaf: factor the 16 x 16 diagonal block (wave 0) ----
     if (w == 0) {
       const int i = lane & (LEAF - 1);
       double r[LEAF];
@@ -197,8 +197,15 @@ __global__ __launch_bounds__(256) void potf2_kernel(double* A, int64_t d, int64_
 #pragma unroll
         for (int j = 0; j < LEAF; ++j) L[b0 + i][b0 + j] = (j <= i) ? r[j] : 0.0;
       }
-      // forward substitution, lane j owning column j of the leaf's inverse:
-      // x[rr] = (delta(rr, j) - sum_{k < rr} L[rr][k] x[k]) / L[rr][rr]
+    }
+    __syncthreads();
+    const int rows = NB - b0 - LEAF;  // rows below the leaf
+    if (w == 0) {
+      // ---- (2a) the leaf's inverse, by forward substitution, lane j owning
+      // column j: x[rr] = (delta(rr, j) - sum_{k < rr} L[rr][k] x[k]) / L[rr][rr].
+      // Needed only for Dinv and the off-diagonal blocks at the end, so it
+      // runs beside (2b).
+      const int i = lane & (LEAF - 1);
       double x[LEAF];
 #pragma unroll
       for (int rr = 0; rr < LEAF; ++rr) {
@@ -219,31 +226,30 @@ __global__ __launch_bounds__(256) void potf2_kernel(double* A, int64_t d, int64_
 #pragma unroll
         for (int rr = 0; rr < LEAF; ++rr) Li[b0 + rr][b0 + i] = (rr >= i) ? x[rr] : 0.0;
       }
-    }
-    __syncthreads();
-    const int rows = NB - b0 - LEAF;  // rows below the leaf
-    if (rows <= 0) break;
-    // ---- (2) rows below: L[R][b0 + c] = sum_{k <= c} A[R][b0 + k] Li[b0 + c][b0 + k] ----
-    double out[3];
+    } else if (tid - 64 < rows) {
+      // ---- (2b) rows below, one row per thread: solve x L11^T = a, i.e.
+      // x[c] = (a[c] - sum_{k < c} x[k] L[c][k]) / L[c][c]
+      const int R = b0 + LEAF + (tid - 64);
+      double x[LEAF];
 #pragma unroll
-    for (int e = 0; e < 3; ++e) {
-      const int idx = tid + 256 * e;
-      out[e] = 0.0;
-      if (idx < rows * LEAF) {
-        const int R = b0 + LEAF + idx / LEAF, c = idx % LEAF;
-        double s = 0.0;
+      for (int c = 0; c < LEAF; ++c) x[c] = L[R][b0 + c];
 #pragma unroll
-        for (int k = 0; k < LEAF; ++k) s = fma(L[R][b0 + k], Li[b0 + c][b0 + k], s);
-        out[e] = s;
+      for (int c = 0; c < LEAF; ++c) {
+        double s0 = x[c], s1 = 0.0;
+#pragma unroll
+        for (int k = 0; k < c; ++k) {
+          if (k & 1)
+            s1 = fma(-x[k], L[b0 + c][b0 + k], s1);
+          else
+            s0 = fma(-x[k], L[b0 + c][b0 + k], s0);
+        }
+        x[c] = (s0 + s1) * rdiag[b0 + c];
       }
-    }
-    __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 3; ++e) {
-      const int idx = tid + 256 * e;
-      if (idx < rows * LEAF) L[b0 + LEAF + idx / LEAF][b0 + idx % LEAF] = out[e];
+      for (int c = 0; c < LEAF; ++c) L[R][b0 + c] = x[c];
     }
     __syncthreads();
+    if (rows <= 0) break;
     // ---- (3) rank-16 update of the lower part of the rest ----
     for (int idx = tid; idx < rows * rows; idx += 256) {
       const int R = b0 + LEAF + idx / rows, C = b0 + LEAF + idx % rows;
