@@ -13,12 +13,12 @@
 // Work matrix A (fp64, d x d, row-major, lda = d) holds J H_d J (lower), then L,
 // then L^-1, in place; its strictly upper triangle is kept at zero.
 // Blocked right-looking Cholesky with 64-wide panels:
-//   potf2: the diagonal block is factored in LDS by one workgroup, which also
-//          inverts it (the inverse serves the panel solve and the inverse pass);
-//   trsm:  panel rows A21 <- A21 L11^-T (row-local, fp64 FMA);
+//   panel: the diagonal block is factored and inverted in LDS (the inverse
+//          serves the panel solve and the inverse pass), and the panel rows
+//          become A21 <- A21 L11^-T (fp64 MFMA), in one launch;
 //   syrk:  A22 <- A22 - A21 A21^T on lower 64x64 tiles (v_mfma_f64_16x16x4).
 // Triangular inverse by recursive doubling: the 64x64 diagonal blocks hold
-// their inverses from potf2; then for s = 64, 128, ... every pair of adjacent
+// their inverses from the panel step; then for s = 64, 128, ... every pair of adjacent
 // inverted s-blocks [[A, 0], [B, C]] is merged with
 //   N21 = -C^-1 (B A^-1)
 // as two batched fp64-MFMA launches per level (log2(d/64) levels), instead of
@@ -127,18 +127,31 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const void* H, int h
 
 // Factor the 64 x 64 diagonal block at k0 (lower Cholesky) and invert the
 // factor, in one workgroup of 4 waves, blocked by 16 columns so that only the
-// 16-column leaves are serial:
-//   for each 16-block kb: (1) one wave factors the 16 x 16 diagonal leaf, a row
-//   per lane in registers; each step broadcasts the current column through LDS
-//   (one write, one batch of reads) and takes the pivot's inverse square root
-//   (v_rsq_f64 + two Newton steps); (2) that wave inverts the leaf by forward
-//   substitution while the other three solve the rows below against the leaf,
-//   one row per thread; (3) all threads apply the rank-16 update to the rest.
-// The off-diagonal 16-blocks of L^-1 follow from the diagonal ones block-row by
-// block-row: Li[I][J] = -Li[I][I] sum_{K=J}^{I-1} L[I][K] Li[K][J].
-// Writes L11 back with a zero upper triangle and L11^-1 to Dinv.
-// info <- first failing order (k0 + c + 1).
+// 16-column leaves are serial. For each 16-block:
+//   (1) wave 0 factors the 16 x 16 diagonal leaf and inverts it in the same
+//       sweep, in registers: lanes 0-15 hold the leaf's rows, lanes 16-31 the
+//       columns of its inverse (started from the identity). Step c takes the
+//       pivot from lane c, its inverse square root (v_rsq_f64 + two Newton
+//       steps), scales entry c of every lane, and subtracts entry c times
+//       L[j][c] (read from lane j) from entry j > c: for a row lane that is the
+//       Cholesky update, for an inverse lane it is forward substitution, so both
+//       share one instruction stream and one set of lane reads;
+//   (2) the rows below the leaf become A21 L11^-T (fp64 MFMA, a 16-row block
+//       per wave);
+//   (3) the lower 16 x 16 tiles of the rest take the rank-16 update
+//       A22 - L21 L21^T (fp64 MFMA).
+// The off-diagonal 16-blocks of L^-1 then follow block-row by block-row:
+//   Li[I][J] = -Li[I][I] sum_{K=J}^{I-1} L[I][K] Li[K][J]  (fp64 MFMA).
+// Then the rows below the block: workgroup b takes rows k0 + 64 (b + 1) ..
+// + 63 and replaces A21 there by A21 L11^-T (fp64 MFMA). Every workgroup
+// factors the block itself (it is small and latency-bound, so the copies cost
+// no time) instead of waiting for one workgroup or a second launch; the
+// workgroups' slab loads are issued before the factorisation and land during it.
+// Workgroup 0 writes L11^-1 to Dinv and sets info (first failing order,
+// k0 + c + 1). L11 itself is not written back: the triangular inverse puts
+// L11^-1 in its place, and nothing reads it in between.
 constexpr int LEAF = 16;
+constexpr int LP = NB + 4;  // LDS pitch in doubles: the MFMA operand reads hit each bank pair at most twice
 
 // 1 / sqrt(p) to fp64 accuracy for p > 0 (hardware estimate + two Newton steps).
 __device__ __forceinline__ double rsqrt_f64(double p) {
@@ -148,142 +161,216 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
   return y;
 }
 
-__global__ __launch_bounds__(256) void potf2_kernel(double* A, int64_t d, int64_t k0, double* Dinv,
+// x of lane l, as a wave-uniform value.
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), l);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// 16 x 16 blocks in LDS (pitch LP) with v_mfma_f64_16x16x4: lane l = 16 lk + li
+// supplies A[li][k] and B[k][li] for k = lk of each 4-deep step, and holds
+// D[lk + 4 r][li] in register r.
+// acc + X Y for X 16 x 16 and Y 16 x 16.
+__device__ __forceinline__ double4v mm16_nn(const double* X, const double* Y, double4v acc, int li, int lk) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(X[li * LP + 4 * s + lk], Y[(4 * s + lk) * LP + li], acc, 0, 0, 0);
+  return acc;
+}
+// acc + sign X Z^T for X, Z 16 x 16.
+template <bool NEG>
+__device__ __forceinline__ double4v mm16_nt(const double* X, const double* Z, double4v acc, int li, int lk) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const double x = X[li * LP + 4 * s + lk];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(NEG ? -x : x, Z[li * LP + 4 * s + lk], acc, 0, 0, 0);
+  }
+  return acc;
+}
+__device__ __forceinline__ double4v load16(const double* P, int li, int lk) {
+  double4v v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = P[(lk + 4 * r) * LP + li];
+  return v;
+}
+__device__ __forceinline__ void store16(double* P, double4v v, int li, int lk) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) P[(lk + 4 * r) * LP + li] = v[r];
+}
+
+__global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_t k0, double* Dinv,
                                                    int32_t* info) {
-  __shared__ double L[NB][NB + 1];
-  __shared__ double Li[NB][NB + 1];
-  __shared__ double tmp[3][LEAF][LEAF + 1];
-  __shared__ double col[NB];
-  __shared__ double rdiag[NB];
+  __shared__ double L[NB * LP];
+  __shared__ double Li[NB * LP];
   const int nb = (int)((d - k0) < NB ? (d - k0) : NB);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    const int r = idx / NB, c = idx % NB;
-    double v = 0.0;
-    if (r < nb && c < nb && c <= r) v = A[(k0 + r) * d + k0 + c];
-    if (r >= nb && r == c) v = 1.0;  // identity padding beyond the matrix
-    L[r][c] = v;
-    Li[r][c] = 0.0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int li = lane & 15, lk = lane >> 4;
+  const double* blk = A + k0 * d + k0;  // the block's (0, 0); always a valid address
+  // this workgroup's slab of rows below the block (none when it is the last)
+  const int64_t r0 = k0 + NB + (int64_t)blockIdx.x * NB;
+  const bool has_slab = r0 < d;
+  double xs[NB / 4];
+  if (has_slab) {
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) {
+      const int64_t r = r0 + w + 4 * q;
+      xs[q] = A[(r < d ? r : r0) * d + k0 + lane];  // rows past d repeat row r0 (not stored)
+    }
+  }
+  {
+    // thread: column lane of rows w + 4q; the loads are unconditional (a
+    // masked-off element reads the block's first entry) and all issued before
+    // the first LDS write
+    double v[NB / 4];
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) {
+      const int r = w + 4 * q;
+      const int rr = r < nb ? r : 0, cc = lane < nb ? lane : 0;  // clamped into the block
+      v[q] = blk[(int64_t)rr * d + cc];
+    }
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) {
+      const int r = w + 4 * q;
+      const bool in = r < nb && lane <= r;
+      L[r * LP + lane] = in ? v[q] : (r == lane ? 1.0 : 0.0);  // identity padding past d
+      Li[r * LP + lane] = 0.0;
+    }
   }
   __syncthreads();
-  bool failed = false;
+  int first_bad = -1;  // first failing pivot of the block (wave 0)
   for (int b0 = 0; b0 < NB; b0 += LEAF) {
-    // ---- (1) leaf: factor the 16 x 16 diagonal block (wave 0) ----
+    // ---- (1) leaf factor and inverse (wave 0; lanes 32-63 repeat 0-31) ----
     if (w == 0) {
-      const int i = lane & (LEAF - 1);
-      double r[LEAF];
+      const int t = li;
+      const bool inv = (lane & 16) != 0;
+      double g[LEAF];
 #pragma unroll
-      for (int j = 0; j < LEAF; ++j) r[j] = L[b0 + i][b0 + j];  // zeros above the diagonal
+      for (int j = 0; j < LEAF; ++j) {
+        const double a = L[(b0 + t) * LP + b0 + j];
+        g[j] = inv ? (j == t ? 1.0 : 0.0) : (j <= t ? a : 0.0);
+      }
+      // Step c updates entry c + 1 (the next pivot) at once and entries
+      // c + 2 .. 15 during step c + 1, where they overlap that pivot's inverse
+      // square root. The empty asm statements pin each update to its step: a
+      // later update would keep its scalar lane reads alive and overflow the
+      // scalar registers.
+      double vprev = 0.0;
 #pragma unroll
       for (int c = 0; c < LEAF; ++c) {
-        col[lane] = r[c];  // column c of the current leaf: lane j holds A[j][c]
-        double cv[LEAF];
-#pragma unroll
-        for (int j = c; j < LEAF; ++j) cv[j] = col[j];
-        double p = cv[c];
-        if (!(p > 0.0)) {
-          if (!failed && b0 + c < nb && lane == 0 && *info == 0) *info = (int32_t)(k0 + b0 + c + 1);
-          failed = true;
-          p = 1.0;
-        }
+        double p = readlane_f64(g[c], c);
+        const bool bad = !(p > 0.0);  // not positive definite (or NaN): go on with 1
+        first_bad = (bad && first_bad < 0) ? b0 + c : first_bad;
+        p = bad ? 1.0 : p;
         const double rs = rsqrt_f64(p);
-        const double lc = r[c] * rs;  // L[i][c]
-        r[c] = lc;
-        if (lane == 0) rdiag[b0 + c] = rs;
+        if (c > 0) {
 #pragma unroll
-        for (int j = c + 1; j < LEAF; ++j) r[j] = fma(-lc, cv[j] * rs, r[j]);
+          for (int j = c + 1; j < LEAF; ++j) {
+            g[j] = fma(-vprev, readlane_f64(vprev, j), g[j]);
+            asm volatile("" : "+v"(g[j]));
+          }
+        }
+        const double vc = g[c] * rs;  // L[t][c] (row lanes) or Li[c][t] (inverse lanes)
+        g[c] = vc;
+        if (c + 1 < LEAF) {
+          g[c + 1] = fma(-vc, readlane_f64(vc, c + 1), g[c + 1]);
+          asm volatile("" : "+v"(g[c + 1]));
+        }
+        vprev = vc;
       }
       if (lane < LEAF) {
 #pragma unroll
-        for (int j = 0; j < LEAF; ++j) L[b0 + i][b0 + j] = (j <= i) ? r[j] : 0.0;
+        for (int j = 0; j < LEAF; ++j) L[(b0 + t) * LP + b0 + j] = (j <= t) ? g[j] : 0.0;
+      } else if (lane < 2 * LEAF) {
+#pragma unroll
+        for (int c = 0; c < LEAF; ++c) Li[(b0 + c) * LP + b0 + t] = (c >= t) ? g[c] : 0.0;
       }
     }
     __syncthreads();
-    const int rows = NB - b0 - LEAF;  // rows below the leaf
-    if (w == 0) {
-      // ---- (2a) the leaf's inverse, by forward substitution, lane j owning
-      // column j: x[rr] = (delta(rr, j) - sum_{k < rr} L[rr][k] x[k]) / L[rr][rr].
-      // Needed only for Dinv and the off-diagonal blocks at the end, so it
-      // runs beside (2b).
-      const int i = lane & (LEAF - 1);
-      double x[LEAF];
-#pragma unroll
-      for (int rr = 0; rr < LEAF; ++rr) {
-        double lr[LEAF];
-#pragma unroll
-        for (int k = 0; k < rr; ++k) lr[k] = L[b0 + rr][b0 + k];
-        double s0 = (rr == i) ? 1.0 : 0.0, s1 = 0.0;
-#pragma unroll
-        for (int k = 0; k < rr; ++k) {
-          if (k & 1)
-            s1 = fma(-lr[k], x[k], s1);
-          else
-            s0 = fma(-lr[k], x[k], s0);
-        }
-        x[rr] = (s0 + s1) * rdiag[b0 + rr];
-      }
-      if (lane < LEAF) {
-#pragma unroll
-        for (int rr = 0; rr < LEAF; ++rr) Li[b0 + rr][b0 + i] = (rr >= i) ? x[rr] : 0.0;
-      }
-    } else if (tid - 64 < rows) {
-      // ---- (2b) rows below, one row per thread: solve x L11^T = a, i.e.
-      // x[c] = (a[c] - sum_{k < c} x[k] L[c][k]) / L[c][c]
-      const int R = b0 + LEAF + (tid - 64);
-      double x[LEAF];
-#pragma unroll
-      for (int c = 0; c < LEAF; ++c) x[c] = L[R][b0 + c];
-#pragma unroll
-      for (int c = 0; c < LEAF; ++c) {
-        double s0 = x[c], s1 = 0.0;
-#pragma unroll
-        for (int k = 0; k < c; ++k) {
-          if (k & 1)
-            s1 = fma(-x[k], L[b0 + c][b0 + k], s1);
-          else
-            s0 = fma(-x[k], L[b0 + c][b0 + k], s0);
-        }
-        x[c] = (s0 + s1) * rdiag[b0 + c];
-      }
-#pragma unroll
-      for (int c = 0; c < LEAF; ++c) L[R][b0 + c] = x[c];
+    const int nrb = (NB - b0 - LEAF) / LEAF;  // 16-row blocks below the leaf
+    if (nrb <= 0) break;
+    // ---- (2) rows below: A21 <- A21 L11^-T, one 16-row block per wave ----
+    if (w < nrb) {
+      double* X = &L[(b0 + LEAF + LEAF * w) * LP + b0];
+      const double4v z = {0.0, 0.0, 0.0, 0.0};
+      const double4v x = mm16_nt<false>(X, &Li[b0 * LP + b0], z, li, lk);
+      store16(X, x, li, lk);  // the wave read its whole block into the MFMAs first
     }
     __syncthreads();
-    if (rows <= 0) break;
-    // ---- (3) rank-16 update of the lower part of the rest ----
-    for (int idx = tid; idx < rows * rows; idx += 256) {
-      const int R = b0 + LEAF + idx / rows, C = b0 + LEAF + idx % rows;
-      if (C > R) continue;
-      double s = 0.0;
-#pragma unroll
-      for (int k = 0; k < LEAF; ++k) s = fma(L[R][b0 + k], L[C][b0 + k], s);
-      L[R][C] -= s;
+    // ---- (3) rank-16 update of the lower tiles of the rest ----
+    for (int tile = w; tile < nrb * (nrb + 1) / 2; tile += 4) {
+      int p = 0;
+      while ((p + 1) * (p + 2) / 2 <= tile) ++p;
+      const int q = tile - p * (p + 1) / 2;
+      double* T = &L[(b0 + LEAF + LEAF * p) * LP + b0 + LEAF + LEAF * q];
+      double4v acc = load16(T, li, lk);
+      acc = mm16_nt<true>(&L[(b0 + LEAF + LEAF * p) * LP + b0], &L[(b0 + LEAF + LEAF * q) * LP + b0], acc, li, lk);
+      store16(T, acc, li, lk);
     }
     __syncthreads();
   }
-  // ---- off-diagonal blocks of L^-1, block-row by block-row ----
+  // ---- off-diagonal blocks of L^-1, block-row by block-row (wave J: block J) ----
   for (int I = 1; I < NB / LEAF; ++I) {
-    // tmp[J] = sum_{K=J}^{I-1} L[I][K] Li[K][J] for J < I
-    for (int idx = tid; idx < I * LEAF * LEAF; idx += 256) {
-      const int J = idx / (LEAF * LEAF), r = (idx / LEAF) % LEAF, c = idx % LEAF;
-      double s = 0.0;
-      for (int k = J * LEAF; k < I * LEAF; ++k) s = fma(L[I * LEAF + r][k], Li[k][J * LEAF + c], s);
-      tmp[J][r][c] = s;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < I * LEAF * LEAF; idx += 256) {
-      const int J = idx / (LEAF * LEAF), r = (idx / LEAF) % LEAF, c = idx % LEAF;
-      double s = 0.0;
+    if (w < I) {
+      const int J = w;
+      double4v tmp = {0.0, 0.0, 0.0, 0.0};
+      for (int K = J; K < I; ++K)
+        tmp = mm16_nn(&L[LEAF * I * LP + LEAF * K], &Li[LEAF * K * LP + LEAF * J], tmp, li, lk);
+      // Li[I][J] = -Li[I][I] tmp, with tmp as the B operand straight from the
+      // registers: step r pairs k = lk + 4 r of both operands
+      const double* D = &Li[LEAF * I * LP + LEAF * I];
+      double4v out = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int k = 0; k < LEAF; ++k) s = fma(Li[I * LEAF + r][I * LEAF + k], tmp[J][k][c], s);
-      Li[I * LEAF + r][J * LEAF + c] = -s;
+      for (int r = 0; r < 4; ++r)
+        out = __builtin_amdgcn_mfma_f64_16x16x4f64(-D[li * LP + lk + 4 * r], tmp[r], out, 0, 0, 0);
+      store16(&Li[LEAF * I * LP + LEAF * J], out, li, lk);
     }
     __syncthreads();
   }
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    const int r = idx / NB, c = idx % NB;
-    if (r < nb && c < nb) A[(k0 + r) * d + k0 + c] = (c <= r) ? L[r][c] : 0.0;
-    if (k0 + r < d) Dinv[(k0 + r) * NB + c] = (r < nb && c < nb && c <= r) ? Li[r][c] : 0.0;
+  if (blockIdx.x == 0) {
+    if (tid == 0 && first_bad >= 0 && first_bad < nb && *info == 0) *info = (int32_t)(k0 + first_bad + 1);
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) {
+      const int r = w + 4 * q, c = lane;
+      if (r < nb) Dinv[(k0 + r) * NB + c] = (c < nb && c <= r) ? Li[r * LP + c] : 0.0;
+    }
+  }
+  if (!has_slab) return;  // uniform over the workgroup
+  // ---- slab: X <- X L11^-T, X staged in L's storage (L is no longer read) ----
+#pragma unroll
+  for (int q = 0; q < NB / 4; ++q) L[(w + 4 * q) * LP + lane] = xs[q];
+  __syncthreads();
+  {
+    // wave (wr, wc): 32 x 32 of the 64 x 64 result; out[i][j] = sum_k X[i][k] Li[j][k]
+    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+    double4v acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[a][b] = (double4v){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int k = 0; k < NB; k += 4) {
+      double av[2], bv[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) av[a] = L[(wr + 16 * a + li) * LP + k + lk];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) bv[b] = Li[(wc + 16 * b + li) * LP + k + lk];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t i = r0 + wr + 16 * a + lk + 4 * r;
+          if (i < d) A[i * d + k0 + wc + 16 * b + li] = acc[a][b][r];
+        }
   }
 }
 
@@ -307,37 +394,6 @@ __device__ inline void mfma_f64_block(const double (*As)[KT + 1], const double (
 #pragma unroll
       for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
   }
-}
-
-// Rows i >= k0+NB: A[i][k0:k0+NB] <- A[i][k0:k0+NB] Linv^T (fp64 MFMA, K = 64).
-__global__ __launch_bounds__(256) void trsm_rows_kernel(double* A, int64_t d, int64_t k0, const double* Dinv) {
-  __shared__ double Xs[64][NB + 1];
-  __shared__ double Bs[NB][64 + 1];  // Bs[k][j] = Linv[j][k]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t r0 = k0 + NB + (int64_t)blockIdx.x * 64;
-  for (int idx = tid; idx < 64 * NB; idx += 256) {
-    const int r = idx / NB, c = idx % NB;
-    Xs[r][c] = (r0 + r < d) ? A[(r0 + r) * d + k0 + c] : 0.0;
-    Bs[c][r] = Dinv[(k0 + r) * NB + c];
-  }
-  __syncthreads();
-  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
-  double4v acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = (double4v){0.0, 0.0, 0.0, 0.0};
-  mfma_f64_block<NB>(Xs, Bs, wr, wc, lane, acc);
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t i = r0 + wr + a * 16 + (lane >> 4) + 4 * r;
-        const int c = wc + b * 16 + (lane & 15);
-        if (i < d) A[i * d + k0 + c] = acc[a][b][r];
-      }
 }
 
 // Delayed Cholesky update: A[i][j] -= sum_{k in [ka, ka + K)} A[i][k] A[j][k]
@@ -541,7 +597,7 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
                      ldh, (const double*)w.lam, w.A);
   GPTQ_CHECK_LAUNCH();
   // Blocked right-looking Cholesky in two levels: NB-wide panels are factored
-  // (potf2 + trsm) inside outer panels of CP columns, each NB panel updating
+  // (panel_kernel) inside outer panels of CP columns, each NB panel updating
   // only the rest of its outer panel; the trailing matrix receives one update
   // of depth CP per outer panel, so it is read and written d / CP times instead
   // of d / NB times.
@@ -550,13 +606,11 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
   for (int64_t p0 = 0; p0 < d; p0 += CP) {
     const int64_t pe = p0 + CP < d ? p0 + CP : d;
     for (int64_t k0 = p0; k0 < pe; k0 += NB) {
-      hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(256), 0, st, w.A, d, k0, w.Dinv, info);
-      GPTQ_CHECK_LAUNCH();
       const int64_t rest = d - k0 - NB;
-      if (rest <= 0) break;
-      const int64_t rb = ceil_div(rest, 64);
-      hipLaunchKernelGGL(trsm_rows_kernel, dim3((unsigned)rb), dim3(256), 0, st, w.A, d, k0, (const double*)w.Dinv);
+      const int64_t rb = rest > 0 ? ceil_div(rest, 64) : 1;
+      hipLaunchKernelGGL(panel_kernel, dim3((unsigned)rb), dim3(256), 0, st, w.A, d, k0, w.Dinv, info);
       GPTQ_CHECK_LAUNCH();
+      if (rest <= 0) break;
       if (k0 + NB < pe) {
         const int64_t c0 = k0 + NB;
         dim3 grid((unsigned)ceil_div(pe - c0, 64), (unsigned)ceil_div(d - c0, 64));

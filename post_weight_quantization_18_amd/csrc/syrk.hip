@@ -201,45 +201,6 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
         outer[f][h][r] = 0.0f;
       }
 
-  // B operand from bB (the I buffer itself on diagonal tiles): the two cases
-  // are separate code paths so every LDS read has one known LDS object.
-  // The DMA of stage s+2 (into the buffer stage s-1 used) is spread over the
-  // four 16-token slices of stage s so that its address arithmetic overlaps the
-  // matrix cores. Fragments run one slice ahead; scheduling barriers keep it to
-  // one slice, which bounds the registers the reads occupy.
-  auto compute_from = [&](const half_t* bI, const half_t* bB, int bp, bool refill, int64_t t_next, int b_next) __attribute__((always_inline)) {
-    const bool full = tile_inside && t_next + KS <= tok1;
-    half8 af[2][FI], bf[2][2];
-#pragma unroll
-    for (int f = 0; f < FI; ++f) af[0][f] = frag(bI + offA[f], TI);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) bf[0][h] = frag(bB + offB[h], bp);
-#pragma unroll
-    for (int kk = 0; kk < KS / 16; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (refill) {
-        constexpr int PI = EI / (KS / 16), PJ = EJ >= KS / 16 ? EJ / (KS / 16) : 1;
-#pragma unroll
-        for (int e = 0; e < PI; ++e) issue_I(kk * PI + e, t_next, b_next, full);
-        if (!j_in_i && kk * PJ < EJ) {
-#pragma unroll
-          for (int e = 0; e < PJ; ++e) issue_J(kk * PJ + e, t_next, b_next, full);
-        }
-      }
-      if (kk + 1 < KS / 16) {
-#pragma unroll
-        for (int f = 0; f < FI; ++f) af[nxt][f] = frag(bI + offA[f] + (kk + 1) * 16 * TI, TI);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) bf[nxt][h] = frag(bB + offB[h] + (kk + 1) * 16 * bp, bp);
-      }
-#pragma unroll
-      for (int f = 0; f < FI; ++f)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          acc[f][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][f], bf[cur][h], acc[f][h], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
   auto fold = [&]() __attribute__((always_inline)) {
     // Fast2Sum(outer, acc): outer <- fl(outer + acc), acc <- exact residual.
 #pragma unroll
@@ -265,33 +226,80 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
 #pragma unroll
   for (int p = 0; p < NBUF - 1; ++p)
     if (p < nstages) issue(tok0 + (int64_t)p * KS, p);
+
+  // Stage s uses ring buffer s mod NBUF and is cut into KS/16 slices of 16
+  // tokens. Slice k issues its share of the DMA of stage s + NBUF - 1 (into the
+  // buffer stage s - 1 used), then the fragment reads of slice k + 1, and only
+  // then its own matrix-core work, so every read has a whole slice of MFMAs to
+  // land. The last slice instead waits for stage s + 1's DMA, passes the
+  // workgroup barrier and reads stage s + 1's first slice: the barrier and that
+  // read are hidden behind the last slice's MFMAs, and once every wave is past
+  // it no wave reads buffer s again, so stage s + 1 may refill it.
   // The stage loop is instantiated once per tile kind (diagonal tiles read B
   // from the I buffer): a branch inside the loop would make the compiler merge
   // the accumulators of the two paths with register copies on every stage.
+  static_assert((KS / 16) % 2 == 0, "fragment slots alternate within a stage");
   auto stage_loop = [&](auto diag_tag) __attribute__((always_inline)) {
     constexpr bool DIAG = decltype(diag_tag)::value;
+    constexpr int PER = DIAG ? EI : EI + EJ;  // DMA instructions per wave per stage
+    constexpr int bp = DIAG ? TI : TJ;
+    auto buf_b = [&](int b) __attribute__((always_inline)) { return DIAG ? stage_i(b) : stage_j(b); };
+    half8 af[2][FI], bf[2][2];
+    auto read_slice = [&](int b, int kk, int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int f = 0; f < FI; ++f) af[slot][f] = frag(stage_i(b) + offA[f] + kk * 16 * TI, TI);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) bf[slot][h] = frag(buf_b(b) + offB[h] + kk * 16 * bp, bp);
+    };
+    // stage s's DMA has landed for every wave once at most the later stages'
+    // loads (up to NBUF - 2 stages of PER loads each) remain in flight
+    auto wait_stage = [&](int st) __attribute__((always_inline)) {
+      const int later = (nstages - 1 - st) < (NBUF - 2) ? (nstages - 1 - st) : (NBUF - 2);
+      wait_vm_stages<PER, NBUF - 2>(later);
+      lds_barrier();
+    };
+    if (nstages > 0) {
+      wait_stage(0);
+      read_slice(0, 0, 0);
+    }
     int cur = 0;
     for (int s = 0; s < nstages; ++s) {
-      // wait for this stage's DMA (the next stage's loads may stay in flight),
-      // barrier, then run the matrix cores while refilling the buffer the
-      // previous stage used.
-      // this stage's loads are complete once at most the later stages' loads
-      // (up to NBUF - 2 stages of PER loads each) remain in flight
-      {
-        constexpr int PER = DIAG ? EI : EI + EJ;
-        const int later = (nstages - 1 - s) < (NBUF - 2) ? (nstages - 1 - s) : (NBUF - 2);
-        wait_vm_stages<PER, NBUF - 2>(later);
-      }
-      lds_barrier();
       const int nxt = cur == 0 ? NBUF - 1 : cur - 1;  // the buffer stage s - 1 used
+      const int cnext = cur == NBUF - 1 ? 0 : cur + 1;
       const bool refill = s + NBUF - 1 < nstages;
       const int64_t t_next = tok0 + (int64_t)(s + NBUF - 1) * KS;
-      if (DIAG)
-        compute_from(stage_i(cur), stage_i(cur), TI, refill, t_next, nxt);
-      else
-        compute_from(stage_i(cur), stage_j(cur), TJ, refill, t_next, nxt);
+      const bool full = tile_inside && t_next + KS <= tok1;
+#pragma unroll
+      for (int kk = 0; kk < KS / 16; ++kk) {
+        if (refill) {
+          constexpr int PI = EI / (KS / 16), PJ = EJ >= KS / 16 ? EJ / (KS / 16) : 1;
+#pragma unroll
+          for (int e = 0; e < PI; ++e) issue_I(kk * PI + e, t_next, nxt, full);
+          if (!DIAG && kk * PJ < EJ) {
+#pragma unroll
+            for (int e = 0; e < PJ; ++e) issue_J(kk * PJ + e, t_next, nxt, full);
+          }
+        }
+        if (kk + 1 < KS / 16) {
+          read_slice(cur, kk + 1, (kk + 1) & 1);
+        } else {
+          // after the last stage this waits for nothing and reads a buffer
+          // that is never used; unconditional, so the read counters the
+          // compiler tracks stay exact
+          wait_stage(s + 1);
+          read_slice(cnext, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int slot = kk & 1;
+#pragma unroll
+        for (int f = 0; f < FI; ++f)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            acc[f][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[slot][f], bf[slot][h], acc[f][h], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if ((s + 1) % FOLD == 0) fold();
-      cur = cur == NBUF - 1 ? 0 : cur + 1;
+      cur = cnext;
     }
   };
   if (j_in_i)
