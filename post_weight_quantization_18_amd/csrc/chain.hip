@@ -204,6 +204,7 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
                                                    int32_t* info) {
   __shared__ double L[NB * LP];
   __shared__ double Li[NB * LP];
+  __shared__ double col[64];  // leaf column broadcast
   const int nb = (int)((d - k0) < NB ? (d - k0) : NB);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -252,11 +253,12 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
         const double a = L[(b0 + t) * LP + b0 + j];
         g[j] = inv ? (j == t ? 1.0 : 0.0) : (j <= t ? a : 0.0);
       }
-      // Step c updates entry c + 1 (the next pivot) at once and entries
-      // c + 2 .. 15 during step c + 1, where they overlap that pivot's inverse
-      // square root. The empty asm statements pin each update to its step: a
-      // later update would keep its scalar lane reads alive and overflow the
-      // scalar registers.
+      // Step c updates entry c + 1 (the next pivot) at once, with L[c + 1][c]
+      // read from lane c + 1, and entries c + 2 .. 15 during step c + 1, where
+      // they overlap that pivot's inverse square root; their L[j][c] come
+      // through LDS (one write, broadcast reads), which keeps the vector ALU
+      // free of lane reads.
+      double colv[LEAF];
       double vprev = 0.0;
 #pragma unroll
       for (int c = 0; c < LEAF; ++c) {
@@ -267,16 +269,15 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
         const double rs = rsqrt_f64(p);
         if (c > 0) {
 #pragma unroll
-          for (int j = c + 1; j < LEAF; ++j) {
-            g[j] = fma(-vprev, readlane_f64(vprev, j), g[j]);
-            asm volatile("" : "+v"(g[j]));
-          }
+          for (int j = c + 1; j < LEAF; ++j) g[j] = fma(-vprev, colv[j], g[j]);
         }
         const double vc = g[c] * rs;  // L[t][c] (row lanes) or Li[c][t] (inverse lanes)
         g[c] = vc;
-        if (c + 1 < LEAF) {
-          g[c + 1] = fma(-vc, readlane_f64(vc, c + 1), g[c + 1]);
-          asm volatile("" : "+v"(g[c + 1]));
+        if (c + 1 < LEAF) g[c + 1] = fma(-vc, readlane_f64(vc, c + 1), g[c + 1]);
+        if (c + 2 < LEAF) {
+          col[lane] = vc;  // the wave's LDS accesses stay in order: the reads see this write
+#pragma unroll
+          for (int j = c + 2; j < LEAF; ++j) colv[j] = col[j];
         }
         vprev = vc;
       }
