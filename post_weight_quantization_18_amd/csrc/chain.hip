@@ -125,6 +125,119 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const void* H, int h
   }
 }
 
+// One 64x64 fp64 MFMA tile step: acc[2][2] += As[rows][k..k+15] * Bs[k..k+15][cols]
+// for a wave's 32x32 sub-tile. As is [64][KT+1] (row, k); Bs is [KT][64+1] (k, col).
+// v_mfma_f64_16x16x4: A lane l holds A[l%16][l/16], B lane l holds B[l/16][l%16],
+// D lane l, reg r holds D[l/16 + 4r][l%16].
+template <int KT>
+__device__ inline void mfma_f64_block(const double (*As)[KT + 1], const double (*Bs)[64 + 1], int wr, int wc,
+                                      int lane, double4v (&acc)[2][2]) {
+  const int li = lane & 15, lk = lane >> 4;
+#pragma unroll
+  for (int k = 0; k < KT; k += 4) {
+    double av[2], bv[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) av[a] = As[wr + a * 16 + li][k + lk];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) bv[b] = Bs[k + lk][wc + b * 16 + li];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
+  }
+}
+
+// Delayed Cholesky update of one 64 x 64 tile (row tile ti, column tile tj
+// from c0): A[i][j] -= sum_{k in [ka, ka + K)} A[i][k] A[j][k] for i < d,
+// j < c1, j <= i (the strictly upper triangle stays zero). 4 waves of 32 x 32
+// (fp64 MFMA 16x16x4); K is staged KT columns at a time through the caller's
+// LDS (As [64][KT + 1], Bs [KT][64 + 1]) with the next slice prefetched into
+// registers.
+template <int KT>
+__device__ __forceinline__ void update_tile(double* A, int64_t d, int64_t ka, int64_t K, int64_t c0, int64_t c1,
+                                            int ti, int tj, double (*As)[KT + 1], double (*Bs)[64 + 1]) {
+  const int64_t i0 = c0 + (int64_t)ti * 64, j0 = c0 + (int64_t)tj * 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+  double4v acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = (double4v){0.0, 0.0, 0.0, 0.0};
+  const int64_t ke = ka + K;
+  // each thread stages 8 elements of each 64 x KT panel, rows idx / KT, columns idx % KT
+  double pa[8], pb[8];
+  auto fetch = [&](int64_t k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e;
+      const int r = idx / KT, c = idx % KT;
+      const int64_t gk = k + c;
+      pa[e] = (i0 + r < d && gk < ke) ? A[(i0 + r) * d + gk] : 0.0;
+      pb[e] = (j0 + r < c1 && gk < ke) ? A[(j0 + r) * d + gk] : 0.0;
+    }
+  };
+  fetch(ka);
+  for (int64_t k = ka; k < ke; k += KT) {
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e;
+      As[idx / KT][idx % KT] = pa[e];
+      Bs[idx % KT][idx / KT] = pb[e];
+    }
+    __syncthreads();
+    if (k + KT < ke) fetch(k + KT);
+    mfma_f64_block<KT>(As, Bs, wr, wc, lane, acc);
+  }
+  // all 16 old values are read before any is written: one memory round trip
+  // for the read-modify-write instead of one per element
+  double old[2][2][4];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t i = i0 + wr + x * 16 + (lane >> 4) + 4 * r;
+        const int64_t j = j0 + wc + y * 16 + (lane & 15);
+        old[x][y][r] = (i < d && j < c1 && j <= i) ? A[i * d + j] : 0.0;
+      }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t i = i0 + wr + x * 16 + (lane >> 4) + 4 * r;
+        const int64_t j = j0 + wc + y * 16 + (lane & 15);
+        if (i < d && j < c1 && j <= i) A[i * d + j] = old[x][y][r] - acc[x][y][r];
+      }
+}
+
+// The update above over a grid of tiles.
+// tri = 1: c1 = d and blockIdx.x enumerates the lower triangle of tiles;
+// tri = 0: grid (column tiles, row tiles), tiles above the diagonal exit.
+__global__ __launch_bounds__(256) void update_f64_kernel(double* A, int64_t d, int64_t ka, int64_t K, int64_t c0,
+                                                         int64_t c1, int tri) {
+  constexpr int KT = 32;
+  __shared__ double As[64][KT + 1];
+  __shared__ double Bs[KT][64 + 1];
+  int ti, tj;
+  if (tri) {
+    const int t = blockIdx.x;
+    ti = (int)((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
+    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+    while (ti * (ti + 1) / 2 > t) --ti;
+    tj = t - ti * (ti + 1) / 2;
+  } else {
+    tj = blockIdx.x;
+    ti = blockIdx.y;
+    if (ti < tj) return;  // uniform per workgroup
+  }
+  update_tile<KT>(A, d, ka, K, c0, c1, ti, tj, As, Bs);
+}
+
 // Factor the 64 x 64 diagonal block at k0 (lower Cholesky) and invert the
 // factor, in one workgroup of 4 waves, blocked by 16 columns so that only the
 // 16-column leaves are serial. For each 16-block:
@@ -200,11 +313,22 @@ __device__ __forceinline__ void store16(double* P, double4v v, int li, int lk) {
   for (int r = 0; r < 4; ++r) P[(lk + 4 * r) * LP + li] = v[r];
 }
 
-__global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_t k0, double* Dinv,
-                                                   int32_t* info) {
+__global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_t k0, int64_t prev, int64_t pe,
+                                                   int rb, double* Dinv, int32_t* info) {
   __shared__ double L[NB * LP];
   __shared__ double Li[NB * LP];
-  __shared__ double col[64];  // leaf column broadcast
+  __shared__ double Pd[NB * LP];  // panel prev's rows of the block: A[k0 + r][prev + c]
+  __shared__ double Xs[NB * LP];  // panel prev's rows of the slab, then the slab itself
+  __shared__ double col[64];      // leaf column broadcast
+  if ((int)blockIdx.x >= rb) {
+    // ---- the pending update of columns [k0 + NB, pe) by panel prev ----
+    const int64_t c0 = k0 + NB;
+    const int ncol = (int)((pe - c0 + 63) / 64);
+    const int u = (int)blockIdx.x - rb, tj = u % ncol, ti = u / ncol;
+    if (ti < tj) return;  // above the diagonal (uniform)
+    update_tile<32>(A, d, prev, NB, c0, pe, ti, tj, (double(*)[33])L, (double(*)[65])Li);
+    return;
+  }
   const int nb = (int)((d - k0) < NB ? (d - k0) : NB);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -213,34 +337,79 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
   // this workgroup's slab of rows below the block (none when it is the last)
   const int64_t r0 = k0 + NB + (int64_t)blockIdx.x * NB;
   const bool has_slab = r0 < d;
-  double xs[NB / 4];
-  if (has_slab) {
-#pragma unroll
-    for (int q = 0; q < NB / 4; ++q) {
-      const int64_t r = r0 + w + 4 * q;
-      xs[q] = A[(r < d ? r : r0) * d + k0 + lane];  // rows past d repeat row r0 (not stored)
-    }
-  }
+  const bool upd = prev >= 0;
   {
-    // thread: column lane of rows w + 4q; the loads are unconditional (a
-    // masked-off element reads the block's first entry) and all issued before
-    // the first LDS write
-    double v[NB / 4];
+    // thread: column lane of rows w + 4q. The loads are unconditional (a
+    // masked-off element reads a valid entry and is replaced) and all issued
+    // before the first LDS write.
+    double v[NB / 4], xs[NB / 4], pd[NB / 4], ps[NB / 4];
 #pragma unroll
     for (int q = 0; q < NB / 4; ++q) {
       const int r = w + 4 * q;
       const int rr = r < nb ? r : 0, cc = lane < nb ? lane : 0;  // clamped into the block
       v[q] = blk[(int64_t)rr * d + cc];
+      const int64_t sr = r0 + r < d ? r0 + r : k0;  // slab rows past d read row k0 (not stored)
+      if (has_slab) xs[q] = A[sr * d + k0 + lane];
+      if (upd) {
+        pd[q] = A[(k0 + rr) * d + prev + lane];
+        if (has_slab) ps[q] = A[sr * d + prev + lane];
+      }
     }
 #pragma unroll
     for (int q = 0; q < NB / 4; ++q) {
       const int r = w + 4 * q;
       const bool in = r < nb && lane <= r;
       L[r * LP + lane] = in ? v[q] : (r == lane ? 1.0 : 0.0);  // identity padding past d
-      Li[r * LP + lane] = 0.0;
+      if (upd) {
+        Pd[r * LP + lane] = r < nb ? pd[q] : 0.0;
+        // the slab waits in Li while panel prev's slab rows sit in Xs
+        if (has_slab) {
+          Li[r * LP + lane] = xs[q];
+          Xs[r * LP + lane] = ps[q];
+        }
+      } else {
+        Li[r * LP + lane] = 0.0;
+        if (has_slab) Xs[r * LP + lane] = xs[q];
+      }
     }
   }
   __syncthreads();
+  if (upd) {
+    // ---- block column k0 takes panel prev's update (the rest of its outer
+    // panel is done by the extra workgroups): block -= Pd Pd^T, slab -= Ps Pd^T;
+    // wave (wr, wc) owns a 32 x 32 quarter of each ----
+    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+    double4v db[2][2], sb[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        db[a][b] = load16(&L[(wr + 16 * a) * LP + wc + 16 * b], li, lk);
+        db[a][b] = mm16_nt<true>(&Pd[(wr + 16 * a) * LP], &Pd[(wc + 16 * b) * LP], db[a][b], li, lk);
+        db[a][b] = mm16_nt<true>(&Pd[(wr + 16 * a) * LP + 16], &Pd[(wc + 16 * b) * LP + 16], db[a][b], li, lk);
+        db[a][b] = mm16_nt<true>(&Pd[(wr + 16 * a) * LP + 32], &Pd[(wc + 16 * b) * LP + 32], db[a][b], li, lk);
+        db[a][b] = mm16_nt<true>(&Pd[(wr + 16 * a) * LP + 48], &Pd[(wc + 16 * b) * LP + 48], db[a][b], li, lk);
+        if (has_slab) {
+          sb[a][b] = load16(&Li[(wr + 16 * a) * LP + wc + 16 * b], li, lk);
+#pragma unroll
+          for (int kb = 0; kb < NB; kb += 16)
+            sb[a][b] = mm16_nt<true>(&Xs[(wr + 16 * a) * LP + kb], &Pd[(wc + 16 * b) * LP + kb], sb[a][b], li, lk);
+        }
+      }
+    __syncthreads();  // every wave has read L, Li, Pd and Xs
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        store16(&L[(wr + 16 * a) * LP + wc + 16 * b], db[a][b], li, lk);
+        if (has_slab) store16(&Xs[(wr + 16 * a) * LP + wc + 16 * b], sb[a][b], li, lk);
+      }
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) Li[(w + 4 * q) * LP + lane] = 0.0;
+    // rows past d of the block must stay identity: they received nothing (Pd
+    // rows past nb are zero), and the factorisation masks the upper triangle
+    __syncthreads();
+  }
   int first_bad = -1;  // first failing pivot of the block (wave 0)
   for (int b0 = 0; b0 < NB; b0 += LEAF) {
     // ---- (1) leaf factor and inverse (wave 0; lanes 32-63 repeat 0-31) ----
@@ -339,10 +508,7 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
     }
   }
   if (!has_slab) return;  // uniform over the workgroup
-  // ---- slab: X <- X L11^-T, X staged in L's storage (L is no longer read) ----
-#pragma unroll
-  for (int q = 0; q < NB / 4; ++q) L[(w + 4 * q) * LP + lane] = xs[q];
-  __syncthreads();
+  // ---- slab: X <- X L11^-T (X in Xs since the start) ----
   {
     // wave (wr, wc): 32 x 32 of the 64 x 64 result; out[i][j] = sum_k X[i][k] Li[j][k]
     const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
@@ -355,7 +521,7 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
     for (int k = 0; k < NB; k += 4) {
       double av[2], bv[2];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) av[a] = L[(wr + 16 * a + li) * LP + k + lk];
+      for (int a = 0; a < 2; ++a) av[a] = Xs[(wr + 16 * a + li) * LP + k + lk];
 #pragma unroll
       for (int b = 0; b < 2; ++b) bv[b] = Li[(wc + 16 * b + li) * LP + k + lk];
 #pragma unroll
@@ -373,110 +539,6 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
           if (i < d) A[i * d + k0 + wc + 16 * b + li] = acc[a][b][r];
         }
   }
-}
-
-// One 64x64 fp64 MFMA tile step: acc[2][2] += As[rows][k..k+15] * Bs[k..k+15][cols]
-// for a wave's 32x32 sub-tile. As is [64][KT+1] (row, k); Bs is [KT][64+1] (k, col).
-// v_mfma_f64_16x16x4: A lane l holds A[l%16][l/16], B lane l holds B[l/16][l%16],
-// D lane l, reg r holds D[l/16 + 4r][l%16].
-template <int KT>
-__device__ inline void mfma_f64_block(const double (*As)[KT + 1], const double (*Bs)[64 + 1], int wr, int wc,
-                                      int lane, double4v (&acc)[2][2]) {
-  const int li = lane & 15, lk = lane >> 4;
-#pragma unroll
-  for (int k = 0; k < KT; k += 4) {
-    double av[2], bv[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) av[a] = As[wr + a * 16 + li][k + lk];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) bv[b] = Bs[k + lk][wc + b * 16 + li];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
-  }
-}
-
-// Delayed Cholesky update: A[i][j] -= sum_{k in [ka, ka + K)} A[i][k] A[j][k]
-// for i in [c0, d), j in [c0, c1), j <= i (the strictly upper triangle stays
-// zero). 64 x 64 tiles (4 waves of 32 x 32, fp64 MFMA 16x16x4), K staged 32
-// columns at a time through LDS with the next slice prefetched into registers.
-// tri = 1: c1 = d and blockIdx.x enumerates the lower triangle of tiles;
-// tri = 0: grid (column tiles, row tiles), tiles above the diagonal exit.
-__global__ __launch_bounds__(256) void update_f64_kernel(double* A, int64_t d, int64_t ka, int64_t K, int64_t c0,
-                                                         int64_t c1, int tri) {
-  constexpr int KT = 32;
-  __shared__ double As[64][KT + 1];
-  __shared__ double Bs[KT][64 + 1];
-  int ti, tj;
-  if (tri) {
-    const int t = blockIdx.x;
-    ti = (int)((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
-    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-    while (ti * (ti + 1) / 2 > t) --ti;
-    tj = t - ti * (ti + 1) / 2;
-  } else {
-    tj = blockIdx.x;
-    ti = blockIdx.y;
-    if (ti < tj) return;  // uniform per workgroup
-  }
-  const int64_t i0 = c0 + (int64_t)ti * 64, j0 = c0 + (int64_t)tj * 64;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
-  double4v acc[2][2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = (double4v){0.0, 0.0, 0.0, 0.0};
-  const int64_t ke = ka + K;
-  // each thread stages 8 elements of each 64 x KT panel, rows idx / KT, columns idx % KT
-  double pa[8], pb[8];
-  auto fetch = [&](int64_t k) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int idx = tid + 256 * e;
-      const int r = idx / KT, c = idx % KT;
-      const int64_t gk = k + c;
-      pa[e] = (i0 + r < d && gk < ke) ? A[(i0 + r) * d + gk] : 0.0;
-      pb[e] = (j0 + r < c1 && gk < ke) ? A[(j0 + r) * d + gk] : 0.0;
-    }
-  };
-  fetch(ka);
-  for (int64_t k = ka; k < ke; k += KT) {
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int idx = tid + 256 * e;
-      As[idx / KT][idx % KT] = pa[e];
-      Bs[idx % KT][idx / KT] = pb[e];
-    }
-    __syncthreads();
-    if (k + KT < ke) fetch(k + KT);
-    mfma_f64_block<KT>(As, Bs, wr, wc, lane, acc);
-  }
-  // all 16 old values are read before any is written: one memory round trip
-  // for the read-modify-write instead of one per element
-  double old[2][2][4];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t i = i0 + wr + x * 16 + (lane >> 4) + 4 * r;
-        const int64_t j = j0 + wc + y * 16 + (lane & 15);
-        old[x][y][r] = (i < d && j < c1 && j <= i) ? A[i * d + j] : 0.0;
-      }
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t i = i0 + wr + x * 16 + (lane >> 4) + 4 * r;
-        const int64_t j = j0 + wc + y * 16 + (lane & 15);
-        if (i < d && j < c1 && j <= i) A[i * d + j] = old[x][y][r] - acc[x][y][r];
-      }
 }
 
 // Every diagonal NB-block of A <- its inverse (lower, zero upper).
@@ -607,17 +669,19 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
   for (int64_t p0 = 0; p0 < d; p0 += CP) {
     const int64_t pe = p0 + CP < d ? p0 + CP : d;
     for (int64_t k0 = p0; k0 < pe; k0 += NB) {
+      // one launch per panel: rb workgroups factor block k0 (each first
+      // applying panel k0 - NB's update to its part of block column k0) and
+      // solve the rows below; the others apply panel k0 - NB's update to the
+      // columns [k0 + NB, pe) of the outer panel
       const int64_t rest = d - k0 - NB;
       const int64_t rb = rest > 0 ? ceil_div(rest, 64) : 1;
-      hipLaunchKernelGGL(panel_kernel, dim3((unsigned)rb), dim3(256), 0, st, w.A, d, k0, w.Dinv, info);
+      const int64_t prev = k0 > p0 ? k0 - NB : -1;
+      const int64_t c0 = k0 + NB;
+      const int64_t nupd = (prev >= 0 && c0 < pe) ? ceil_div(pe - c0, 64) * ceil_div(d - c0, 64) : 0;
+      hipLaunchKernelGGL(panel_kernel, dim3((unsigned)(rb + nupd)), dim3(256), 0, st, w.A, d, k0, prev, pe,
+                         (int)rb, w.Dinv, info);
       GPTQ_CHECK_LAUNCH();
       if (rest <= 0) break;
-      if (k0 + NB < pe) {
-        const int64_t c0 = k0 + NB;
-        dim3 grid((unsigned)ceil_div(pe - c0, 64), (unsigned)ceil_div(d - c0, 64));
-        hipLaunchKernelGGL(update_f64_kernel, grid, dim3(256), 0, st, w.A, d, k0, (int64_t)NB, c0, pe, 0);
-        GPTQ_CHECK_LAUNCH();
-      }
     }
     if (pe < d) {
       const int64_t rb = ceil_div(d - pe, 64);
