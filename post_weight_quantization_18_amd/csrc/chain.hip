@@ -422,33 +422,40 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
         const double a = L[(b0 + t) * LP + b0 + j];
         g[j] = inv ? (j == t ? 1.0 : 0.0) : (j <= t ? a : 0.0);
       }
-      // Step c updates entry c + 1 (the next pivot) at once, with L[c + 1][c]
-      // read from lane c + 1, and entries c + 2 .. 15 during step c + 1, where
-      // they overlap that pivot's inverse square root; their L[j][c] come
-      // through LDS (one write, broadcast reads), which keeps the vector ALU
-      // free of lane reads.
+      // Step c updates entry c + 1 at once, with L[c + 1][c] read from lane
+      // c + 1, and entries c + 2 .. 15 during step c + 1, where they overlap
+      // that pivot's inverse square root; their L[j][c] come through LDS (one
+      // write, broadcast reads issued in step c, a whole step before use).
+      // The pivot chain is short: lane c + 1 holds L[c + 1][c] itself, so its
+      // updated diagonal, the next pivot, needs no broadcast; a failing pivot
+      // is replaced by 1 after the rsqrt, off the chain.
       double colv[LEAF];
       double vprev = 0.0;
+      double p = readlane_f64(g[0], 0);
 #pragma unroll
       for (int c = 0; c < LEAF; ++c) {
-        double p = readlane_f64(g[c], c);
+        double rs = rsqrt_f64(p);
         const bool bad = !(p > 0.0);  // not positive definite (or NaN): go on with 1
+        rs = bad ? 1.0 : rs;
         first_bad = (bad && first_bad < 0) ? b0 + c : first_bad;
-        p = bad ? 1.0 : p;
-        const double rs = rsqrt_f64(p);
         if (c > 0) {
 #pragma unroll
           for (int j = c + 1; j < LEAF; ++j) g[j] = fma(-vprev, colv[j], g[j]);
         }
         const double vc = g[c] * rs;  // L[t][c] (row lanes) or Li[c][t] (inverse lanes)
         g[c] = vc;
-        if (c + 1 < LEAF) g[c + 1] = fma(-vc, readlane_f64(vc, c + 1), g[c + 1]);
+        if (c + 1 < LEAF) {
+          // lane c + 1 holds L[c + 1][c] itself: its updated diagonal is the next pivot
+          p = readlane_f64(fma(-vc, vc, g[c + 1]), c + 1);
+          g[c + 1] = fma(-vc, readlane_f64(vc, c + 1), g[c + 1]);
+        }
         if (c + 2 < LEAF) {
           col[lane] = vc;  // the wave's LDS accesses stay in order: the reads see this write
 #pragma unroll
           for (int j = c + 2; j < LEAF; ++j) colv[j] = col[j];
         }
         vprev = vc;
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (lane < LEAF) {
 #pragma unroll
