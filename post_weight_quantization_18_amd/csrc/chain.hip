@@ -564,11 +564,16 @@ __global__ __launch_bounds__(256) void put_diag_inverse_kernel(double* A, int64_
 //   MODE 0: T[r][col - a0] = sum_{k in [col tile, c0)} B[r][k] Ainv[k][col]
 //   MODE 1: A[r][col] = -sum_{k in [c0, r tile end)} Cinv[r][k] T[k][col - a0]
 // grid: x = column tile in [a0, c0), y = row tile in [c0, c1), z = pair.
-template <int MODE>
-__global__ __launch_bounds__(256) void merge_kernel(double* A, int64_t d, double* T, int64_t ldt, int64_t s) {
+// KG groups of 4 waves split each tile's K range into equal KT-aligned parts
+// (the last padded with zeros, so every group runs the same iterations) and
+// the groups' tiles are summed in LDS in group order: at small d the longest
+// K range, not the tile count, sets the launch's time.
+template <int MODE, int KG>
+__global__ __launch_bounds__(256 * KG) void merge_kernel(double* A, int64_t d, double* T, int64_t ldt, int64_t s) {
   constexpr int KT = 32;
-  __shared__ double As[64][KT + 1];
-  __shared__ double Bs[KT][64 + 1];
+  constexpr int AS = 64 * (KT + 1), BS = KT * (64 + 1);  // one group's A and B stages
+  static_assert(KG == 1 || (KG - 1) * 64 * 64 <= KG * (AS + BS), "the partial tiles fit in the stages");
+  __shared__ double smem[KG * (AS + BS)];
   const int64_t a0 = (int64_t)blockIdx.z * 2 * s, c0 = a0 + s;
   int64_t c1 = a0 + 2 * s;
   if (c1 > d) c1 = d;
@@ -583,8 +588,12 @@ __global__ __launch_bounds__(256) void merge_kernel(double* A, int64_t d, double
     kb = c0;
     ke = r0 + 64 < c1 ? r0 + 64 : c1;
   }
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = (int)(threadIdx.x >> 8);  // K group
+  const int tid = threadIdx.x & 255, lane = tid & 63, w = tid >> 6;
   const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+  const int64_t part = (ke - kb + KG * KT - 1) / (KG * KT) * KT;  // K per group, a multiple of KT
+  const int64_t gb = kb + g * part;
+  const int64_t ge = gb + part < ke ? gb + part : ke;  // may be empty for the last groups
   double4v acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -598,16 +607,18 @@ __global__ __launch_bounds__(256) void merge_kernel(double* A, int64_t d, double
       const int idx = tid + 256 * e;
       const int ar = idx / KT, ac = idx % KT;
       const int64_t gr = r0 + ar, gk = k + ac;
-      pa[e] = (gr < c1 && gk < ke) ? A[gr * d + gk] : 0.0;
+      pa[e] = (gr < c1 && gk < ge) ? A[gr * d + gk] : 0.0;
       const int br = idx / 64, bc = idx % 64;
       const int64_t bk = k + br, gc = col0 + bc;
       double v = 0.0;
-      if (bk < ke && gc < c0) v = (MODE == 0) ? A[bk * d + gc] : T[bk * ldt + (gc - a0)];
+      if (bk < ge && gc < c0) v = (MODE == 0) ? A[bk * d + gc] : T[bk * ldt + (gc - a0)];
       pb[e] = v;
     }
   };
-  fetch(kb);
-  for (int64_t k = kb; k < ke; k += KT) {
+  double (*As)[KT + 1] = (double(*)[KT + 1])(smem + g * AS);
+  double (*Bs)[64 + 1] = (double(*)[64 + 1])(smem + KG * AS + g * BS);
+  fetch(gb);
+  for (int64_t k = 0; k < part; k += KT) {  // the same count in every group
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -616,8 +627,34 @@ __global__ __launch_bounds__(256) void merge_kernel(double* A, int64_t d, double
       Bs[idx / 64][idx % 64] = pb[e];
     }
     __syncthreads();
-    if (k + KT < ke) fetch(k + KT);
+    if (k + KT < part) fetch(gb + k + KT);
     mfma_f64_block<KT>(As, Bs, wr, wc, lane, acc);
+  }
+  if constexpr (KG > 1) {
+    // groups 1 .. KG-1 leave their 64 x 64 tiles in the (now free) stages;
+    // group 0 adds them in group order and alone writes the result
+    __syncthreads();
+    if (g > 0) {
+      double* mine = smem + (g - 1) * 64 * 64;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            mine[(wr + a * 16 + (lane >> 4) + 4 * r) * 64 + wc + b * 16 + (lane & 15)] = acc[a][b][r];
+    }
+    __syncthreads();
+    if (g > 0) return;
+#pragma unroll
+    for (int h = 0; h < KG - 1; ++h)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[a][b][r] += smem[h * 64 * 64 + (wr + a * 16 + (lane >> 4) + 4 * r) * 64 + wc + b * 16 + (lane & 15)];
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -704,10 +741,18 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
   for (int64_t s = NB; s < d; s *= 2) {
     const int64_t pairs = ceil_div(d, 2 * s);
     dim3 grid((unsigned)(s / 64), (unsigned)(s / 64), (unsigned)pairs);
-    hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, st, w.A, d, w.T, ldt, s);
-    GPTQ_CHECK_LAUNCH();
-    hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, st, w.A, d, w.T, ldt, s);
-    GPTQ_CHECK_LAUNCH();
+    // a grid that cannot fill the GPU splits each tile's K range over 2 wave groups
+    if ((int64_t)grid.x * grid.y * grid.z < 512) {
+      hipLaunchKernelGGL((merge_kernel<0, 2>), grid, dim3(512), 0, st, w.A, d, w.T, ldt, s);
+      GPTQ_CHECK_LAUNCH();
+      hipLaunchKernelGGL((merge_kernel<1, 2>), grid, dim3(512), 0, st, w.A, d, w.T, ldt, s);
+      GPTQ_CHECK_LAUNCH();
+    } else {
+      hipLaunchKernelGGL((merge_kernel<0, 1>), grid, dim3(256), 0, st, w.A, d, w.T, ldt, s);
+      GPTQ_CHECK_LAUNCH();
+      hipLaunchKernelGGL((merge_kernel<1, 1>), grid, dim3(256), 0, st, w.A, d, w.T, ldt, s);
+      GPTQ_CHECK_LAUNCH();
+    }
   }
   hipLaunchKernelGGL(store_u_kernel, dim3((unsigned)ceil_div(d, 256) < 64 ? (unsigned)ceil_div(d, 256) : 64u,
                                           (unsigned)d),
