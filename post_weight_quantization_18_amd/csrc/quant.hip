@@ -178,6 +178,9 @@ struct ColArgs {
   int ngroups;
   float* E;        // errors out: E[r * lde + ecol + k] for the block's columns k
   int64_t lde, ecol;
+  half_t* Eh;      // when set, also the block's errors as scaled fp16 pairs (as esplit_kernel
+  half_t* El;      // writes them, K-tiled with slab stride m * 32) and the row scales einv
+  float* einv;
   uint8_t* codes;
   float* scales;
   uint8_t* zeros;
@@ -399,6 +402,35 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
     Steps<G, 0>::run(st, a, r, g, Us, rdiag, bw, first);
   }
 
+  if (a.Eh) {
+    // the row's power-of-two scale over the block (quad max of |e|; columns
+    // past bw hold 0), then the fp16 pair of every error: lane g's 32 columns
+    // are K-slab g, 32 consecutive halves at g * m * 32 + r * 32
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) mx = fmaxf(mx, fabsf(st.w[k]));
+    mx = fmaxf(mx, quad_xor1(mx));
+    mx = fmaxf(mx, quad_xor2(mx));
+    int ex = 0;
+    if (mx > 0.0f) frexpf(mx, &ex);
+    const float sc = mx > 0.0f ? ldexpf(1.0f, 15 - ex) : 1.0f;
+    if (live && cols_ok) {
+      half_t h[CPL], l[CPL];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        const float x = st.w[k] * sc;
+        h[k] = (half_t)x;
+        l[k] = (half_t)(x - (float)h[k]);
+      }
+      const int64_t o = (int64_t)g * a.m * 32 + r * 32;
+#pragma unroll
+      for (int k = 0; k < CPL; k += 8) {
+        *(uint4*)(a.Eh + o + k) = *(const uint4*)(h + k);
+        *(uint4*)(a.El + o + k) = *(const uint4*)(l + k);
+      }
+      if (g == 0) a.einv[r] = 1.0f / sc;
+    }
+  }
   if (live && cols_ok) {
     float* erow = a.E + r * a.lde + a.ecol + g * CPL;
 #pragma unroll
@@ -628,6 +660,11 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
     const int64_t sb0 = (a.j0 / S) * S;
     const int64_t sb1 = (sb0 + S) < d ? (sb0 + S) : d;
     a.ecol = a.j0 - sb0;
+    // an inner trailing update follows: the column loop splits its own errors
+    const bool inner = a.j0 + a.bw < sb1;
+    a.Eh = inner ? w.Ehb : nullptr;
+    a.El = inner ? w.Elb : nullptr;
+    a.einv = inner ? w.einv_b : nullptr;
     gptq_status_t s;
     switch (group) {
       case 0: s = launch_colloop<0>(a, st); break;
@@ -639,10 +676,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
     if (s != GPTQ_OK) return s;
     const int64_t j1 = a.j0 + a.bw;
     if (j1 < sb1) {
-      // the rest of the super-block: K = this block
-      hipLaunchKernelGGL(esplit_kernel, dim3(egrid), dim3(256), 0, st, (const float*)(w.Esb + a.ecol), S, m, a.bw,
-                         w.Ehb, w.Elb, m * 32, w.einv_b);
-      GPTQ_CHECK_LAUNCH();
+      // the rest of the super-block: K = this block (split by the column loop)
       t.C = w.Wk + j1;
       t.Ah = w.Ehb;
       t.Al = w.Elb;
