@@ -338,6 +338,26 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
   const int64_t r0 = k0 + NB + (int64_t)blockIdx.x * NB;
   const bool has_slab = r0 < d;
   const bool upd = prev >= 0;
+  // With a pending update (prev >= 0), wave 1 + v (v = 0, 1, 2) updates the
+  // slab's 16-row bands v and v + 3 (so a band is read and rewritten by one
+  // wave only); their old values come straight from memory in the MFMA result
+  // layout: band p, column tile q, register r of lane (lk, li) holds slab row
+  // 16 p + lk + 4 r, column 16 q + li.
+  const bool band_wave = upd && has_slab && w > 0;
+  double4v sold[2][4];
+  if (band_wave) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int p = (w - 1) + 3 * h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t row = r0 + 16 * p + lk + 4 * r;
+          sold[h][q][r] = (p < 4) ? A[(row < d ? row : r0) * d + k0 + 16 * q + li] : 0.0;
+        }
+    }
+  }
   {
     // thread: column lane of rows w + 4q. The loads are unconditional (a
     // masked-off element reads a valid entry and is replaced) and all issued
@@ -349,10 +369,11 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
       const int rr = r < nb ? r : 0, cc = lane < nb ? lane : 0;  // clamped into the block
       v[q] = blk[(int64_t)rr * d + cc];
       const int64_t sr = r0 + r < d ? r0 + r : k0;  // slab rows past d read row k0 (not stored)
-      if (has_slab) xs[q] = A[sr * d + k0 + lane];
       if (upd) {
         pd[q] = A[(k0 + rr) * d + prev + lane];
         if (has_slab) ps[q] = A[sr * d + prev + lane];
+      } else if (has_slab) {
+        xs[q] = A[sr * d + k0 + lane];
       }
     }
 #pragma unroll
@@ -360,55 +381,61 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
       const int r = w + 4 * q;
       const bool in = r < nb && lane <= r;
       L[r * LP + lane] = in ? v[q] : (r == lane ? 1.0 : 0.0);  // identity padding past d
+      Li[r * LP + lane] = 0.0;
       if (upd) {
         Pd[r * LP + lane] = r < nb ? pd[q] : 0.0;
-        // the slab waits in Li while panel prev's slab rows sit in Xs
-        if (has_slab) {
-          Li[r * LP + lane] = xs[q];
-          Xs[r * LP + lane] = ps[q];
-        }
-      } else {
-        Li[r * LP + lane] = 0.0;
-        if (has_slab) Xs[r * LP + lane] = xs[q];
+        if (has_slab) Xs[r * LP + lane] = ps[q];  // panel prev's slab rows, replaced band by band
+      } else if (has_slab) {
+        Xs[r * LP + lane] = xs[q];
       }
     }
   }
   __syncthreads();
   if (upd) {
     // ---- block column k0 takes panel prev's update (the rest of its outer
-    // panel is done by the extra workgroups): block -= Pd Pd^T, slab -= Ps Pd^T;
-    // wave (wr, wc) owns a 32 x 32 quarter of each ----
-    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
-    double4v db[2][2], sb[2][2];
+    // panel is done by the extra workgroups): block -= Pd Pd^T, slab -= Ps Pd^T.
+    // Wave 0 updates only the first 16 x 16 tile and goes on to factor it;
+    // waves 1-3 update the other lower tiles of the block and the slab
+    // meanwhile, and the barrier after the first leaf joins them. Every tile
+    // and band is read and written by one wave. Rows of the block past d stay
+    // identity (the Pd rows past nb are zero); the upper tiles are not needed
+    // (the factorisation reads the lower triangle only). ----
+    if (w == 0) {
+      double4v t = load16(&L[0], li, lk);
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+      for (int kb = 0; kb < NB; kb += 16) t = mm16_nt<true>(&Pd[kb], &Pd[kb], t, li, lk);
+      store16(&L[0], t, li, lk);
+    } else {
+      // the 9 lower tiles other than (0, 0): (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
+      for (int tix = w - 1; tix < 9; tix += 3) {
+        const int p = tix < 2 ? 1 : (tix < 5 ? 2 : 3);
+        const int q = tix - (p == 1 ? 0 : (p == 2 ? 2 : 5));
+        double* T = &L[16 * p * LP + 16 * q];
+        double4v t = load16(T, li, lk);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        db[a][b] = load16(&L[(wr + 16 * a) * LP + wc + 16 * b], li, lk);
-        db[a][b] = mm16_nt<true>(&Pd[(wr + 16 * a) * LP], &Pd[(wc + 16 * b) * LP], db[a][b], li, lk);
-        db[a][b] = mm16_nt<true>(&Pd[(wr + 16 * a) * LP + 16], &Pd[(wc + 16 * b) * LP + 16], db[a][b], li, lk);
-        db[a][b] = mm16_nt<true>(&Pd[(wr + 16 * a) * LP + 32], &Pd[(wc + 16 * b) * LP + 32], db[a][b], li, lk);
-        db[a][b] = mm16_nt<true>(&Pd[(wr + 16 * a) * LP + 48], &Pd[(wc + 16 * b) * LP + 48], db[a][b], li, lk);
-        if (has_slab) {
-          sb[a][b] = load16(&Li[(wr + 16 * a) * LP + wc + 16 * b], li, lk);
+        for (int kb = 0; kb < NB; kb += 16) t = mm16_nt<true>(&Pd[16 * p * LP + kb], &Pd[16 * q * LP + kb], t, li, lk);
+        store16(T, t, li, lk);
+      }
+      if (band_wave) {
 #pragma unroll
-          for (int kb = 0; kb < NB; kb += 16)
-            sb[a][b] = mm16_nt<true>(&Xs[(wr + 16 * a) * LP + kb], &Pd[(wc + 16 * b) * LP + kb], sb[a][b], li, lk);
+        for (int h = 0; h < 2; ++h) {
+          const int p = (w - 1) + 3 * h;
+          if (p < 4) {
+            double4v sb[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              sb[q] = sold[h][q];
+#pragma unroll
+              for (int kb = 0; kb < NB; kb += 16)
+                sb[q] = mm16_nt<true>(&Xs[16 * p * LP + kb], &Pd[16 * q * LP + kb], sb[q], li, lk);
+            }
+            // the wave's reads of its band precede these writes (one wave, in order)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) store16(&Xs[16 * p * LP + 16 * q], sb[q], li, lk);
+          }
         }
       }
-    __syncthreads();  // every wave has read L, Li, Pd and Xs
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        store16(&L[(wr + 16 * a) * LP + wc + 16 * b], db[a][b], li, lk);
-        if (has_slab) store16(&Xs[(wr + 16 * a) * LP + wc + 16 * b], sb[a][b], li, lk);
-      }
-#pragma unroll
-    for (int q = 0; q < NB / 4; ++q) Li[(w + 4 * q) * LP + lane] = 0.0;
-    // rows past d of the block must stay identity: they received nothing (Pd
-    // rows past nb are zero), and the factorisation masks the upper triangle
-    __syncthreads();
+    }
   }
   int first_bad = -1;  // first failing pivot of the block (wave 0)
   for (int b0 = 0; b0 < NB; b0 += LEAF) {
