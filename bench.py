@@ -3,9 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config opt2.7b-fc1]
 
 One step = the whole hot path on one layer with W and X already resident in
-HBM: H accumulated over the layer's calibration tokens in chunks of 16
-sequences (32768 tokens per call), the fp64 inverse-Hessian factor, then the
-column loop with lazy 128-column updates, trailing GEMMs and packing.
+HBM: H accumulated over all of the layer's calibration tokens in one call
+(--chunk-tokens splits it into calls of that many tokens, as a caller that
+streams its calibration batches would), the fp64 inverse-Hessian factor, then
+the column loop with lazy 128-column updates, trailing GEMMs and packing.
 Prints one JSON line (rank 0). The per-stage device times come from HIP events
 recorded on the stream the library launches on (torch's current stream).
 """
@@ -27,7 +28,7 @@ from post_weight_quantization_18_amd import synthetic as S
 PEAK_FP16_TFLOPS = 2516.6     # MI355X dense fp16/bf16 MFMA, fp32 accumulate
 PEAK_FP64_TFLOPS = 78.6       # MI355X fp64 (vector and matrix)
 PEAK_FP32_MFMA_TFLOPS = 157.3
-CHUNK_TOKENS = 32768          # 16 sequences of 2048 tokens per accumulate call
+CHUNK_TOKENS = 262144         # the whole calibration set (128 sequences of 2048) per accumulate call
 
 # HBM traffic of one SYRK launch (syrk_kernel) at the default workload, from two
 # rocprofv3 --pmc passes over this command (FETCH_SIZE, WRITE_SIZE, KiB per
@@ -36,6 +37,7 @@ CHUNK_TOKENS = 32768          # 16 sequences of 2048 tokens per accumulate call
 # figure is only reported while the kernel source is the one it was taken on.
 SYRK_TRAFFIC = {
     "config": "opt2.7b-fc1",
+    "chunk_tokens": 262144,
     "source_sha256_16": "8e9f6472d558ce0c",   # syrk.hip + common.h
     "fetch_bytes": 306194.703125 * 1024 * 2.0,
     "write_bytes": 56320.0 * 1024 * 1.0,
@@ -52,9 +54,9 @@ def _syrk_source_hash():
     return h.hexdigest()[:16]
 
 
-def syrk_traffic(cfg_name):
+def syrk_traffic(cfg_name, chunk):
     t = SYRK_TRAFFIC
-    if cfg_name != t["config"] or _syrk_source_hash() != t["source_sha256_16"]:
+    if cfg_name != t["config"] or chunk != t["chunk_tokens"] or _syrk_source_hash() != t["source_sha256_16"]:
         return None
     return t["fetch_bytes"] + t["write_bytes"]
 
@@ -66,6 +68,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--config", default="opt2.7b-fc1", choices=sorted(S.CONFIGS))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--chunk-tokens", type=int, default=CHUNK_TOKENS,
+                   help="tokens per gptq_accumulate_hessian call (the whole X stays resident either way)")
     p.add_argument("--cpu-sample-rows", type=int, default=None)
     p.add_argument("--cpu-sample-tokens", type=int, default=None)
     p.add_argument("--copy-calibration", action="store_true",
@@ -85,14 +89,16 @@ def copy_calibration():
 class LayerRun:
     """Preallocated buffers for one layer; step() enqueues the whole hot path."""
 
-    def __init__(self, cfg: S.LayerConfig, w: torch.Tensor, x: torch.Tensor):
+    def __init__(self, cfg: S.LayerConfig, w: torch.Tensor, x: torch.Tensor, chunk: int = CHUNK_TOKENS):
+        chunk = min(chunk, cfg.n_tokens)
         self.cfg = cfg
         self.w, self.x = w, x
         dev = w.device
         d, m = cfg.d, cfg.m
         self.H = torch.empty(d, d, dtype=torch.float64, device=dev)
         self.U = torch.empty(d, d, dtype=torch.float32, device=dev)
-        self.ws_h = torch.empty(max(1, G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, d, CHUNK_TOKENS)),
+        self.chunk = chunk
+        self.ws_h = torch.empty(max(1, G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, d, chunk)),
                                 dtype=torch.uint8, device=dev)
         self.ws_c = torch.empty(G.workspace_bytes(G.WS_PREPARE_HINV, 0, d), dtype=torch.uint8, device=dev)
         qcfg = G.make_qcfg(cfg.bits, cfg.group, cfg.grid)
@@ -110,16 +116,16 @@ class LayerRun:
         self.info = None
 
     def n_chunks(self):
-        return (self.cfg.n_tokens + CHUNK_TOKENS - 1) // CHUNK_TOKENS
+        return (self.cfg.n_tokens + self.chunk - 1) // self.chunk
 
     def step(self, timed_chunks=False):
         cfg = self.cfg
         self.ev[0].record()
         for i in range(self.n_chunks()):
-            t0 = i * CHUNK_TOKENS
+            t0 = i * self.chunk
             if timed_chunks:
                 self.ev_h[2 * i].record()
-            G.accumulate_hessian(self.H, self.x[t0:t0 + CHUNK_TOKENS], accumulate=i > 0, workspace=self.ws_h)
+            G.accumulate_hessian(self.H, self.x[t0:t0 + self.chunk], accumulate=i > 0, workspace=self.ws_h)
             if timed_chunks:
                 self.ev_h[2 * i + 1].record()
         self.ev[1].record()
@@ -215,7 +221,7 @@ def main():
     x = S.make_activations(cfg, dev)
     torch.cuda.synchronize()
     _say("inputs resident; allocating buffers")
-    run = LayerRun(cfg, w, x)
+    run = LayerRun(cfg, w, x, args.chunk_tokens)
     for i in range(args.warmup):
         run.step()
         torch.cuda.synchronize()
@@ -242,18 +248,18 @@ def main():
 
     d, m, n = cfg.d, cfg.m, cfg.n_tokens
     # algorithmic work
-    f_syrk_call = CHUNK_TOKENS * d * (d + 1)                     # lower triangle of 2 X^T X per call
+    f_syrk_call = run.chunk * d * (d + 1)                     # lower triangle of 2 X^T X per call
     f_syrk = n * d * (d + 1)
     f_chain = 2 * d ** 3 / 3                                     # Cholesky + triangular inverse
     syrk_call_ms = sum(syrk_calls) / len(syrk_calls)
     syrk_tflops = f_syrk_call / (syrk_call_ms * 1e-3) / 1e12
-    traffic = syrk_traffic(cfg.name)
+    traffic = syrk_traffic(cfg.name, run.chunk)
     roofline = {"bound": "mfma", "kernel": "gptq_accumulate_hessian (syrk_kernel + split-K fp64 combine)",
                 "achieved": round(syrk_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(syrk_tflops / PEAK_FP16_TFLOPS, 4),
                 "traffic": None if traffic is None else round(traffic),
                 "traffic_unit": "HBM bytes per syrk_kernel launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-                "per_launch": {"flops": f_syrk_call, "tokens": CHUNK_TOKENS, "avg_ms": round(syrk_call_ms, 4)}}
+                "per_launch": {"flops": f_syrk_call, "tokens": run.chunk, "avg_ms": round(syrk_call_ms, 4)}}
     result = {
         "metric": "GPTQ layer quantize throughput (weights quantized per second, whole hot path)",
         "value": cfg.n_weights / (ms_per_step * 1e-3),
@@ -269,7 +275,7 @@ def main():
         "data": "synthetic (seeded correlated-Gaussian X with outlier channels, N(0,0.02^2) W with outlier columns)",
         "config": {"workload": f"{cfg.name}: W {m}x{d} {cfg.w_dtype}, X {n}x{d} fp16, {cfg.bits}-bit {cfg.grid} "
                                f"{'per-row' if cfg.group == 0 else 'g' + str(cfg.group)}, block 128, damp {cfg.damp}",
-                   "chunk_tokens": CHUNK_TOKENS, "m": m, "d": d, "n_tokens": n},
+                   "chunk_tokens": run.chunk, "m": m, "d": d, "n_tokens": n},
         "stages_ms": {k: round(v, 4) for k, v in stage.items()},
         "mfma_frac": {"syrk_fp16": round(f_syrk / (stage["hessian"] * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
                       "chain_fp64": round(f_chain / (stage["hinv_chain"] * 1e-3) / 1e12 / PEAK_FP64_TFLOPS, 4)},

@@ -1,5 +1,5 @@
 """Full-size layers through the C ABI, in the launch configuration the
-benchmark times (token chunks of 32768 per gptq_accumulate_hessian call).
+benchmark times (one gptq_accumulate_hessian call over all 262144 tokens).
 
 * OPT-13B attention projection (5120 x 5120, 262144 tokens, 3-bit g128): the
   whole oracle runs, and the usual parity gates apply.
@@ -31,7 +31,7 @@ from parity_util import assert_gates, compare_layer, gpu_layer, say
 
 pytestmark = pytest.mark.gpu
 
-CHUNK = 32768
+CHUNK = 262144
 DEV = torch.device("cuda:0")
 
 
