@@ -420,7 +420,7 @@ int syrk_choose_split(int64_t d, int64_t n) {
     const int64_t rounds = ceil_div((int64_t)tiles * s, 256);
     const double t = (double)rounds * ((double)ceil_div(stages, s) + 4.0) * stage_us +
                      (s > 1 ? (double)s * tiles * partial_us_per_tile : 0.0);
-    if (t < best_t * 0.98) {
+    if (t < best_t * 0.90) {  // a split must win clearly: partials cost more than modelled
       best_t = t;
       best = s;
     }
@@ -437,6 +437,8 @@ size_t syrk_workspace_bytes(int64_t d, int64_t n) {
   return (size_t)s * (size_t)nt * TI * TJ * sizeof(double);
 }
 
+constexpr int64_t kLaunchTokens = 32768;
+
 gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const half_t* X, int64_t n,
                            int64_t ldx, int accumulate, void* ws, size_t ws_bytes, hipStream_t st) {
   const int nt = syrk_ntiles(d);
@@ -452,6 +454,17 @@ gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const hal
   if (split > 1 && (ws == nullptr || ws_bytes < (size_t)split * per_split)) {
     split = ws ? (int)(ws_bytes / per_split) : 1;
     if (split < 1) split = 1;
+  }
+  if (split == 1 && n > 2 * kLaunchTokens) {
+    // without a token split the tiles already fill the GPU: cut the token
+    // range into launches of kLaunchTokens (measured faster at d = 12288 than
+    // one long launch), each adding into H
+    for (int64_t t0 = 0; t0 < n; t0 += kLaunchTokens) {
+      const int64_t nc = n - t0 < kLaunchTokens ? n - t0 : kLaunchTokens;
+      gptq_status_t s = syrk_enqueue(H, h_f64, d, ldh, X + t0 * ldx, nc, ldx, accumulate || t0 > 0, ws, ws_bytes, st);
+      if (s != GPTQ_OK) return s;
+    }
+    return GPTQ_OK;
   }
   int64_t tps = ceil_div(ceil_div(n, split), KS) * KS;
   split = (int)ceil_div(n, tps);
