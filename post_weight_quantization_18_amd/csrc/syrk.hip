@@ -70,14 +70,31 @@ __device__ __forceinline__ void wait_vm_stages(int later) {
   }
 }
 
+// Work split of one launch over the tile slots (t = 0 .. ntiles-1) and the
+// launch's S stages of KS tokens:
+//  * slots [0, dp_tiles) (whole rounds of 256): one workgroup per tile over
+//    all S stages, written straight into H;
+//  * the remaining slots (stream-K): nsk workgroups take equal ranges of W
+//    consecutive (slot, stage) units in slot-major order. W < S, so a range
+//    covers the end of one tile and at most the start of the next: two
+//    segments, each written as an fp64 partial tile to part[(k * 2 + seg)],
+//    which syrk_sk_reduce_kernel sums per tile in workgroup order.
+// With fewer than 256 tiles the launch instead splits every tile's stages
+// into nsplit equal ranges (nsplit * ntiles workgroups, partial tile per
+// workgroup, summed by syrk_reduce_kernel): there the workgroups running
+// together then stream the same token range, which shares X in the L2, where
+// stream-K ranges would start at unrelated tokens.
 struct SyrkArgs {
   const half_t* X;
   int64_t ldx, n, d;
-  int64_t tokens_per_split;
-  int nsplit, ntiles;
-  void* out;        // H (direct) or fp64 partial tiles
+  int ntiles, dp_tiles;
+  int64_t S, W;     // stages per tile; stages per stream-K workgroup
+  int nsplit;       // > 0: token-split mode (dp_tiles = 0)
+  int64_t Ssp;      // stages per split
+  double* part;     // partial tiles: stream-K [k][2][TI][TJ], split [split][tile][TI][TJ]
+  void* H;
   int64_t ldh;
-  int h_f64, accumulate, direct;
+  int h_f64, accumulate;
 };
 
 // Tile t -> (bi, bj): the tiles of I-block bi are bj = 0 .. 2 bi + 1, so t lies
@@ -111,15 +128,56 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   // ring of NBUF stages; stage buffer b holds the I tile then the J tile
   __shared__ __attribute__((aligned(1024))) half_t ring[NBUF * KS * (TI + TJ)];
 
-  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int split = logical / a.ntiles;
-  const int t = logical - split * a.ntiles;
+  // this workgroup's segments: (slot, first stage, end stage, partial slot or -1 for H)
+  int seg_t[2], seg_p[2];
+  int64_t seg_s0[2], seg_s1[2];
+  int nseg = 0;
+  if ((int)blockIdx.x < a.dp_tiles) {
+    seg_t[0] = xcd_logical_block(blockIdx.x, a.dp_tiles);
+    seg_s0[0] = 0;
+    seg_s1[0] = a.S;
+    seg_p[0] = -1;
+    nseg = 1;
+  } else if (a.nsplit > 0) {
+    const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int split = logical / a.ntiles;
+    seg_t[0] = logical - split * a.ntiles;
+    seg_s0[0] = (int64_t)split * a.Ssp;
+    seg_s1[0] = seg_s0[0] + a.Ssp < a.S ? seg_s0[0] + a.Ssp : a.S;
+    seg_p[0] = logical;
+    nseg = 1;
+  } else {
+    // consecutive ranges (neighbouring tiles) on one XCD, as for whole tiles
+    // (dp_tiles is a multiple of 256, so the XCD of a block is its index mod 8)
+    const int k = xcd_logical_block((int)blockIdx.x - a.dp_tiles, (int)gridDim.x - a.dp_tiles);
+    const int64_t total = (int64_t)(a.ntiles - a.dp_tiles) * a.S;
+    const int64_t b0 = (int64_t)k * a.W;
+    const int64_t b1 = b0 + a.W < total ? b0 + a.W : total;
+    if (b0 >= total) return;  // uniform
+    const int64_t u = b0 / a.S;
+    seg_t[0] = a.dp_tiles + (int)u;
+    seg_s0[0] = b0 - u * a.S;
+    seg_s1[0] = b1 - u * a.S < a.S ? b1 - u * a.S : a.S;
+    seg_p[0] = 2 * k;
+    nseg = 1;
+    if (b1 > (u + 1) * a.S) {
+      seg_t[1] = a.dp_tiles + (int)u + 1;
+      seg_s0[1] = 0;
+      seg_s1[1] = b1 - (u + 1) * a.S;
+      seg_p[1] = 2 * k + 1;
+      nseg = 2;
+    }
+  }
+  for (int sg = 0; sg < nseg; ++sg) {
+  if (sg > 0) __syncthreads();  // every wave is done with the ring
+  const int t = seg_t[sg];
   int bi, bj;
-  if (!tile_coords(t, a.d, bi, bj)) return;  // empty slot: the workgroup exits (uniform)
+  if (!tile_coords(t, a.d, bi, bj)) continue;  // empty slot (uniform)
   const int64_t I0 = (int64_t)bi * TI, J0 = (int64_t)bj * TJ;
+  double* const part_out = seg_p[sg] < 0 ? nullptr : a.part + (int64_t)seg_p[sg] * TI * TJ;
 
-  const int64_t tok0 = (int64_t)split * a.tokens_per_split;
-  int64_t tok1 = tok0 + a.tokens_per_split;
+  const int64_t tok0 = seg_s0[sg] * KS;
+  int64_t tok1 = seg_s1[sg] * KS;
   if (tok1 > a.n) tok1 = a.n;
   const int nstages = tok1 > tok0 ? (int)((tok1 - tok0 + KS - 1) / KS) : 0;
 
@@ -320,10 +378,9 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) v[r] = 2.0 * ((double)outer[f][h][r] + (double)acc[f][h][r]);
       const int li0 = wi * 32 * FI + f * 32 + 4 * hl, lj = wj * 64 + h * 32 + col;
-      if (!a.direct) {
+      if (part_out) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ((double*)a.out)[((int64_t)logical * TI + li0 + 8 * (r >> 2) + (r & 3)) * TJ + lj] = v[r];
+        for (int r = 0; r < 16; ++r) part_out[(int64_t)(li0 + 8 * (r >> 2) + (r & 3)) * TJ + lj] = v[r];
         continue;
       }
       const int64_t j = J0 + lj;
@@ -333,8 +390,8 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int64_t i = I0 + li0 + 8 * (r >> 2) + (r & 3);
           const bool ok = i < a.d && j <= i;
-          old[r] = !ok ? 0.0 : a.h_f64 ? ((const double*)a.out)[i * a.ldh + j]
-                                        : (double)((const float*)a.out)[i * a.ldh + j];
+          old[r] = !ok ? 0.0 : a.h_f64 ? ((const double*)a.H)[i * a.ldh + j]
+                                        : (double)((const float*)a.H)[i * a.ldh + j];
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[r] += old[r];
@@ -344,15 +401,16 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
         const int64_t i = I0 + li0 + 8 * (r >> 2) + (r & 3);
         if (i < a.d && j <= i) {
           if (a.h_f64)
-            ((double*)a.out)[i * a.ldh + j] = v[r];
+            ((double*)a.H)[i * a.ldh + j] = v[r];
           else
-            ((float*)a.out)[i * a.ldh + j] = (float)v[r];
+            ((float*)a.H)[i * a.ldh + j] = (float)v[r];
         }
       }
     }
+  }  // segments
 }
 
-// Sums the split-K partial tiles in split order and adds them to H.
+// Token-split mode: H (+)= the sum of the tile's partials in split order.
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(const double* __restrict__ part, int nsplit,
                                                           int ntiles, void* Hout, int64_t d, int64_t ldh,
                                                           int h_f64, int accumulate) {
@@ -368,6 +426,40 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const double* __restri
     if (i >= d || j > i) continue;
     double s = 0.0;
     for (int sp = 0; sp < nsplit; ++sp) s += part[((int64_t)sp * ntiles + t) * per_tile + within];
+    if (h_f64) {
+      double* H = (double*)Hout + i * ldh + j;
+      *H = accumulate ? *H + s : s;
+    } else {
+      float* H = (float*)Hout + i * ldh + j;
+      *H = (float)(accumulate ? (double)*H + s : s);
+    }
+  }
+}
+
+// Stream-K tiles: H (+)= the sum, in workgroup order, of the partial tiles of
+// the workgroups whose ranges cover the tile (see SyrkArgs).
+__global__ __launch_bounds__(256) void syrk_sk_reduce_kernel(const double* __restrict__ part, int dp_tiles,
+                                                             int sk_tiles, int64_t S, int64_t W, int nsk,
+                                                             void* Hout, int64_t d, int64_t ldh, int h_f64,
+                                                             int accumulate) {
+  const int64_t per_tile = (int64_t)TI * TJ;
+  const int64_t total = (int64_t)sk_tiles * per_tile;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int u = (int)(idx / per_tile);
+    const int64_t within = idx - (int64_t)u * per_tile;
+    int bi, bj;
+    if (!tile_coords(dp_tiles + u, d, bi, bj)) continue;
+    const int64_t i = (int64_t)bi * TI + within / TJ, j = (int64_t)bj * TJ + within % TJ;
+    if (i >= d || j > i) continue;
+    const int64_t kf = ((int64_t)u * S) / W;
+    int64_t kl = ((int64_t)(u + 1) * S - 1) / W;
+    if (kl > nsk - 1) kl = nsk - 1;
+    double s = 0.0;
+    for (int64_t k = kf; k <= kl; ++k) {
+      const int seg = (k * W) / S == u ? 0 : 1;  // the tile is k's first or second segment
+      s += part[(k * 2 + seg) * per_tile + within];
+    }
     if (h_f64) {
       double* H = (double*)Hout + i * ldh + j;
       *H = accumulate ? *H + s : s;
@@ -396,6 +488,17 @@ int syrk_ntiles(int64_t d) {
   return (int)(T * (T + 1));
 }
 
+constexpr int64_t kLaunchTokens = 32768;
+constexpr int kSkMax = 256;            // stream-K workgroups: one round
+constexpr int64_t kSkMinStages = 16;   // at least 1024 tokens per stream-K range
+
+// Tokens per launch: with whole rounds of tiles to run (ntiles >= 256) a long
+// token range is cut into launches of kLaunchTokens (measured faster at
+// d = 12288 than one long launch); otherwise one launch takes them all.
+int64_t syrk_launch_tokens(int64_t d, int64_t n) {
+  return (syrk_ntiles(d) >= kSkMax && n > 2 * kLaunchTokens) ? kLaunchTokens : n;
+}
+
 // Real (non-empty) tiles of the lower triangle at width d.
 int syrk_real_tiles(int64_t d) {
   const int64_t ti = ceil_div(d, TI), tj = ceil_div(d, TJ);
@@ -404,10 +507,9 @@ int syrk_real_tiles(int64_t d) {
   return (int)n;
 }
 
-// Token split S: minimises an estimate of the call's time,
-//   ceil(tiles * S / 256) rounds x (stages per split + 4) stage times
-//   + the fp64 partial tiles written and read back (S > 1),
-// with one workgroup per CU (the LDS ring takes most of a CU's LDS).
+// Token split for fewer than 256 tiles: minimises an estimate of the call's
+// time, ceil(tiles * s / 256) rounds x (stages per split + 4) stage times +
+// the fp64 partial tiles written and read back; a split must win by 10%.
 int syrk_choose_split(int64_t d, int64_t n) {
   const int64_t stages = ceil_div(n, KS);
   const int tiles = syrk_real_tiles(d);
@@ -420,7 +522,7 @@ int syrk_choose_split(int64_t d, int64_t n) {
     const int64_t rounds = ceil_div((int64_t)tiles * s, 256);
     const double t = (double)rounds * ((double)ceil_div(stages, s) + 4.0) * stage_us +
                      (s > 1 ? (double)s * tiles * partial_us_per_tile : 0.0);
-    if (t < best_t * 0.90) {  // a split must win clearly: partials cost more than modelled
+    if (t < best_t * 0.90) {
       best_t = t;
       best = s;
     }
@@ -428,16 +530,60 @@ int syrk_choose_split(int64_t d, int64_t n) {
   return best;
 }
 
+struct SkPlan {
+  int dp_tiles, sk_tiles, nsk;
+  int64_t S, W;
+  int nsplit;  // > 0: token-split mode
+  int64_t Ssp;
+};
+
+SkPlan sk_plan(int64_t d, int64_t n_launch) {
+  SkPlan p;
+  const int nt = syrk_ntiles(d);
+  p.S = ceil_div(n_launch, KS);
+  p.nsplit = 0;
+  p.Ssp = 0;
+  if (nt < kSkMax) {
+    const int s = syrk_choose_split(d, n_launch);
+    p.dp_tiles = 0;
+    p.sk_tiles = 0;
+    p.nsk = 0;
+    p.W = 0;
+    if (s <= 1) {
+      p.dp_tiles = nt;  // one workgroup per tile, straight into H
+    } else {
+      p.Ssp = ceil_div(p.S, s);
+      p.nsplit = (int)ceil_div(p.S, p.Ssp);
+    }
+    return p;
+  }
+  p.dp_tiles = nt / kSkMax * kSkMax;
+  p.sk_tiles = nt - p.dp_tiles;
+  const int64_t units = (int64_t)p.sk_tiles * p.S;
+  if (units == 0) {
+    p.nsk = 0;
+    p.W = 0;
+    return p;
+  }
+  // W stages per workgroup: a share of one round, at least kSkMinStages, and
+  // at most S, so that a range touches two tiles at most
+  int64_t W = ceil_div(units, kSkMax);
+  const int64_t lo = kSkMinStages < p.S ? kSkMinStages : p.S;
+  if (W < lo) W = lo;
+  if (W > p.S) W = p.S;
+  p.W = W;
+  p.nsk = (int)ceil_div(units, W);  // <= 256: units <= 255 S
+  return p;
+}
+
 }  // namespace
 
 size_t syrk_workspace_bytes(int64_t d, int64_t n) {
-  const int nt = syrk_ntiles(d);
-  const int s = syrk_choose_split(d, n);
-  if (s <= 1) return 0;
-  return (size_t)s * (size_t)nt * TI * TJ * sizeof(double);
+  if (n <= 0) return 0;
+  const SkPlan p = sk_plan(d, syrk_launch_tokens(d, n));
+  if (p.nsplit > 0) return (size_t)p.nsplit * syrk_ntiles(d) * TI * TJ * sizeof(double);
+  return (size_t)p.nsk * 2 * TI * TJ * sizeof(double);
 }
-
-constexpr int64_t kLaunchTokens = 32768;
 
 gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const half_t* X, int64_t n,
                            int64_t ldx, int accumulate, void* ws, size_t ws_bytes, hipStream_t st) {
@@ -449,47 +595,57 @@ gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const hal
     }
     return GPTQ_OK;
   }
-  int split = syrk_choose_split(d, n);
-  const size_t per_split = (size_t)nt * TI * TJ * sizeof(double);
-  if (split > 1 && (ws == nullptr || ws_bytes < (size_t)split * per_split)) {
-    split = ws ? (int)(ws_bytes / per_split) : 1;
-    if (split < 1) split = 1;
-  }
-  if (split == 1 && n > 2 * kLaunchTokens) {
-    // without a token split the tiles already fill the GPU: cut the token
-    // range into launches of kLaunchTokens (measured faster at d = 12288 than
-    // one long launch), each adding into H
-    for (int64_t t0 = 0; t0 < n; t0 += kLaunchTokens) {
-      const int64_t nc = n - t0 < kLaunchTokens ? n - t0 : kLaunchTokens;
+  const int64_t nl = syrk_launch_tokens(d, n);
+  if (nl < n) {
+    for (int64_t t0 = 0; t0 < n; t0 += nl) {
+      const int64_t nc = n - t0 < nl ? n - t0 : nl;
       gptq_status_t s = syrk_enqueue(H, h_f64, d, ldh, X + t0 * ldx, nc, ldx, accumulate || t0 > 0, ws, ws_bytes, st);
       if (s != GPTQ_OK) return s;
     }
     return GPTQ_OK;
   }
-  int64_t tps = ceil_div(ceil_div(n, split), KS) * KS;
-  split = (int)ceil_div(n, tps);
-
+  SkPlan p = sk_plan(d, n);
+  const size_t need = p.nsplit > 0 ? (size_t)p.nsplit * nt * TI * TJ * sizeof(double)
+                                   : (size_t)p.nsk * 2 * TI * TJ * sizeof(double);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) {
+    // no room for the partial tiles: every tile gets one workgroup
+    p.dp_tiles = nt;
+    p.sk_tiles = 0;
+    p.nsk = 0;
+    p.nsplit = 0;
+  }
   SyrkArgs a;
   a.X = X;
   a.ldx = ldx;
   a.n = n;
   a.d = d;
-  a.tokens_per_split = tps;
-  a.nsplit = split;
   a.ntiles = nt;
+  a.dp_tiles = p.dp_tiles;
+  a.S = p.S;
+  a.W = p.W;
+  a.nsplit = p.nsplit;
+  a.Ssp = p.Ssp;
+  a.part = (double*)ws;
+  a.H = H;
   a.ldh = ldh;
   a.h_f64 = h_f64;
   a.accumulate = accumulate;
-  a.direct = split == 1;
-  a.out = split == 1 ? H : ws;
-  hipLaunchKernelGGL(syrk_kernel, dim3(nt * split), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL(syrk_kernel, dim3(p.nsplit > 0 ? p.nsplit * nt : p.dp_tiles + p.nsk), dim3(NT), 0, st, a);
   GPTQ_CHECK_LAUNCH();
-  if (split > 1) {
+  if (p.nsplit > 0) {
     const int64_t total = (int64_t)nt * TI * TJ;
     int blocks = (int)ceil_div(total, 256 * 4);
     if (blocks > 16384) blocks = 16384;
-    hipLaunchKernelGGL(syrk_reduce_kernel, dim3(blocks), dim3(256), 0, st, (const double*)ws, split, nt, H,
-                       d, ldh, h_f64, accumulate);
+    hipLaunchKernelGGL(syrk_reduce_kernel, dim3(blocks), dim3(256), 0, st, (const double*)ws, p.nsplit, nt, H, d,
+                       ldh, h_f64, accumulate);
+    GPTQ_CHECK_LAUNCH();
+  }
+  if (p.nsk > 0) {
+    const int64_t total = (int64_t)p.sk_tiles * TI * TJ;
+    int blocks = (int)ceil_div(total, 256 * 4);
+    if (blocks > 16384) blocks = 16384;
+    hipLaunchKernelGGL(syrk_sk_reduce_kernel, dim3(blocks), dim3(256), 0, st, (const double*)ws, p.dp_tiles,
+                       p.sk_tiles, p.S, p.W, p.nsk, H, d, ldh, h_f64, accumulate);
     GPTQ_CHECK_LAUNCH();
   }
   return GPTQ_OK;

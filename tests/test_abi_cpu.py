@@ -47,9 +47,15 @@ def test_status_strings_and_version(lib):
 
 def test_workspace_sizes(lib):
     d, n = 2560, 262144
-    syrk = G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, d, n)
-    assert syrk % (256 * 128 * 8) == 0          # whole fp64 partial tiles
-    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 49152, n) == 0   # enough tiles: no split
+    tile = 256 * 128 * 8                        # one fp64 partial tile
+    # 110 tiles < 256: the tokens split in two, one partial tile per tile and split
+    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, d, n) == 2 * 110 * tile
+    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 768, 4096) == 3 * 12 * tile
+    # 37056 tiles: 144 whole rounds, then 192 tiles over one stream-K round of
+    # 256 workgroups with two partial tiles each
+    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 49152, n) == 256 * 2 * tile
+    # 256 x 257 tiles: whole rounds only, no partials
+    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 65536, n) == 0
     chain = G.workspace_bytes(G.WS_PREPARE_HINV, 0, d)
     assert chain >= d * d * 8
     cfg = G.make_qcfg(4)
