@@ -768,8 +768,15 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
   for (int64_t s = NB; s < d; s *= 2) {
     const int64_t pairs = ceil_div(d, 2 * s);
     dim3 grid((unsigned)(s / 64), (unsigned)(s / 64), (unsigned)pairs);
-    // a grid that cannot fill the GPU splits each tile's K range over 2 wave groups
-    if ((int64_t)grid.x * grid.y * grid.z < 512) {
+    // a grid that cannot fill the GPU splits each tile's K range over 2 wave
+    // groups; counted are the tiles that have work (the last pair may be
+    // partial or past d)
+    int64_t active = 0;
+    for (int64_t pr = 0; pr < pairs; ++pr) {
+      const int64_t c0 = pr * 2 * s + s, c1 = pr * 2 * s + 2 * s < d ? pr * 2 * s + 2 * s : d;
+      if (c0 < d) active += (s / 64) * ceil_div(c1 - c0, 64);
+    }
+    if (active < 512) {
       hipLaunchKernelGGL((merge_kernel<0, 2>), grid, dim3(512), 0, st, w.A, d, w.T, ldt, s);
       GPTQ_CHECK_LAUNCH();
       hipLaunchKernelGGL((merge_kernel<1, 2>), grid, dim3(512), 0, st, w.A, d, w.T, ldt, s);

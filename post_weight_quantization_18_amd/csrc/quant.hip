@@ -137,11 +137,30 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* W, int w_f32, int
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= m) return;
   float vmin = INFINITY, vmax = -INFINITY;
-  for (int64_t j = lane; j < d; j += 64) {
-    float v = w_f32 ? ((const float*)W)[r * ldw + j] : (float)((const half_t*)W)[r * ldw + j];
-    Wk[r * d + j] = v;
-    vmin = fminf(vmin, v);
-    vmax = fmaxf(vmax, v);
+  const bool vec = !w_f32 && (ldw % 8) == 0 && (d % 8) == 0 && (((uintptr_t)W) & 15) == 0;
+  if (vec) {
+    // 8 weights per lane per pass: one 16-byte load, two 16-byte stores
+    const half_t* wr = (const half_t*)W + r * ldw;
+    float* kr = Wk + r * d;
+    for (int64_t j = 8 * lane; j < d; j += 8 * 64) {
+      const half8 h = *(const half8*)(wr + j);
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = (float)h[e];
+        vmin = fminf(vmin, v[e]);
+        vmax = fmaxf(vmax, v[e]);
+      }
+      *(float4*)(kr + j) = make_float4(v[0], v[1], v[2], v[3]);
+      *(float4*)(kr + j + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  } else {
+    for (int64_t j = lane; j < d; j += 64) {
+      float v = w_f32 ? ((const float*)W)[r * ldw + j] : (float)((const half_t*)W)[r * ldw + j];
+      Wk[r * d + j] = v;
+      vmin = fminf(vmin, v);
+      vmax = fmaxf(vmax, v);
+    }
   }
   if (!per_row) return;
   for (int off = 32; off > 0; off >>= 1) {
@@ -564,11 +583,21 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* codes, int64_t
     }
     out[r * nwords + wd] = word;
   }
-  if (W_hat) {
+  if (W_hat && (((uintptr_t)W_hat) & 15) != 0) {
     for (int64_t j = threadIdx.x; j < d; j += 256) {
       const int64_t g = group ? j / group : 0;
       const float s = scales[r * ngroups + g], z = (float)zeros[r * ngroups + g];
       W_hat[r * d + j] = s * ((float)crow[j] - z);
+    }
+  } else if (W_hat) {
+    // 4 weights per thread per pass (d and the groups are multiples of 32, so
+    // the four share a group and the accesses are aligned)
+    for (int64_t j = 4 * threadIdx.x; j < d; j += 4 * 256) {
+      const int64_t g = group ? j / group : 0;
+      const float s = scales[r * ngroups + g], z = (float)zeros[r * ngroups + g];
+      const uchar4 c = *(const uchar4*)(crow + j);
+      *(float4*)(W_hat + r * d + j) =
+          make_float4(s * ((float)c.x - z), s * ((float)c.y - z), s * ((float)c.z - z), s * ((float)c.w - z));
     }
   }
 }
