@@ -17,7 +17,10 @@ Sources (cited by page title and section):
   Generative Pre-trained Transformers" (nubint) -- "Proposed method" and
   "Key findings".
 * [ZLY] "GPTQ：用于生成式预训练 Transformer 的准确训练后量化" (zhiliyouxian
-  blog) -- "数学基础 / 问题公式化" (the objective) and "超参数选择" (defaults).
+  blog) -- "数学基础 / 问题公式化" (the objective), "超参数选择" and "实践指南"
+  (defaults, the desc_act option).
+* [CSDN] "GPTQ量化参数搜索工具：自动寻找最优配置" -- its parameter table, which
+  names --desc_act and --static_groups.
 
 Everything is numpy float64. fp16/fp32 inputs are upcast exactly. Library
 primitives (matmul, numpy.linalg.cholesky, numpy.linalg.inv) serve as single
@@ -220,7 +223,8 @@ def _check_group(d, group, block):
 
 def gptq_quantize(w, u, bits: int, grid: str = GRID_ASYM, group: int = 0,
                   block: int = 128, follow_codes=None, follow_zeros=None,
-                  band: float = 1e-3, blocked: bool = True) -> QuantResult:
+                  band: float = 1e-3, blocked: bool = True,
+                  col_grid=None) -> QuantResult:
     """Quantize W [m, d] column by column in natural order with the factor U.
 
     [FDE] figure "Quantize a column, correct the rest", steps 1-4, for column i:
@@ -244,6 +248,10 @@ def gptq_quantize(w, u, bits: int, grid: str = GRID_ASYM, group: int = 0,
     mismatch. In both cases the oracle then continues with the given code, so
     that one legitimate choice at a boundary does not cascade down the row.
     follow_zeros does the same for the per-group integer zero points.
+
+    col_grid (optional, (s [m, d], z [m, d])): a fixed grid for every column,
+    fitted beforehand (static groups); no grid is fitted in the loop, and
+    res.scales / res.zeros are left to the caller.
     """
     w = np.array(w, dtype=np.float64, copy=True)
     u = np.asarray(u, dtype=np.float64)
@@ -255,7 +263,13 @@ def gptq_quantize(w, u, bits: int, grid: str = GRID_ASYM, group: int = 0,
     res = QuantResult(m, d, ngroups)
     maxq = maxq_of(bits, grid)
 
-    if group == 0:
+    if col_grid is not None:
+        s_col = np.asarray(col_grid[0], dtype=np.float64)
+        z_col = np.asarray(col_grid[1]).astype(np.int64)
+        if s_col.shape != (m, d) or z_col.shape != (m, d):
+            raise ValueError("col_grid must be two [m, d] arrays")
+        group = 0
+    elif group == 0:
         s, z, _ = fit_grid(w, bits, grid)
         res.scales[:, 0] = s
         res.zeros[:, 0] = z
@@ -277,6 +291,8 @@ def gptq_quantize(w, u, bits: int, grid: str = GRID_ASYM, group: int = 0,
                     z = fz
                 res.scales[:, j // group] = s
                 res.zeros[:, j // group] = z
+            if col_grid is not None:
+                s, z = s_col[:, j], z_col[:, j]
             col = w[:, j]
             p = col / s + z
             c = np.clip(np.rint(p), 0, maxq).astype(np.int64)
@@ -350,6 +366,101 @@ def quantize_layer(w, x_chunks, bits: int, grid: str = GRID_ASYM, group: int = 0
     u = inverse_hessian_factor(hd)
     res = gptq_quantize(w, u, bits, grid, group, block, **kw)
     return res, h, u, lam
+
+
+# ---------------------------------------------------------------------------
+# Act-order (desc_act) and static groups. The pages name both options and
+# nothing more: [ZLY] "实践指南" passes desc_act (sort the columns by their
+# activations, off by default) and "超参数选择" lists its default; [CSDN] lists
+# --desc_act and --static_groups among the tool's parameters. Readings:
+#  * the size of column j's activations is H_jj = 2 sum_t x_tj^2, and the
+#    columns are quantized in descending H_jj, ties in index order;
+#  * without static groups, groups are runs of g consecutive columns in that
+#    order, each fitted at its first column on the current (updated) weights;
+#  * with static groups, the grid of every natural group of g columns is
+#    fitted before the loop on the original weights, and each column keeps its
+#    natural group's grid wherever the order puts it.
+# ---------------------------------------------------------------------------
+def act_order_perm(h) -> np.ndarray:
+    """perm[j] = the natural column quantized j-th: descending diag(H), ties in
+    index order."""
+    dg = np.diag(np.asarray(h, dtype=np.float64))
+    return np.argsort(-dg, kind="stable")
+
+
+def static_group_grids(w, bits: int, grid: str, group: int):
+    """Grid of every natural group of `group` columns, fitted on the original
+    weights: (s [m, d/group], z [m, d/group])."""
+    w = np.asarray(w, dtype=np.float64)
+    m, d = w.shape
+    ng = d // group
+    s = np.zeros((m, ng))
+    z = np.zeros((m, ng), dtype=np.int64)
+    for k in range(ng):
+        s[:, k], z[:, k], _ = fit_grid(w[:, k * group:(k + 1) * group], bits, grid)
+    return s, z
+
+
+def gptq_quantize_ordered(w, u_perm, perm, bits: int, grid: str = GRID_ASYM, group: int = 0,
+                          static_groups: bool = False, block: int = 128, follow_codes=None,
+                          follow_zeros=None, band: float = 1e-3, blocked: bool = True):
+    """The column loop in the order perm, with U the factor of the permuted
+    damped Hessian (H_d[perm][:, perm]). Inputs and outputs are in natural
+    column order.
+
+    Returns (res, g_idx): res.codes / w_hat / err / p / dist at natural
+    columns; res.scales / res.zeros [m, ngroups] by group number; g_idx [d] the
+    group number of every natural column (0 for one grid per row).
+    follow_codes / follow_zeros are in natural order like the outputs."""
+    w = np.asarray(w, dtype=np.float64)
+    perm = np.asarray(perm, dtype=np.int64)
+    m, d = w.shape
+    if sorted(perm.tolist()) != list(range(d)):
+        raise ValueError("perm is not a permutation of the columns")
+    _check_group(d, group, block)
+    wp = w[:, perm]
+    fc = None if follow_codes is None else np.asarray(follow_codes)[:, perm]
+    if group and static_groups:
+        s_g, z_g = static_group_grids(w, bits, grid, group)
+        gcol = perm // group  # natural group of the j-th quantized column
+        res_p = gptq_quantize(wp, u_perm, bits, grid, 0, block, follow_codes=fc, band=band,
+                              blocked=blocked, col_grid=(s_g[:, gcol], z_g[:, gcol]))
+        res = QuantResult(m, d, d // group)
+        res.scales[:] = s_g
+        res.zeros[:] = z_g
+        g_idx = np.arange(d) // group
+    else:
+        res_p = gptq_quantize(wp, u_perm, bits, grid, group, block, follow_codes=fc,
+                              follow_zeros=follow_zeros, band=band, blocked=blocked)
+        res = QuantResult(m, d, res_p.scales.shape[1])
+        res.scales[:] = res_p.scales
+        res.zeros[:] = res_p.zeros
+        res.zero_band_mismatch = res_p.zero_band_mismatch
+        res.zero_hard_mismatch = res_p.zero_hard_mismatch
+        g_idx = np.zeros(d, dtype=np.int64)
+        if group:
+            g_idx[perm] = np.arange(d) // group
+    for name in ("codes", "w_hat", "err", "p", "dist"):
+        getattr(res, name)[:, perm] = getattr(res_p, name)
+    res.band_mismatch = res_p.band_mismatch
+    res.hard_mismatch = res_p.hard_mismatch
+    res.hard_positions = [(r, int(perm[j])) for r, j in res_p.hard_positions]
+    return res, g_idx
+
+
+def quantize_layer_act_order(w, x_chunks, bits: int, grid: str = GRID_ASYM, group: int = 0,
+                             static_groups: bool = False, block: int = 128,
+                             percdamp: float = 0.01, **kw):
+    """The hot path with act-order: H, the order, the permuted damped H, its
+    factor, the column loop in that order.
+
+    Returns (result, g_idx, perm, H, U_perm, lambda); H is in natural order."""
+    h = hessian(x_chunks)
+    perm = act_order_perm(h)
+    hd, lam = damp(h[np.ix_(perm, perm)], percdamp)
+    u = inverse_hessian_factor(hd)
+    res, g_idx = gptq_quantize_ordered(w, u, perm, bits, grid, group, static_groups, block, **kw)
+    return res, g_idx, perm, h, u, lam
 
 
 # ---------------------------------------------------------------------------
