@@ -422,12 +422,30 @@ def gptq_quantize_ordered(w, u_perm, perm, bits: int, grid: str = GRID_ASYM, gro
     fc = None if follow_codes is None else np.asarray(follow_codes)[:, perm]
     if group and static_groups:
         s_g, z_g = static_group_grids(w, bits, grid, group)
+        zb = zh = 0
+        if follow_zeros is not None and grid == GRID_ASYM:
+            # the zero points of another implementation, judged as in the loop:
+            # an adjacent zero is taken when -lo/s lies within `band` of the
+            # half-integer between the two (an exact tie such as a group whose
+            # extremes are +-a, where -lo/s = maxq/2, falls either way in
+            # finite precision); anything else is a hard mismatch
+            fz = np.asarray(follow_zeros).astype(np.int64)
+            for k in range(d // group):
+                lo = np.minimum(np.min(w[:, k * group:(k + 1) * group], axis=1), 0.0)
+                zr = -lo / s_g[:, k]
+                diff = fz[:, k] != z_g[:, k]
+                near = np.abs(zr - (np.minimum(fz[:, k], z_g[:, k]) + 0.5)) < band
+                adj = np.abs(fz[:, k] - z_g[:, k]) == 1
+                zb += int(np.sum(diff & near & adj))
+                zh += int(np.sum(diff & ~(near & adj)))
+                z_g[:, k] = np.where(diff, fz[:, k], z_g[:, k])
         gcol = perm // group  # natural group of the j-th quantized column
         res_p = gptq_quantize(wp, u_perm, bits, grid, 0, block, follow_codes=fc, band=band,
                               blocked=blocked, col_grid=(s_g[:, gcol], z_g[:, gcol]))
         res = QuantResult(m, d, d // group)
         res.scales[:] = s_g
         res.zeros[:] = z_g
+        res.zero_band_mismatch, res.zero_hard_mismatch = zb, zh
         g_idx = np.arange(d) // group
     else:
         res_p = gptq_quantize(wp, u_perm, bits, grid, group, block, follow_codes=fc,

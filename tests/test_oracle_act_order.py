@@ -170,3 +170,26 @@ def test_follow_mode_maps_positions_to_natural_columns():
     res2, _, _, _, _, _ = O.quantize_layer_act_order(w, x, 4, "asym", 0, block=4, follow_codes=planted)
     assert res2.hard_mismatch >= 1
     assert (int(far), col) in res2.hard_positions
+
+
+def test_static_zero_follow_mode_at_an_exact_tie():
+    """A group whose extremes are -a and +a has -lo/s = maxq/2 exactly, a
+    half-integer: either neighbour is a legitimate zero point in finite
+    precision. Follow mode takes the other neighbour as a band mismatch; a
+    zero two steps away is a hard mismatch."""
+    m, d, g = 2, 8, 4
+    w = np.array([[-0.5, 0.25, 0.5, 0.125, 0.3, -0.2, 0.1, 0.05],
+                  [0.1, 0.2, 0.3, 0.4, -0.1, -0.2, -0.3, 0.05]])
+    s_g, z_g = O.static_group_grids(w, 4, "asym", g)
+    assert -(-0.5) / s_g[0, 0] == pytest.approx(7.5, abs=1e-12)
+    u = np.eye(d)
+    perm = np.arange(d)[::-1].copy()
+    other = z_g.copy()
+    other[0, 0] = 15 - z_g[0, 0]  # the other side of 7.5
+    res, _ = O.gptq_quantize_ordered(w, u, perm, 4, "asym", g, True, follow_zeros=other)
+    assert (res.zero_band_mismatch, res.zero_hard_mismatch) == (1, 0)
+    assert res.zeros[0, 0] == other[0, 0]
+    far = z_g.copy()
+    far[1, 1] += 2
+    res2, _ = O.gptq_quantize_ordered(w, u, perm, 4, "asym", g, True, follow_zeros=far)
+    assert res2.zero_hard_mismatch == 1
