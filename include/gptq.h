@@ -147,6 +147,55 @@ gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int
                                   uint32_t* qcodes, float* scales, uint8_t* zeros, float* W_hat,
                                   float* err_sq, void* workspace, size_t ws_bytes, void* stream);
 
+/* Act-order (desc_act): the order in which to quantize the columns, largest
+ * activations first. The zhiliyouxian blog ("实践指南", "超参数选择") passes
+ * desc_act, which sorts the columns by their activations (off by default);
+ * the CSDN page "GPTQ量化参数搜索工具" lists --desc_act and --static_groups. The
+ * pages say no more; this library reads the size of column j's activations as
+ * H_jj = 2 sum_t x_tj^2.
+ *  H        device [d][ldh] (only the diagonal is read), h_dtype GPTQ_F32 | GPTQ_F64.
+ *  perm     device int32 [d], out: perm[j] = the column with the j-th largest
+ *           H_jj, equal values in index order (+0 = -0; a NaN sorts first).
+ *  d        1 <= d <= INT32_MAX. */
+gptq_status_t gptq_act_order(const void* H, int32_t h_dtype, int64_t d, int64_t ldh, int32_t* perm, void* stream);
+
+/* The Hessian in the order perm: Hp[i][j] = H[perm[i]][perm[j]] for j <= i
+ * (lower triangles; H's lower triangle is read). Pass Hp to gptq_prepare_hinv
+ * to get the factor that gptq_quantize_layer_ordered takes.
+ *  H, Hp    device [d][ldh] / [d][ldhp], both h_dtype (GPTQ_F32 | GPTQ_F64);
+ *           Hp may not alias H.
+ *  perm     device int32 [d], a permutation of 0 .. d-1 (entries outside
+ *           [0, d) are read as 0: the result is then meaningless, but every
+ *           access stays inside H). */
+gptq_status_t gptq_permute_hessian(const void* H, int32_t h_dtype, int64_t d, int64_t ldh, const int32_t* perm,
+                                   void* Hp, int64_t ldhp, void* stream);
+
+/* gptq_quantize_layer with the columns quantized in the order perm instead of
+ * the natural one (act-order). W and every output stay in natural column
+ * order; U must be the factor of the Hessian in that order
+ * (gptq_permute_hessian, then gptq_prepare_hinv). Same sources as
+ * gptq_act_order; the group readings are this library's:
+ *  static_groups 0: groups are runs of group_size columns in the order perm,
+ *           each fitted at its first column on the current (error-updated)
+ *           weights, as in natural order; group k of the outputs is the k-th
+ *           such run.
+ *  static_groups 1: the grid of every natural group of group_size columns is
+ *           fitted on the original W before the loop; each column is rounded on
+ *           its natural group's grid wherever the order puts it; group k is
+ *           natural columns [k * group_size, (k + 1) * group_size).
+ *  With group_size 0 (one grid per row) both give the same result.
+ *  perm     device int32 [d], a permutation of 0 .. d-1 (entries outside
+ *           [0, d) are read as 0: the result is then meaningless, but every
+ *           access stays inside the buffers).
+ *  g_idx    device int32 [d], may be NULL: the group number of every natural
+ *           column (0 for one grid per row).
+ *  Other arguments, sizes and the workspace as gptq_quantize_layer; d <= INT32_MAX. */
+gptq_status_t gptq_quantize_layer_ordered(const void* W, int32_t w_dtype, int64_t m, int64_t d, int64_t ldw,
+                                          const void* U, int32_t u_dtype, int64_t ldu, const gptq_qcfg_t* cfg,
+                                          const int32_t* perm, int32_t static_groups, uint32_t* qcodes,
+                                          float* scales, uint8_t* zeros, int32_t* g_idx, float* W_hat,
+                                          float* err_sq, void* workspace, size_t ws_bytes, void* stream);
+
 /* Bit packing of integer codes (one byte per code) into the row-wise LSB-first
  * bitstream gptq_quantize_layer writes (which packs in its own epilogue).
  * FDE breakdown, section 01: the output is 3-bit (or 4-bit) weights that an

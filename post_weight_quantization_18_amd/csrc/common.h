@@ -67,11 +67,20 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
                             size_t ws_bytes, hipStream_t st);
 size_t chain_workspace_bytes(int64_t d);
 
+// perm (optional): the quantization order, W and the outputs staying in natural
+// column order; static_groups and g_idx as in gptq_quantize_layer_ordered.
 gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int64_t ldw, const void* U,
                             int u_f64, int64_t ldu, const gptq_qcfg_t& cfg, uint32_t* qcodes,
                             float* scales, uint8_t* zeros, float* W_hat, float* err_sq, void* ws,
-                            size_t ws_bytes, hipStream_t st);
+                            size_t ws_bytes, hipStream_t st, const int32_t* perm = nullptr,
+                            int static_groups = 0, int32_t* g_idx = nullptr);
 size_t quant_workspace_bytes(int64_t m, int64_t d, const gptq_qcfg_t& cfg);
+
+// Act-order: perm[j] = the column with the j-th largest H_jj (ties in index
+// order); Hp = H gathered into that order (lower triangles).
+gptq_status_t act_order_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, int32_t* perm, hipStream_t st);
+gptq_status_t permute_hessian_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, const int32_t* perm,
+                                      void* Hp, int64_t ldp, hipStream_t st);
 
 // C[i][j] -= rowscale[i] * cscale * sum_k A[i][k] B[k][j] for i < M, j < N, with
 // A = Ah + Al and B = Bh + Bl given as fp16 pairs and the product taken as

@@ -108,6 +108,38 @@ gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int
                        W_hat, err_sq, workspace, ws_bytes, (hipStream_t)stream);
 }
 
+gptq_status_t gptq_act_order(const void* H, int32_t h_dtype, int64_t d, int64_t ldh, int32_t* perm, void* stream) {
+  if (!H || !perm || d <= 0 || ldh < d) return GPTQ_ERR_INVALID_ARG;
+  if (d > INT32_MAX) return GPTQ_ERR_INVALID_ARG;
+  if (h_dtype != GPTQ_F32 && h_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
+  return act_order_enqueue(H, h_dtype == GPTQ_F64, d, ldh, perm, (hipStream_t)stream);
+}
+
+gptq_status_t gptq_permute_hessian(const void* H, int32_t h_dtype, int64_t d, int64_t ldh, const int32_t* perm,
+                                   void* Hp, int64_t ldhp, void* stream) {
+  if (!H || !perm || !Hp || d <= 0 || ldh < d || ldhp < d) return GPTQ_ERR_INVALID_ARG;
+  if (h_dtype != GPTQ_F32 && h_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
+  if (H == Hp) return GPTQ_ERR_INVALID_ARG;
+  return permute_hessian_enqueue(H, h_dtype == GPTQ_F64, d, ldh, perm, Hp, ldhp, (hipStream_t)stream);
+}
+
+gptq_status_t gptq_quantize_layer_ordered(const void* W, int32_t w_dtype, int64_t m, int64_t d, int64_t ldw,
+                                          const void* U, int32_t u_dtype, int64_t ldu, const gptq_qcfg_t* cfg,
+                                          const int32_t* perm, int32_t static_groups, uint32_t* qcodes,
+                                          float* scales, uint8_t* zeros, int32_t* g_idx, float* W_hat,
+                                          float* err_sq, void* workspace, size_t ws_bytes, void* stream) {
+  if (!W || !U || !cfg || !perm || !qcodes || !scales || !zeros) return GPTQ_ERR_INVALID_ARG;
+  if (static_groups != 0 && static_groups != 1) return GPTQ_ERR_INVALID_ARG;
+  if (m <= 0 || d <= 0 || d % 32 || d > INT32_MAX || ldw < d || ldu < d) return GPTQ_ERR_INVALID_ARG;
+  if (w_dtype != GPTQ_F16 && w_dtype != GPTQ_F32) return GPTQ_ERR_INVALID_ARG;
+  if (u_dtype != GPTQ_F32 && u_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
+  if (u_dtype == GPTQ_F32 && (ldu % 4 || !aligned(U, 16))) return GPTQ_ERR_INVALID_ARG;
+  if (!valid_qcfg(*cfg, d)) return GPTQ_ERR_UNSUPPORTED;
+  if (!workspace || !aligned(workspace, 256)) return GPTQ_ERR_WORKSPACE;
+  return quant_enqueue(W, w_dtype == GPTQ_F32, m, d, ldw, U, u_dtype == GPTQ_F64, ldu, *cfg, qcodes, scales, zeros,
+                       W_hat, err_sq, workspace, ws_bytes, (hipStream_t)stream, perm, static_groups, g_idx);
+}
+
 gptq_status_t gptq_pack_codes(const uint8_t* codes, int64_t m, int64_t d, int32_t bits, uint32_t* out,
                               void* stream) {
   if (!codes || !out || m <= 0 || d <= 0) return GPTQ_ERR_INVALID_ARG;

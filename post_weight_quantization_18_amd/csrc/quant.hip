@@ -48,6 +48,7 @@ struct QuantWs {
   half_t* Uth;      // nblocks x d x BLK: U[blk, c] transposed, K-tiled by 32, scaled, fp16 high
   half_t* Utl;      //                                                         fp16 low
   float* U32;       // d x d (only when U is fp64)
+  int32_t* inv;     // d: position of every natural column in the quantization order
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -92,6 +93,7 @@ QuantWs quant_ws(void* ws, int64_t m, int64_t d, int group, int u_f64) {
   w.Uth = (half_t*)take((size_t)nb * d * BLK * sizeof(half_t));
   w.Utl = (half_t*)take((size_t)nb * d * BLK * sizeof(half_t));
   w.U32 = u_f64 ? (float*)take((size_t)d * d * sizeof(float)) : nullptr;
+  w.inv = (int32_t*)take((size_t)d * sizeof(int32_t));
   return w;
 }
 
@@ -101,6 +103,7 @@ size_t quant_ws_total(int64_t m, int64_t d, int group, int u_f64) {
              2 * align256((size_t)m * S * 2) + 2 * align256((size_t)m * 4) + align256((size_t)m * d) +
              align256((size_t)d * 4) + 2 * align256(4) + 2 * align256((size_t)nb * d * BLK * 2);
   if (u_f64) b += align256((size_t)d * d * 4);
+  b += align256((size_t)d * 4);
   return b;
 }
 
@@ -130,14 +133,16 @@ __device__ inline GridFit fit_grid(float vmin, float vmax, int ternary, float ma
 
 // W (fp16 | fp32) -> fp32 working copy; for one grid per row, fit it on the
 // original row. One wave per row.
+// With perm set, column j of the copy is column perm[j] of W (entries outside
+// [0, d) read column 0).
 __global__ __launch_bounds__(256) void prep_kernel(const void* W, int w_f32, int64_t m, int64_t d, int64_t ldw,
-                                                   float* Wk, int per_row, int ternary, float maxq, float* scales,
-                                                   uint8_t* zeros) {
+                                                   const int32_t* perm, float* Wk, int per_row, int ternary,
+                                                   float maxq, float* scales, uint8_t* zeros) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= m) return;
   float vmin = INFINITY, vmax = -INFINITY;
-  const bool vec = !w_f32 && (ldw % 8) == 0 && (d % 8) == 0 && (((uintptr_t)W) & 15) == 0;
+  const bool vec = !perm && !w_f32 && (ldw % 8) == 0 && (d % 8) == 0 && (((uintptr_t)W) & 15) == 0;
   if (vec) {
     // 8 weights per lane per pass: one 16-byte load, two 16-byte stores
     const half_t* wr = (const half_t*)W + r * ldw;
@@ -156,7 +161,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* W, int w_f32, int
     }
   } else {
     for (int64_t j = lane; j < d; j += 64) {
-      float v = w_f32 ? ((const float*)W)[r * ldw + j] : (float)((const half_t*)W)[r * ldw + j];
+      int64_t c = j;
+      if (perm) {
+        c = perm[j];
+        if (c < 0 || c >= d) c = 0;
+      }
+      float v = w_f32 ? ((const float*)W)[r * ldw + c] : (float)((const half_t*)W)[r * ldw + c];
       Wk[r * d + j] = v;
       vmin = fminf(vmin, v);
       vmax = fmaxf(vmax, v);
@@ -171,6 +181,47 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* W, int w_f32, int
     GridFit g = fit_grid(vmin, vmax, ternary, maxq);
     scales[r] = g.s;
     zeros[r] = (uint8_t)g.z;
+  }
+}
+
+// Static groups: the grid of every natural group of `group` columns, fitted on
+// the original weights before the column loop. One wave per row.
+__global__ __launch_bounds__(256) void static_fit_kernel(const void* W, int w_f32, int64_t m, int64_t d, int64_t ldw,
+                                                         int group, int ternary, float maxq, float* scales,
+                                                         uint8_t* zeros) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= m) return;
+  const int64_t ng = d / group;
+  for (int64_t k = 0; k < ng; ++k) {
+    float vmin = INFINITY, vmax = -INFINITY;
+    for (int64_t t = lane; t < group; t += 64) {
+      const int64_t c = k * group + t;
+      const float v = w_f32 ? ((const float*)W)[r * ldw + c] : (float)((const half_t*)W)[r * ldw + c];
+      vmin = fminf(vmin, v);
+      vmax = fmaxf(vmax, v);
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      vmin = fminf(vmin, __shfl_xor(vmin, off));
+      vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+    }
+    if (lane == 0) {
+      GridFit g = fit_grid(vmin, vmax, ternary, maxq);
+      scales[r * ng + k] = g.s;
+      zeros[r * ng + k] = (uint8_t)g.z;
+    }
+  }
+}
+
+// inv[perm[j]] = j, and the group number of every natural column: j / group
+// in the order, c / group with static groups, 0 for one grid per row.
+__global__ __launch_bounds__(256) void order_index_kernel(const int32_t* perm, int64_t d, int group, int static_groups,
+                                                          int32_t* inv, int32_t* g_idx) {
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < d; j += (int64_t)gridDim.x * 256) {
+    int64_t c = perm[j];
+    if (c < 0 || c >= d) c = 0;
+    inv[c] = (int32_t)j;
+    if (g_idx) g_idx[c] = group == 0 ? 0 : (int32_t)((static_groups ? c : j) / group);
   }
 }
 
@@ -204,6 +255,7 @@ struct ColArgs {
   float* scales;
   uint8_t* zeros;
   float* err_sq;
+  const int32_t* perm;  // quantization order (static groups: grids by natural group)
   int first;
 };
 
@@ -223,6 +275,7 @@ struct LaneState {
   float w[CPL];         // the lane's 32 working weights, then its 32 errors
   uint32_t cw[CPL / 4]; // its 32 codes, one byte each
   float s, rs, zf, esum;
+  float cs[CPL], crs[CPL], cz[CPL];  // static groups: the grid of each of its 32 columns
 };
 
 template <int O>
@@ -298,6 +351,11 @@ __device__ __forceinline__ void col_step(LaneState& st, const ColArgs& a, int64_
       st.rs = 1.0f / gf.s;
     }
   }
+  if constexpr (G == -2) {
+    st.s = st.cs[LI];
+    st.rs = st.crs[LI];
+    st.zf = st.cz[LI];
+  }
   const bool owner = (g == O);
   const float wv = st.w[LI];
   const float p = wv * st.rs + st.zf;
@@ -337,7 +395,9 @@ struct Steps {
 
 // G = 0: one grid per row (already fitted); G = 32, 64, 128: refit at every
 // group start inside the block; G = -1: groups span whole blocks, refit at the
-// group's first block from the current working weights.
+// group's first block from the current working weights; G = -2: static groups,
+// every column takes the grid of its natural group perm[j] / group (fitted
+// before the loop).
 template <int G>
 __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
   __shared__ __attribute__((aligned(16))) float Us[BLK][UPITCH];
@@ -385,7 +445,7 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
     st.s = a.scales[rr];
     st.zf = (float)a.zeros[rr];
     st.rs = 1.0f / st.s;
-  } else if (G < 0) {
+  } else if (G == -1) {
     const int gi = (int)(a.j0 / a.group);
     if (a.j0 % a.group == 0) {
       // the group spans whole blocks: each lane scans a quarter of it
@@ -413,6 +473,17 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
       st.zf = (float)a.zeros[rr * a.ngroups + gi];
     }
     st.rs = 1.0f / st.s;
+  } else if (G == -2) {
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int64_t j = a.j0 + g * CPL + k;
+      int64_t c = j < a.d ? a.perm[j] : 0;
+      if (c < 0 || c >= a.d) c = 0;
+      const int64_t gi = c / a.group;
+      st.cs[k] = a.scales[rr * a.ngroups + gi];
+      st.crs[k] = 1.0f / st.cs[k];
+      st.cz[k] = (float)a.zeros[rr * a.ngroups + gi];
+    }
   }
 
   if (live) {
@@ -563,10 +634,14 @@ __global__ __launch_bounds__(256) void usplit_kernel(const float* U, int64_t ldu
 }
 
 // Packs one row per workgroup into the LSB-first bitstream and, when W_hat is
-// given, writes W_hat = s * (code - z).
+// given, writes W_hat = s * (code - z). With inv set the codes are in the
+// quantization order and natural column c is read from position inv[c]
+// (entries outside [0, d) read position 0); its group is c / group with static
+// groups, else inv[c] / group.
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* codes, int64_t ldc, int64_t m, int64_t d,
                                                    int bits, uint32_t* out, float* W_hat, const float* scales,
-                                                   const uint8_t* zeros, int group, int ngroups) {
+                                                   const uint8_t* zeros, int group, int ngroups,
+                                                   const int32_t* inv, int static_groups) {
   const int64_t r = blockIdx.x;
   if (r >= m) return;
   const uint8_t* crow = codes + r * ldc;
@@ -578,16 +653,26 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* codes, int64_t
     uint32_t word = 0;
     for (; j <= jend; ++j) {
       const int64_t shift = j * bits - b0;
-      const uint32_t c = crow[j];
+      int64_t jp = j;
+      if (inv) {
+        jp = inv[j];
+        if (jp < 0 || jp >= d) jp = 0;
+      }
+      const uint32_t c = crow[jp];
       word |= shift >= 0 ? (c << shift) : (c >> (-shift));
     }
     out[r * nwords + wd] = word;
   }
-  if (W_hat && (((uintptr_t)W_hat) & 15) != 0) {
+  if (W_hat && (inv || (((uintptr_t)W_hat) & 15) != 0)) {
     for (int64_t j = threadIdx.x; j < d; j += 256) {
-      const int64_t g = group ? j / group : 0;
+      int64_t jp = j;
+      if (inv) {
+        jp = inv[j];
+        if (jp < 0 || jp >= d) jp = 0;
+      }
+      const int64_t g = group ? (static_groups ? j : jp) / group : 0;
       const float s = scales[r * ngroups + g], z = (float)zeros[r * ngroups + g];
-      W_hat[r * d + j] = s * ((float)crow[j] - z);
+      W_hat[r * d + j] = s * ((float)crow[jp] - z);
     }
   } else if (W_hat) {
     // 4 weights per thread per pass (d and the groups are multiples of 32, so
@@ -617,7 +702,8 @@ size_t quant_workspace_bytes(int64_t m, int64_t d, const gptq_qcfg_t& cfg) {
 
 gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int64_t ldw, const void* U, int u_f64,
                             int64_t ldu, const gptq_qcfg_t& cfg, uint32_t* qcodes, float* scales, uint8_t* zeros,
-                            float* W_hat, float* err_sq, void* ws, size_t ws_bytes, hipStream_t st) {
+                            float* W_hat, float* err_sq, void* ws, size_t ws_bytes, hipStream_t st,
+                            const int32_t* perm, int static_groups, int32_t* g_idx) {
   const size_t need = quant_ws_total(m, d, cfg.group_size, u_f64);
   if (ws == nullptr || ws_bytes < need) return GPTQ_ERR_WORKSPACE;
   QuantWs w = quant_ws(ws, m, d, cfg.group_size, u_f64);
@@ -625,6 +711,17 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   const float maxq = ternary ? 2.0f : (float)((1 << cfg.bits) - 1);
   const int group = cfg.group_size;
   const int ngroups = group ? (int)(d / group) : 1;
+  const bool stat = perm && static_groups && group > 0;
+  if (perm) {
+    hipLaunchKernelGGL(order_index_kernel, dim3((unsigned)(ceil_div(d, 256) < 1024 ? ceil_div(d, 256) : 1024)),
+                       dim3(256), 0, st, perm, d, group, stat ? 1 : 0, w.inv, g_idx);
+    GPTQ_CHECK_LAUNCH();
+  }
+  if (stat) {
+    hipLaunchKernelGGL(static_fit_kernel, dim3((unsigned)ceil_div(m, 4)), dim3(256), 0, st, W, w_f32, m, d, ldw,
+                       group, ternary, maxq, scales, zeros);
+    GPTQ_CHECK_LAUNCH();
+  }
 
   const float* U32 = (const float*)U;
   int64_t ldu32 = ldu;
@@ -648,7 +745,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
                        ldu32, d, (const uint32_t*)w.umax, w.Uth, w.Utl, w.uinv);
     GPTQ_CHECK_LAUNCH();
   }
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)ceil_div(m, 4)), dim3(256), 0, st, W, w_f32, m, d, ldw, w.Wk,
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)ceil_div(m, 4)), dim3(256), 0, st, W, w_f32, m, d, ldw, perm, w.Wk,
                      group == 0 ? 1 : 0, ternary, maxq, scales, zeros);
   GPTQ_CHECK_LAUNCH();
 
@@ -667,6 +764,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   a.scales = scales;
   a.zeros = zeros;
   a.err_sq = err_sq;
+  a.perm = perm;
   const int64_t S = sb_width(d, group);
   a.E = w.Esb;
   a.lde = S;
@@ -695,7 +793,9 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
     a.El = inner ? w.Elb : nullptr;
     a.einv = inner ? w.einv_b : nullptr;
     gptq_status_t s;
-    switch (group) {
+    if (stat)
+      s = launch_colloop<-2>(a, st);
+    else switch (group) {
       case 0: s = launch_colloop<0>(a, st); break;
       case 32: s = launch_colloop<32>(a, st); break;
       case 64: s = launch_colloop<64>(a, st); break;
@@ -732,7 +832,8 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
     }
   }
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)m), dim3(256), 0, st, (const uint8_t*)w.codes, d, m, d, cfg.bits,
-                     qcodes, W_hat, (const float*)scales, (const uint8_t*)zeros, group, ngroups);
+                     qcodes, W_hat, (const float*)scales, (const uint8_t*)zeros, group, ngroups,
+                     perm ? (const int32_t*)w.inv : (const int32_t*)nullptr, stat ? 1 : 0);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
@@ -740,7 +841,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
 gptq_status_t pack_enqueue(const uint8_t* codes, int64_t ldc, int64_t m, int64_t d, int bits, uint32_t* out,
                            hipStream_t st) {
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)m), dim3(256), 0, st, codes, ldc, m, d, bits, out, (float*)nullptr,
-                     (const float*)nullptr, (const uint8_t*)nullptr, 0, 1);
+                     (const float*)nullptr, (const uint8_t*)nullptr, 0, 1, (const int32_t*)nullptr, 0);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }

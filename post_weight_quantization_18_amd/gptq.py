@@ -8,8 +8,12 @@ Entry points (same names as include/gptq.h):
     accumulate_hessian(H, X, accumulate)      H (+)= 2 X^T X, lower triangle
     prepare_hinv(H, damp)                      U = chol_upper((H + lambda I)^-1)
     quantize_layer(W, U, bits, group_size, grid)
+    act_order(H)                               column order of descending diag(H)
+    permute_hessian(H, perm)                   H gathered into that order
+    quantize_layer_ordered(W, U, perm, bits, group_size, grid, static_groups)
     pack_codes(codes, bits)
-and quantize(W, x_chunks, ...) which runs the three stages of one layer.
+and quantize(W, x_chunks, ...) which runs the stages of one layer (natural
+order, or act-order with act_order=True).
 """
 
 from __future__ import annotations
@@ -28,7 +32,8 @@ GPTQ_GRID_ASYM_MINMAX, GPTQ_GRID_TERNARY = 0, 1
 WS_ACCUMULATE_HESSIAN, WS_PREPARE_HINV, WS_QUANTIZE_LAYER = 0, 1, 2
 
 EXPORTED = ["gptq_abi_version", "gptq_status_string", "gptq_workspace_bytes", "gptq_accumulate_hessian",
-            "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack_codes"]
+            "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_act_order", "gptq_permute_hessian",
+            "gptq_quantize_layer_ordered", "gptq_pack_codes"]
 
 
 class QCfg(ctypes.Structure):
@@ -61,6 +66,13 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_quantize_layer.restype = i32
     lib.gptq_quantize_layer.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, ctypes.POINTER(QCfg), vp, vp, vp, vp,
                                         vp, vp, sz, vp]
+    lib.gptq_act_order.restype = i32
+    lib.gptq_act_order.argtypes = [vp, i32, i64, i64, vp, vp]
+    lib.gptq_permute_hessian.restype = i32
+    lib.gptq_permute_hessian.argtypes = [vp, i32, i64, i64, vp, vp, i64, vp]
+    lib.gptq_quantize_layer_ordered.restype = i32
+    lib.gptq_quantize_layer_ordered.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, ctypes.POINTER(QCfg), vp, i32,
+                                                vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gptq_pack_codes.restype = i32
     lib.gptq_pack_codes.argtypes = [vp, i64, i64, i32, vp, vp]
     _lib = lib
@@ -183,6 +195,69 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, group_size: int 
     return out
 
 
+def act_order(H: torch.Tensor) -> torch.Tensor:
+    """int32 device [d]: perm[j] = the column with the j-th largest H_jj (ties in index order)."""
+    lib = load_library()
+    _need_cuda(H, "H")
+    d = H.shape[0]
+    perm = torch.empty(d, dtype=torch.int32, device=H.device)
+    _check(lib.gptq_act_order(_ptr(H), _DT[H.dtype], d, _rowmajor_ld(H, "H"), _ptr(perm), _stream(H.device)),
+           "gptq_act_order")
+    return perm
+
+
+_act_order = act_order  # `quantize` takes a flag of the same name
+
+
+def permute_hessian(H: torch.Tensor, perm: torch.Tensor, Hp: torch.Tensor | None = None) -> torch.Tensor:
+    """Hp[i][j] = H[perm[i]][perm[j]] for j <= i (lower triangles), same dtype as H."""
+    lib = load_library()
+    _need_cuda(H, "H")
+    _need_cuda(perm, "perm")
+    if perm.dtype != torch.int32 or not perm.is_contiguous():
+        raise ValueError("perm must be contiguous int32")
+    d = H.shape[0]
+    if Hp is None:
+        Hp = torch.empty(d, d, dtype=H.dtype, device=H.device)
+    _check(lib.gptq_permute_hessian(_ptr(H), _DT[H.dtype], d, _rowmajor_ld(H, "H"), _ptr(perm), _ptr(Hp),
+                                    _rowmajor_ld(Hp, "Hp"), _stream(H.device)), "gptq_permute_hessian")
+    return Hp
+
+
+def quantize_layer_ordered(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, bits: int, group_size: int = 0,
+                           grid: str = "asym", static_groups: bool = False, block_size: int = 128,
+                           want_w_hat: bool = True, workspace=None, out=None):
+    """quantize_layer with the columns quantized in the order perm (U: the factor of
+    the Hessian in that order). Outputs in natural column order, plus g_idx int32 [d]."""
+    lib = load_library()
+    _need_cuda(W, "W")
+    _need_cuda(U, "U")
+    _need_cuda(perm, "perm")
+    if perm.dtype != torch.int32 or not perm.is_contiguous():
+        raise ValueError("perm must be contiguous int32")
+    m, d = W.shape
+    cfg = make_qcfg(bits, group_size, grid, block_size)
+    ng = d // group_size if group_size else 1
+    dev = W.device
+    if out is None:
+        out = {
+            "qcodes": torch.empty(m, d * bits // 32, dtype=torch.int32, device=dev),
+            "scales": torch.empty(m, ng, dtype=torch.float32, device=dev),
+            "zeros": torch.empty(m, ng, dtype=torch.uint8, device=dev),
+            "g_idx": torch.empty(d, dtype=torch.int32, device=dev),
+            "w_hat": torch.empty(m, d, dtype=torch.float32, device=dev) if want_w_hat else None,
+            "err_sq": torch.empty(m, dtype=torch.float32, device=dev),
+        }
+    ws = _workspace(workspace_bytes(WS_QUANTIZE_LAYER, m, d, 0, cfg), dev, workspace)
+    _check(lib.gptq_quantize_layer_ordered(_ptr(W), _DT[W.dtype], m, d, _rowmajor_ld(W, "W"), _ptr(U), _DT[U.dtype],
+                                           _rowmajor_ld(U, "U"), ctypes.byref(cfg), _ptr(perm),
+                                           int(bool(static_groups)), _ptr(out["qcodes"]), _ptr(out["scales"]),
+                                           _ptr(out["zeros"]), _ptr(out["g_idx"]), _ptr(out["w_hat"]),
+                                           _ptr(out["err_sq"]), _ptr(ws), ws.numel(), _stream(dev)),
+           "gptq_quantize_layer_ordered")
+    return out
+
+
 def pack_codes(codes: torch.Tensor, bits: int) -> torch.Tensor:
     """codes uint8 [m, d] -> int32 storage of the uint32 bitstream [m, d*bits/32]."""
     lib = load_library()
@@ -196,18 +271,30 @@ def pack_codes(codes: torch.Tensor, bits: int) -> torch.Tensor:
 
 
 def quantize(W: torch.Tensor, x_chunks, bits: int, group_size: int = 0, grid: str = "asym", damp: float = 0.01,
-             h_dtype: torch.dtype = torch.float64, u_dtype: torch.dtype = torch.float32, want_w_hat: bool = True):
+             h_dtype: torch.dtype = torch.float64, u_dtype: torch.dtype = torch.float32, want_w_hat: bool = True,
+             act_order: bool = False, static_groups: bool = False):
     """The whole hot path of one layer: H over the chunks, U, then the column loop.
-    Returns (result dict, H, U, lam). Raises when H + lam I is not positive definite."""
+    Returns (result dict, H, U, lam). Raises when H + lam I is not positive definite.
+    With act_order the columns go in descending diag(H) (result["perm"]), U is the
+    factor of the permuted H, and the outputs are still in natural column order."""
     if isinstance(x_chunks, torch.Tensor):
         x_chunks = [x_chunks]
     d = W.shape[1]
     H = torch.empty(d, d, dtype=h_dtype, device=W.device)
     for i, xc in enumerate(x_chunks):
         accumulate_hessian(H, xc, accumulate=i > 0)
-    U, info, lam = prepare_hinv(H, damp, u_dtype=u_dtype)
+    perm = None
+    if act_order:
+        perm = _act_order(H)
+        U, info, lam = prepare_hinv(permute_hessian(H, perm), damp, u_dtype=u_dtype)
+    else:
+        U, info, lam = prepare_hinv(H, damp, u_dtype=u_dtype)
     bad = int(info.item())
     if bad:
         raise GPTQError(GPTQ_ERR_INVALID_ARG, f"H + lambda I is not positive definite (reversed minor {bad})")
-    res = quantize_layer(W, U, bits, group_size, grid, want_w_hat=want_w_hat)
+    if act_order:
+        res = quantize_layer_ordered(W, U, perm, bits, group_size, grid, static_groups, want_w_hat=want_w_hat)
+        res["perm"] = perm
+    else:
+        res = quantize_layer(W, U, bits, group_size, grid, want_w_hat=want_w_hat)
     return res, H, U, lam

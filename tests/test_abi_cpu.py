@@ -93,6 +93,21 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert q(G.make_qcfg(4, group_size=384), d=512) == G.GPTQ_ERR_UNSUPPORTED  # must divide d
     assert q(G.make_qcfg(4), d=200) == G.GPTQ_ERR_INVALID_ARG                # d % 32
     assert q(G.make_qcfg(4), ws=None) == G.GPTQ_ERR_WORKSPACE
+    # act_order / permute_hessian: null, ldh < d, bad dtype, aliasing
+    assert lib.gptq_act_order(None, 2, 64, 64, fake, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_act_order(fake, 2, 64, 32, fake, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_act_order(fake, 0, 64, 64, fake, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_permute_hessian(fake, 2, 64, 64, fake, fake, 64, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_permute_hessian(fake, 2, 64, 64, fake, _vp(1 << 24), 60, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_permute_hessian(fake, 2, 64, 64, None, _vp(1 << 24), 64, None) == G.GPTQ_ERR_INVALID_ARG
+    # quantize_layer_ordered: no order, bad static flag, unsupported configuration
+    def qo(cfg, perm=fake, static=0, d=256):
+        return lib.gptq_quantize_layer_ordered(fake, 1, 8, d, d, fake, 1, d, ctypes.byref(cfg), perm, static, fake,
+                                               fake, fake, None, None, None, fake, 1 << 40, None)
+    assert qo(G.make_qcfg(4), perm=None) == G.GPTQ_ERR_INVALID_ARG
+    assert qo(G.make_qcfg(4, group_size=128), static=2) == G.GPTQ_ERR_INVALID_ARG
+    assert qo(G.make_qcfg(5)) == G.GPTQ_ERR_UNSUPPORTED
+    assert qo(G.make_qcfg(4), d=200) == G.GPTQ_ERR_INVALID_ARG
     # pack: d*bits not a multiple of 32
     assert lib.gptq_pack_codes(fake, 4, 12, 3, fake, None) == G.GPTQ_ERR_INVALID_ARG
     assert lib.gptq_pack_codes(fake, 4, 64, 5, fake, None) == G.GPTQ_ERR_INVALID_ARG
