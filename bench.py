@@ -1,12 +1,16 @@
 """Benchmark of the GPTQ layer-quantization hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config opt2.7b-fc1]
+                    [--act-order [--static-groups]]
 
 One step = the whole hot path on one layer with W and X already resident in
 HBM: H accumulated over all of the layer's calibration tokens in one call
 (--chunk-tokens splits it into calls of that many tokens, as a caller that
 streams its calibration batches would), the fp64 inverse-Hessian factor, then
 the column loop with lazy 128-column updates, trailing GEMMs and packing.
+With --act-order the step also orders the columns by descending H_jj, gathers
+H into that order before the chain, and runs the column loop in that order
+(--static-groups: grids fitted on the original weights' natural groups).
 Prints one JSON line (rank 0). The per-stage device times come from HIP events
 recorded on the stream the library launches on (torch's current stream).
 """
@@ -68,6 +72,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--config", default="opt2.7b-fc1", choices=sorted(S.CONFIGS))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--act-order", action="store_true",
+                   help="quantize the columns in descending H_jj (desc_act)")
+    p.add_argument("--static-groups", action="store_true",
+                   help="with --act-order: grids of the natural groups, fitted on the original weights")
     p.add_argument("--chunk-tokens", type=int, default=CHUNK_TOKENS,
                    help="tokens per gptq_accumulate_hessian call (the whole X stays resident either way)")
     p.add_argument("--cpu-sample-rows", type=int, default=None)
@@ -89,14 +97,19 @@ def copy_calibration():
 class LayerRun:
     """Preallocated buffers for one layer; step() enqueues the whole hot path."""
 
-    def __init__(self, cfg: S.LayerConfig, w: torch.Tensor, x: torch.Tensor, chunk: int = CHUNK_TOKENS):
+    def __init__(self, cfg: S.LayerConfig, w: torch.Tensor, x: torch.Tensor, chunk: int = CHUNK_TOKENS,
+                 act_order: bool = False, static_groups: bool = False):
         chunk = min(chunk, cfg.n_tokens)
         self.cfg = cfg
+        self.act_order, self.static_groups = act_order, static_groups
         self.w, self.x = w, x
         dev = w.device
         d, m = cfg.d, cfg.m
         self.H = torch.empty(d, d, dtype=torch.float64, device=dev)
         self.U = torch.empty(d, d, dtype=torch.float32, device=dev)
+        if act_order:
+            self.perm = torch.empty(d, dtype=torch.int32, device=dev)
+            self.Hp = torch.empty(d, d, dtype=torch.float64, device=dev)
         self.chunk = chunk
         self.ws_h = torch.empty(max(1, G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, d, chunk)),
                                 dtype=torch.uint8, device=dev)
@@ -111,7 +124,9 @@ class LayerRun:
             "w_hat": torch.empty(m, d, dtype=torch.float32, device=dev),
             "err_sq": torch.empty(m, dtype=torch.float32, device=dev),
         }
-        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        if act_order:
+            self.out["g_idx"] = torch.empty(d, dtype=torch.int32, device=dev)
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         self.ev_h = [torch.cuda.Event(enable_timing=True) for _ in range(2 * self.n_chunks())]
         self.info = None
 
@@ -129,14 +144,27 @@ class LayerRun:
             if timed_chunks:
                 self.ev_h[2 * i + 1].record()
         self.ev[1].record()
-        _, self.info, self.lam = G.prepare_hinv(self.H, cfg.damp, U=self.U, workspace=self.ws_c)
+        h = self.H
+        if self.act_order:
+            G.act_order(self.H, self.perm)
+            h = G.permute_hessian(self.H, self.perm, self.Hp)
+        self.ev[4].record()
+        _, self.info, self.lam = G.prepare_hinv(h, cfg.damp, U=self.U, workspace=self.ws_c)
         self.ev[2].record()
-        G.quantize_layer(self.w, self.U, cfg.bits, cfg.group, cfg.grid, workspace=self.ws_q, out=self.out)
+        if self.act_order:
+            G.quantize_layer_ordered(self.w, self.U, self.perm, cfg.bits, cfg.group, cfg.grid, self.static_groups,
+                                     workspace=self.ws_q, out=self.out)
+        else:
+            G.quantize_layer(self.w, self.U, cfg.bits, cfg.group, cfg.grid, workspace=self.ws_q, out=self.out)
         self.ev[3].record()
 
     def stage_ms(self):
-        return {"hessian": self.ev[0].elapsed_time(self.ev[1]), "hinv_chain": self.ev[1].elapsed_time(self.ev[2]),
-                "quantize": self.ev[2].elapsed_time(self.ev[3]), "total": self.ev[0].elapsed_time(self.ev[3])}
+        st = {"hessian": self.ev[0].elapsed_time(self.ev[1])}
+        if self.act_order:
+            st["act_order"] = self.ev[1].elapsed_time(self.ev[4])
+        st.update({"hinv_chain": self.ev[4].elapsed_time(self.ev[2]), "quantize": self.ev[2].elapsed_time(self.ev[3]),
+                   "total": self.ev[0].elapsed_time(self.ev[3])})
+        return st
 
     def syrk_call_ms(self):
         return [self.ev_h[2 * i].elapsed_time(self.ev_h[2 * i + 1]) for i in range(self.n_chunks())]
@@ -146,7 +174,7 @@ def _say(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, w, x, rows=None, tokens=None):
+def cpu_baseline(cfg, w, x, rows=None, tokens=None, act_order=False, static_groups=False):
     """The fp64 oracle, as it stands, on a bounded sample of the same layer
     (about 10-30 s of CPU work), extrapolated to the whole layer:
       * H over `tokens` calibration tokens, scaled by N / tokens;
@@ -154,7 +182,9 @@ def cpu_baseline(cfg, w, x, rows=None, tokens=None):
         that H (at most 6144), scaled by (d / d_s)^3;
       * the column loop on `rows` rows at full width, scaled by m / rows. Its
         cost does not depend on U's values, so at d > d_s it runs on a stand-in
-        upper-triangular U (unit diagonal, 1e-3 above it)."""
+        upper-triangular U (unit diagonal, 1e-3 above it).
+    With act_order the oracle's order, permuted H and ordered loop are timed
+    instead (the order from the sampled H)."""
     import numpy as np
 
     import oracle as O
@@ -177,14 +207,21 @@ def cpu_baseline(cfg, w, x, rows=None, tokens=None):
     t0 = time.perf_counter()
     h = O.hessian([xs[i:i + 4096] for i in range(0, tokens, 4096)])
     t1 = time.perf_counter()
-    hd, _ = O.damp(h[:d_s, :d_s], cfg.damp)
+    if act_order:
+        perm = O.act_order_perm(h)
+        hd, _ = O.damp(h[np.ix_(perm[:d_s], perm[:d_s])], cfg.damp)
+    else:
+        hd, _ = O.damp(h[:d_s, :d_s], cfg.damp)
     u = O.inverse_hessian_factor(hd)
     t2 = time.perf_counter()
     if d_s < d:
         u = np.triu(np.full((d, d), 1e-3))
         np.fill_diagonal(u, 1.0)
     t3 = time.perf_counter()
-    O.gptq_quantize(ws, u, cfg.bits, cfg.grid, cfg.group)
+    if act_order:
+        O.gptq_quantize_ordered(ws, u, perm, cfg.bits, cfg.grid, cfg.group, static_groups)
+    else:
+        O.gptq_quantize(ws, u, cfg.bits, cfg.grid, cfg.group)
     t4 = time.perf_counter()
     t_h = (t1 - t0) * cfg.n_tokens / tokens
     t_chain = (t2 - t1) * (d / d_s) ** 3
@@ -195,7 +232,7 @@ def cpu_baseline(cfg, w, x, rows=None, tokens=None):
         "unit": "weights/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{cfg.name}: H over {tokens} of {cfg.n_tokens} tokens (x{cfg.n_tokens / tokens:g}); chain on "
+        "sample": (f"{cfg.name}{' act-order' if act_order else ''}: H over {tokens} of {cfg.n_tokens} tokens (x{cfg.n_tokens / tokens:g}); chain on "
                    f"the leading {d_s}x{d_s} block (x{(d / d_s) ** 3:g}); column loop on {rows} of {cfg.m} rows "
                    f"(x{cfg.m / rows:g}); measured {t1 - t0 + t2 - t1 + t4 - t3:.1f} s, extrapolated "
                    f"{total:.1f} s per layer"),
@@ -221,7 +258,9 @@ def main():
     x = S.make_activations(cfg, dev)
     torch.cuda.synchronize()
     _say("inputs resident; allocating buffers")
-    run = LayerRun(cfg, w, x, args.chunk_tokens)
+    if args.static_groups and not args.act_order:
+        raise SystemExit("--static-groups needs --act-order")
+    run = LayerRun(cfg, w, x, args.chunk_tokens, args.act_order, args.static_groups)
     for i in range(args.warmup):
         run.step()
         torch.cuda.synchronize()
@@ -274,7 +313,9 @@ def main():
         "dtype": "f16 MFMA->f32/f64 (H), f64 (U), f32 (column loop, trailing GEMM)",
         "data": "synthetic (seeded correlated-Gaussian X with outlier channels, N(0,0.02^2) W with outlier columns)",
         "config": {"workload": f"{cfg.name}: W {m}x{d} {cfg.w_dtype}, X {n}x{d} fp16, {cfg.bits}-bit {cfg.grid} "
-                               f"{'per-row' if cfg.group == 0 else 'g' + str(cfg.group)}, block 128, damp {cfg.damp}",
+                               f"{'per-row' if cfg.group == 0 else 'g' + str(cfg.group)}, block 128, damp {cfg.damp}"
+                               + (", act-order" + (" + static groups" if args.static_groups else "")
+                                  if args.act_order else ""),
                    "chunk_tokens": run.chunk, "m": m, "d": d, "n_tokens": n},
         "stages_ms": {k: round(v, 4) for k, v in stage.items()},
         "mfma_frac": {"syrk_fp16": round(f_syrk / (stage["hessian"] * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
@@ -283,7 +324,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         _say("timing the oracle on a bounded sample (cpu_baseline)")
-        result["cpu_baseline"] = cpu_baseline(cfg, w, x, args.cpu_sample_rows, args.cpu_sample_tokens)
+        result["cpu_baseline"] = cpu_baseline(cfg, w, x, args.cpu_sample_rows, args.cpu_sample_tokens,
+                                              args.act_order, args.static_groups)
     print(json.dumps(result), flush=True)
 
 

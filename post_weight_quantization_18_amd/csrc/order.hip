@@ -23,25 +23,36 @@ __device__ __forceinline__ uint64_t order_key(double v) {
 }
 
 // rank(i) = the number of columns that come before column i: a larger key, or
-// an equal key at a lower index; perm[rank(i)] = i. One thread per column;
-// the keys of all columns are staged through LDS 1024 at a time.
+// an equal key at a lower index; perm[rank(i)] = i. One workgroup per 64
+// columns (one per lane); the keys are staged through LDS 2048 at a time, the
+// four waves count over a quarter of each chunk, and the four partial counts
+// are added in LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void order_rank_kernel(const T* H, int64_t d, int64_t ldh, int32_t* perm) {
-  __shared__ uint64_t keys[1024];
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  constexpr int CH = 2048;
+  __shared__ uint64_t keys[CH];
+  __shared__ int32_t part[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
   const uint64_t ki = order_key(i < d ? (double)H[i * ldh + i] : 0.0);
-  int64_t rank = 0;
-  for (int64_t t0 = 0; t0 < d; t0 += 1024) {
-    const int n = (int)(d - t0 < 1024 ? d - t0 : 1024);
+  int32_t rank = 0;
+  for (int64_t t0 = 0; t0 < d; t0 += CH) {
+    const int n = (int)(d - t0 < CH ? d - t0 : CH);
     __syncthreads();
     for (int k = threadIdx.x; k < n; k += 256) keys[k] = order_key((double)H[(t0 + k) * ldh + t0 + k]);
     __syncthreads();
-    for (int k = 0; k < n; ++k) {
+    const int q = (n + 3) / 4;
+    const int kb = wv * q, ke = kb + q < n ? kb + q : n;
+    const int64_t il = i - t0;  // the tie-break compares chunk-local indices
+#pragma unroll 8
+    for (int k = kb; k < ke; ++k) {
       const uint64_t kv = keys[k];
-      rank += (kv > ki) || (kv == ki && t0 + k < i);
+      rank += (kv > ki) || (kv == ki && k < il);
     }
   }
-  if (i < d) perm[rank] = (int32_t)i;
+  part[wv][lane] = rank;
+  __syncthreads();
+  if (wv == 0 && i < d) perm[part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane]] = (int32_t)i;
 }
 
 // Hp[i][j] = H[perm[i]][perm[j]] for j <= i, read from H's lower triangle.
@@ -65,7 +76,7 @@ __global__ __launch_bounds__(256) void permute_h_kernel(const T* H, int64_t d, i
 }  // namespace
 
 gptq_status_t act_order_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, int32_t* perm, hipStream_t st) {
-  const dim3 grid((unsigned)ceil_div(d, 256));
+  const dim3 grid((unsigned)ceil_div(d, 64));
   if (h_f64)
     hipLaunchKernelGGL(order_rank_kernel<double>, grid, dim3(256), 0, st, (const double*)H, d, ldh, perm);
   else

@@ -184,6 +184,55 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* W, int w_f32, int
   }
 }
 
+// The gathering copy for an order perm when a row of W fits in CAPB bytes of
+// LDS (the smallest of 8, 16, 32 and 64 KB that holds it, so that small rows
+// leave room for more workgroups): one workgroup per row reads the row
+// coalesced into LDS (16-byte pieces when vec), then writes column j of the
+// copy from LDS entry perm[j] (entries outside [0, d) read 0). For one grid
+// per row it also fits that grid on the gathered values.
+template <typename T, int CAPB>
+__global__ __launch_bounds__(256) void prep_gather_kernel(const T* W, int64_t m, int64_t d, int64_t ldw,
+                                                          const int32_t* perm, float* Wk, int per_row, int ternary,
+                                                          float maxq, float* scales, uint8_t* zeros, int vec) {
+  __shared__ __attribute__((aligned(16))) T row[CAPB / sizeof(T)];
+  __shared__ float red[2][4];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (vec) {
+    const uint4* src = (const uint4*)(W + r * ldw);
+    for (int64_t k = tid; k < d * (int64_t)sizeof(T) / 16; k += 256) ((uint4*)row)[k] = src[k];
+  } else {
+    for (int64_t j = tid; j < d; j += 256) row[j] = W[r * ldw + j];
+  }
+  __syncthreads();
+  float vmin = INFINITY, vmax = -INFINITY;
+  for (int64_t j = tid; j < d; j += 256) {
+    int64_t c = perm[j];
+    if (c < 0 || c >= d) c = 0;
+    const float v = (float)row[c];
+    Wk[r * d + j] = v;
+    vmin = fminf(vmin, v);
+    vmax = fmaxf(vmax, v);
+  }
+  if (!per_row) return;
+  for (int off = 32; off > 0; off >>= 1) {
+    vmin = fminf(vmin, __shfl_xor(vmin, off));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = vmin;
+    red[1][tid >> 6] = vmax;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    vmin = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
+    vmax = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    GridFit g = fit_grid(vmin, vmax, ternary, maxq);
+    scales[r] = g.s;
+    zeros[r] = (uint8_t)g.z;
+  }
+}
+
 // Static groups: the grid of every natural group of `group` columns, fitted on
 // the original weights before the column loop. One wave per row.
 __global__ __launch_bounds__(256) void static_fit_kernel(const void* W, int w_f32, int64_t m, int64_t d, int64_t ldw,
@@ -637,14 +686,24 @@ __global__ __launch_bounds__(256) void usplit_kernel(const float* U, int64_t ldu
 // given, writes W_hat = s * (code - z). With inv set the codes are in the
 // quantization order and natural column c is read from position inv[c]
 // (entries outside [0, d) read position 0); its group is c / group with static
-// groups, else inv[c] / group.
+// groups, else inv[c] / group. STAGE > 0: the row of codes is first copied
+// into STAGE bytes of LDS (d <= STAGE, d % 16 == 0, ldc % 16 == 0), so that
+// the gathered reads come from LDS.
+constexpr int PACK_STAGE_MAX = 49152;
+template <int STAGE>
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* codes, int64_t ldc, int64_t m, int64_t d,
                                                    int bits, uint32_t* out, float* W_hat, const float* scales,
                                                    const uint8_t* zeros, int group, int ngroups,
                                                    const int32_t* inv, int static_groups) {
+  __shared__ __attribute__((aligned(16))) uint8_t cs[STAGE > 0 ? STAGE : 16];
   const int64_t r = blockIdx.x;
   if (r >= m) return;
   const uint8_t* crow = codes + r * ldc;
+  if constexpr (STAGE > 0) {
+    for (int64_t k = threadIdx.x; k < d / 16; k += 256) *(uint4*)(cs + 16 * k) = *(const uint4*)(crow + 16 * k);
+    __syncthreads();
+    crow = cs;
+  }
   const int64_t nwords = d * bits / 32;
   for (int64_t wd = threadIdx.x; wd < nwords; wd += 256) {
     const int64_t b0 = wd * 32;
@@ -745,8 +804,30 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
                        ldu32, d, (const uint32_t*)w.umax, w.Uth, w.Utl, w.uinv);
     GPTQ_CHECK_LAUNCH();
   }
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)ceil_div(m, 4)), dim3(256), 0, st, W, w_f32, m, d, ldw, perm, w.Wk,
-                     group == 0 ? 1 : 0, ternary, maxq, scales, zeros);
+  const int64_t row_bytes = d * (w_f32 ? 4 : 2);
+  if (perm && row_bytes <= 65536) {
+    const int vec = (row_bytes % 16 == 0) && ((ldw * (w_f32 ? 4 : 2)) % 16 == 0) && (((uintptr_t)W) & 15) == 0;
+    const int pr = group == 0 ? 1 : 0;
+    const dim3 g((unsigned)m), b(256);
+#define GPTQ_GATHER(T, CAPB) \
+  hipLaunchKernelGGL((prep_gather_kernel<T, CAPB>), g, b, 0, st, (const T*)W, m, d, ldw, perm, w.Wk, pr, ternary, \
+                     maxq, scales, zeros, vec)
+    if (w_f32) {
+      if (row_bytes <= 8192) GPTQ_GATHER(float, 8192);
+      else if (row_bytes <= 16384) GPTQ_GATHER(float, 16384);
+      else if (row_bytes <= 32768) GPTQ_GATHER(float, 32768);
+      else GPTQ_GATHER(float, 65536);
+    } else {
+      if (row_bytes <= 8192) GPTQ_GATHER(half_t, 8192);
+      else if (row_bytes <= 16384) GPTQ_GATHER(half_t, 16384);
+      else if (row_bytes <= 32768) GPTQ_GATHER(half_t, 32768);
+      else GPTQ_GATHER(half_t, 65536);
+    }
+#undef GPTQ_GATHER
+  } else {
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)ceil_div(m, 4)), dim3(256), 0, st, W, w_f32, m, d, ldw, perm,
+                       w.Wk, group == 0 ? 1 : 0, ternary, maxq, scales, zeros);
+  }
   GPTQ_CHECK_LAUNCH();
 
   ColArgs a;
@@ -831,16 +912,29 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
       if ((s = tgemm_enqueue(t, st)) != GPTQ_OK) return s;
     }
   }
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)m), dim3(256), 0, st, (const uint8_t*)w.codes, d, m, d, cfg.bits,
-                     qcodes, W_hat, (const float*)scales, (const uint8_t*)zeros, group, ngroups,
-                     perm ? (const int32_t*)w.inv : (const int32_t*)nullptr, stat ? 1 : 0);
+#define GPTQ_PACK(STAGE, INV)                                                                                       \
+  hipLaunchKernelGGL(pack_kernel<STAGE>, dim3((unsigned)m), dim3(256), 0, st, (const uint8_t*)w.codes, d, m, d,      \
+                     cfg.bits, qcodes, W_hat, (const float*)scales, (const uint8_t*)zeros, group, ngroups, INV,       \
+                     stat ? 1 : 0)
+  if (perm && d <= PACK_STAGE_MAX && d % 16 == 0) {
+    const int32_t* inv = w.inv;
+    if (d <= 8192) GPTQ_PACK(8192, inv);
+    else if (d <= 16384) GPTQ_PACK(16384, inv);
+    else if (d <= 32768) GPTQ_PACK(32768, inv);
+    else GPTQ_PACK(PACK_STAGE_MAX, inv);
+  } else {
+    const int32_t* inv = perm ? (const int32_t*)w.inv : (const int32_t*)nullptr;
+    GPTQ_PACK(0, inv);
+  }
+#undef GPTQ_PACK
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
 
 gptq_status_t pack_enqueue(const uint8_t* codes, int64_t ldc, int64_t m, int64_t d, int bits, uint32_t* out,
                            hipStream_t st) {
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)m), dim3(256), 0, st, codes, ldc, m, d, bits, out, (float*)nullptr,
+  hipLaunchKernelGGL(pack_kernel<0>, dim3((unsigned)m), dim3(256), 0, st, codes, ldc, m, d, bits, out,
+                     (float*)nullptr,
                      (const float*)nullptr, (const uint8_t*)nullptr, 0, 1, (const int32_t*)nullptr, 0);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;

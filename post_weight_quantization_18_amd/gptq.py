@@ -195,12 +195,15 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, group_size: int 
     return out
 
 
-def act_order(H: torch.Tensor) -> torch.Tensor:
+def act_order(H: torch.Tensor, perm: torch.Tensor | None = None) -> torch.Tensor:
     """int32 device [d]: perm[j] = the column with the j-th largest H_jj (ties in index order)."""
     lib = load_library()
     _need_cuda(H, "H")
     d = H.shape[0]
-    perm = torch.empty(d, dtype=torch.int32, device=H.device)
+    if perm is None:
+        perm = torch.empty(d, dtype=torch.int32, device=H.device)
+    elif perm.dtype != torch.int32 or not perm.is_contiguous() or perm.numel() != d:
+        raise ValueError("perm must be contiguous int32 [d]")
     _check(lib.gptq_act_order(_ptr(H), _DT[H.dtype], d, _rowmajor_ld(H, "H"), _ptr(perm), _stream(H.device)),
            "gptq_act_order")
     return perm

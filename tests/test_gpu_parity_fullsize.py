@@ -161,3 +161,102 @@ def test_layer_properties_full_size(name):
     say(f"[check] {name}: OBS identity max rel err {obs_rel:.2e}; GPTQ / RTN loss on {len(rows)} rows = {ratio:.4f}")
     assert obs_rel <= 1e-3
     assert ratio < 1.0
+
+
+# ---------------------------------------------------------------------------
+# act-order (desc_act) at full size
+# ---------------------------------------------------------------------------
+@pytest.mark.timeout(1200)
+def test_act_order_parity_opt13b_attn_full():
+    """The whole oracle's act-order path at 5120 x 5120, 262144 tokens."""
+    from parity_util import assert_ordered_gates, compare_layer_ordered, gpu_layer_ordered
+    cfg = S.CONFIGS["opt13b-attn"]
+    say(f"[case] full layer act-order {cfg.name} m={cfg.m} d={cfg.d} n={cfg.n_tokens}")
+    w, x = S.make_layer(cfg, device="cuda")
+    w, x = w.cpu(), x.cpu()
+    gpu = gpu_layer_ordered(w, x, cfg.bits, cfg.group, cfg.grid, False, cfg.damp)
+    stats = compare_layer_ordered(w, x, cfg.bits, cfg.group, cfg.grid, False, gpu, cfg.damp, cfg.name + "-act-order")
+    assert_ordered_gates(stats, False, cfg.group)
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name,static", [("opt175b-q", True)])
+def test_act_order_properties_full_size(name, static):
+    """d = 12288 with act-order: the order against the oracle's on the GPU's
+    own diagonal and against H_jj from X, sampled entries of the permuted H,
+    U against the permuted H_d, and the output checks of the natural-order
+    test with g_idx."""
+    cfg = S.CONFIGS[name]
+    say(f"[case] full-size act-order properties {name} static={static} m={cfg.m} d={cfg.d}")
+    rng = np.random.default_rng(12)
+    w = S.make_weights(cfg, DEV)
+    x = S.make_activations(cfg, DEV)
+    d, m = cfg.d, cfg.m
+    H = torch.empty(d, d, dtype=torch.float64, device=DEV)
+    G.accumulate_hessian(H, x, accumulate=False)
+    perm = G.act_order(H)
+    Hp = G.permute_hessian(H, perm)
+    U, info, lam_t = G.prepare_hinv(Hp, cfg.damp, u_dtype=torch.float64)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    lam = float(lam_t.item())
+    res = G.quantize_layer_ordered(w, U, perm, cfg.bits, cfg.group, cfg.grid, static)
+    torch.cuda.synchronize()
+
+    p = perm.cpu().numpy().astype(np.int64)
+    hdiag = torch.diagonal(H).cpu().numpy()
+    np.testing.assert_array_equal(p, O.act_order_perm(np.diag(hdiag)))
+    dx = _diag_h(x).cpu().numpy()[p]
+    assert np.all(dx[1:] <= dx[:-1] * (1 + 1e-7))
+    say(f"[check] {name}: order bit-exact on the GPU's diagonal; H_jj from X non-increasing along it")
+
+    ii = np.sort(rng.choice(d, 64, replace=False))
+    pt = torch.as_tensor(p, device=DEV)
+    for i in ii.tolist():
+        jj = torch.arange(0, i + 1, max(1, i // 50), device=DEV)
+        a = torch.maximum(pt[i], pt[jj])
+        b = torch.minimum(pt[i], pt[jj])
+        assert torch.equal(Hp[i, jj], H[a, b])
+    worst = 0.0
+    for j in rng.choice(d, 3, replace=False).tolist():
+        v = _hd_column(Hp, j, lam)
+        y = U.t() @ (U @ v)
+        e = torch.zeros_like(y)
+        e[j] = 1.0
+        worst = max(worst, float((y - e).abs().max().item()))
+    say(f"[check] {name}: sampled Hp exact; max |U^T U Hp_d e_j - e_j| = {worst:.2e}")
+    assert worst <= 1e-6
+
+    gidx = res["g_idx"].cpu().numpy().astype(np.int64)
+    if static:
+        np.testing.assert_array_equal(gidx, np.arange(d) // cfg.group)
+    else:
+        want = np.empty(d, np.int64)
+        want[p] = np.arange(d) // cfg.group
+        np.testing.assert_array_equal(gidx, want)
+    rows = np.sort(rng.choice(m, 24, replace=False))
+    rt = torch.as_tensor(rows, device=DEV)
+    codes = O.unpack_codes(res["qcodes"][rt].cpu().numpy().view(np.uint32), cfg.bits, d)
+    maxq = O.maxq_of(cfg.bits, cfg.grid)
+    assert codes.max() <= maxq
+    scales = res["scales"][rt].cpu().numpy()
+    zeros = res["zeros"][rt].cpu().numpy().astype(np.int64)
+    w_hat = res["w_hat"][rt].cpu().numpy()
+    expect = scales[:, gidx].astype(np.float32) * (codes.astype(np.float32) - zeros[:, gidx].astype(np.float32))
+    assert np.array_equal(w_hat, expect)
+    wr = w[rt].double()
+    if static:
+        s_o, z_o = O.static_group_grids(wr.cpu().numpy(), cfg.bits, cfg.grid, cfg.group)
+        assert float(np.max(np.abs(scales - s_o) / s_o)) <= 1e-6
+        assert int(np.max(np.abs(zeros - z_o))) <= 1
+    delta = wr - res["w_hat"][rt].double()
+    loss = _row_losses(x, delta)
+    obs = res["err_sq"][rt].double()
+    ident = loss + 0.5 * lam * (delta * delta).sum(1)
+    obs_rel = float(((obs - ident).abs() / ident).max().item())
+    rtn = O.rtn_quantize(wr.cpu().numpy(), cfg.bits, cfg.grid, cfg.group)
+    loss_rtn = _row_losses(x, wr - torch.as_tensor(rtn.w_hat, device=DEV))
+    ratio = float(loss.sum().item() / loss_rtn.sum().item())
+    say(f"[check] {name}: OBS identity max rel err {obs_rel:.2e}; act-order / RTN loss on {len(rows)} rows = {ratio:.4f}")
+    assert obs_rel <= 1e-3
+    assert ratio < 1.0
