@@ -196,6 +196,23 @@ gptq_status_t gptq_quantize_layer_ordered(const void* W, int32_t w_dtype, int64_
                                           float* scales, uint8_t* zeros, int32_t* g_idx, float* W_hat,
                                           float* err_sq, void* workspace, size_t ws_bytes, void* stream);
 
+/* Generation with the packed weights: y = W_hat x for one token (batch 1),
+ * the weights dequantized on the fly, y[r] = sum_j s[r][g(j)] (c[r][j] - z[r][g(j)]) x[j]
+ * with g(j) = j / group_size (0 for one grid per row). FDE breakdown, section
+ * 01: an inference kernel reads the 3/4-bit weights and dequantizes them on
+ * the fly; nubint review, "Key findings": 3-bit OPT-175B generation speedups.
+ *  qcodes   device uint32 [m][d * bits / 32], the bitstream gptq_quantize_layer
+ *           writes (4-byte aligned).  scales / zeros: device [m][ngroups] as
+ *           written by gptq_quantize_layer.
+ *  bits     2, 3, 4 or 8 (ternary codes use bits = 2).
+ *  group_size 0, or a multiple of 32 dividing d (natural column groups; the
+ *           g_idx layout of act-order without static groups is not taken).
+ *  x        device fp16 [d], 16-byte aligned.   y device float [m], out.
+ *  d % 32 == 0. Sums are carried in fp32: per 32-code chunk sum c x and
+ *  sum x, then s (sum c x - z sum x), added over chunks and across a wave. */
+gptq_status_t gptq_dequant_gemv(const uint32_t* qcodes, const float* scales, const uint8_t* zeros, int64_t m,
+                                int64_t d, int32_t bits, int32_t group_size, const void* x, float* y, void* stream);
+
 /* Bit packing of integer codes (one byte per code) into the row-wise LSB-first
  * bitstream gptq_quantize_layer writes (which packs in its own epilogue).
  * FDE breakdown, section 01: the output is 3-bit (or 4-bit) weights that an

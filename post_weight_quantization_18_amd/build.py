@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgptq_mi355x.so")
-SOURCES = ["gptq_api.hip", "syrk.hip", "chain.hip", "quant.hip", "trail.hip", "order.hip"]
+SOURCES = ["gptq_api.hip", "syrk.hip", "chain.hip", "quant.hip", "trail.hip", "order.hip", "gemv.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

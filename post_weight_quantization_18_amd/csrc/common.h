@@ -105,6 +105,10 @@ struct TgemmArgs {
 };
 gptq_status_t tgemm_enqueue(const TgemmArgs& a, hipStream_t st);
 
+// y = W_hat x from the packed codes (one token); x fp16 [d] 16-byte aligned.
+gptq_status_t dq_gemv_enqueue(const uint32_t* q, const float* scales, const uint8_t* zeros, int64_t m, int64_t d,
+                              int bits, int group, const half_t* x, float* y, hipStream_t st);
+
 gptq_status_t pack_enqueue(const uint8_t* codes, int64_t ldc, int64_t m, int64_t d, int bits,
                            uint32_t* out, hipStream_t st);
 

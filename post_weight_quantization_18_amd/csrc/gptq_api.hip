@@ -140,6 +140,15 @@ gptq_status_t gptq_quantize_layer_ordered(const void* W, int32_t w_dtype, int64_
                        W_hat, err_sq, workspace, ws_bytes, (hipStream_t)stream, perm, static_groups, g_idx);
 }
 
+gptq_status_t gptq_dequant_gemv(const uint32_t* qcodes, const float* scales, const uint8_t* zeros, int64_t m,
+                                int64_t d, int32_t bits, int32_t group_size, const void* x, float* y, void* stream) {
+  if (!qcodes || !scales || !zeros || !x || !y || m <= 0 || d <= 0 || d % 32) return GPTQ_ERR_INVALID_ARG;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_INVALID_ARG;
+  if (group_size < 0 || (group_size && (group_size % 32 || d % group_size))) return GPTQ_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(qcodes, 4)) return GPTQ_ERR_INVALID_ARG;
+  return dq_gemv_enqueue(qcodes, scales, zeros, m, d, bits, group_size, (const half_t*)x, y, (hipStream_t)stream);
+}
+
 gptq_status_t gptq_pack_codes(const uint8_t* codes, int64_t m, int64_t d, int32_t bits, uint32_t* out,
                               void* stream) {
   if (!codes || !out || m <= 0 || d <= 0) return GPTQ_ERR_INVALID_ARG;

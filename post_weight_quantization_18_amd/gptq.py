@@ -11,6 +11,7 @@ Entry points (same names as include/gptq.h):
     act_order(H)                               column order of descending diag(H)
     permute_hessian(H, perm)                   H gathered into that order
     quantize_layer_ordered(W, U, perm, bits, group_size, grid, static_groups)
+    dequant_gemv(qcodes, scales, zeros, bits, group_size, x)   y = W_hat x, one token
     pack_codes(codes, bits)
 and quantize(W, x_chunks, ...) which runs the stages of one layer (natural
 order, or act-order with act_order=True).
@@ -33,7 +34,7 @@ WS_ACCUMULATE_HESSIAN, WS_PREPARE_HINV, WS_QUANTIZE_LAYER = 0, 1, 2
 
 EXPORTED = ["gptq_abi_version", "gptq_status_string", "gptq_workspace_bytes", "gptq_accumulate_hessian",
             "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_act_order", "gptq_permute_hessian",
-            "gptq_quantize_layer_ordered", "gptq_pack_codes"]
+            "gptq_quantize_layer_ordered", "gptq_dequant_gemv", "gptq_pack_codes"]
 
 
 class QCfg(ctypes.Structure):
@@ -73,6 +74,8 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_quantize_layer_ordered.restype = i32
     lib.gptq_quantize_layer_ordered.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, ctypes.POINTER(QCfg), vp, i32,
                                                 vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gptq_dequant_gemv.restype = i32
+    lib.gptq_dequant_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp]
     lib.gptq_pack_codes.restype = i32
     lib.gptq_pack_codes.argtypes = [vp, i64, i64, i32, vp, vp]
     _lib = lib
@@ -259,6 +262,25 @@ def quantize_layer_ordered(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor,
                                            _ptr(out["err_sq"]), _ptr(ws), ws.numel(), _stream(dev)),
            "gptq_quantize_layer_ordered")
     return out
+
+
+def dequant_gemv(qcodes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, bits: int, group_size: int,
+                 x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y fp32 [m] = W_hat x with W_hat dequantized on the fly from the packed
+    codes (the quantize_layer outputs); x fp16 [d]."""
+    lib = load_library()
+    for t, n in ((qcodes, "qcodes"), (scales, "scales"), (zeros, "zeros"), (x, "x")):
+        _need_cuda(t, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if x.dtype != torch.float16 or scales.dtype != torch.float32 or zeros.dtype != torch.uint8:
+        raise ValueError("x fp16, scales fp32, zeros uint8")
+    m, d = qcodes.shape[0], x.shape[0]
+    if y is None:
+        y = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check(lib.gptq_dequant_gemv(_ptr(qcodes), _ptr(scales), _ptr(zeros), m, d, bits, group_size, _ptr(x), _ptr(y),
+                                 _stream(x.device)), "gptq_dequant_gemv")
+    return y
 
 
 def pack_codes(codes: torch.Tensor, bits: int) -> torch.Tensor:

@@ -108,6 +108,12 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert qo(G.make_qcfg(4, group_size=128), static=2) == G.GPTQ_ERR_INVALID_ARG
     assert qo(G.make_qcfg(5)) == G.GPTQ_ERR_UNSUPPORTED
     assert qo(G.make_qcfg(4), d=200) == G.GPTQ_ERR_INVALID_ARG
+    # dequant_gemv: d % 32, bits, group not a multiple of 32, misaligned x
+    assert lib.gptq_dequant_gemv(fake, fake, fake, 4, 40, 4, 0, fake, fake, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_dequant_gemv(fake, fake, fake, 4, 64, 5, 0, fake, fake, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_dequant_gemv(fake, fake, fake, 4, 96, 3, 48, fake, fake, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_dequant_gemv(fake, fake, fake, 4, 64, 3, 0, _vp((1 << 20) + 2), fake, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_dequant_gemv(None, fake, fake, 4, 64, 3, 0, fake, fake, None) == G.GPTQ_ERR_INVALID_ARG
     # pack: d*bits not a multiple of 32
     assert lib.gptq_pack_codes(fake, 4, 12, 3, fake, None) == G.GPTQ_ERR_INVALID_ARG
     assert lib.gptq_pack_codes(fake, 4, 64, 5, fake, None) == G.GPTQ_ERR_INVALID_ARG
