@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config opt2.7b-fc1]
                     [--act-order [--static-groups]]
+    python bench.py --gemv [--steps K] [--warmup W]
 
 One step = the whole hot path on one layer with W and X already resident in
 HBM: H accumulated over all of the layer's calibration tokens in one call
@@ -11,6 +12,9 @@ the column loop with lazy 128-column updates, trailing GEMMs and packing.
 With --act-order the step also orders the columns by descending H_jj, gathers
 H into that order before the chain, and runs the column loop in that order
 (--static-groups: grids fitted on the original weights' natural groups).
+--gemv times generation with the packed weights instead: one token through the
+six layers of an OPT-175B block (q, k, v, out, fc1, fc2; 3-bit, g128), each a
+dequantizing matrix-vector product that streams its packed codes from HBM.
 Prints one JSON line (rank 0). The per-stage device times come from HIP events
 recorded on the stream the library launches on (torch's current stream).
 """
@@ -24,6 +28,7 @@ import platform
 import sys
 import time
 
+import numpy as np
 import torch
 
 from post_weight_quantization_18_amd import gptq as G
@@ -74,6 +79,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--act-order", action="store_true",
                    help="quantize the columns in descending H_jj (desc_act)")
+    p.add_argument("--gemv", action="store_true",
+                   help="time the dequantizing matrix-vector product over an OPT-175B block instead")
     p.add_argument("--static-groups", action="store_true",
                    help="with --act-order: grids of the natural groups, fitted on the original weights")
     p.add_argument("--chunk-tokens", type=int, default=CHUNK_TOKENS,
@@ -241,6 +248,94 @@ def cpu_baseline(cfg, w, x, rows=None, tokens=None, act_order=False, static_grou
     }
 
 
+def gemv_bench(args):
+    """One step = one token through the six OPT-175B block layers, each
+    y = W_hat x from its packed 3-bit g128 codes (synthetic random codes,
+    scales and zero points: the time does not depend on their values)."""
+    dev = torch.device("cuda:0")
+    layers = []
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    for name in S.OPT175B_BLOCK:
+        cfg = S.CONFIGS[name]
+        m, d, bits, group = cfg.m, cfg.d, cfg.bits, cfg.group
+        ng = d // group
+        q = torch.randint(-2 ** 31, 2 ** 31 - 1, (m, d * bits // 32), dtype=torch.int32, device=dev, generator=gen)
+        sc = torch.rand(m, ng, device=dev, generator=gen) * 0.01 + 1e-3
+        z = torch.randint(0, 1 << bits, (m, ng), dtype=torch.uint8, device=dev, generator=gen)
+        x = torch.randn(d, device=dev, generator=gen).half()
+        y = torch.empty(m, dtype=torch.float32, device=dev)
+        nbytes = m * d * bits // 8 + m * ng * 5 + d * 2 + m * 4
+        layers.append((name, q, sc, z, bits, group, x, y, nbytes))
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers]
+
+    def step(timed):
+        for i, (name, q, sc, z, bits, group, x, y, nb) in enumerate(layers):
+            if timed:
+                ev[i][0].record()
+            G.dequant_gemv(q, sc, z, bits, group, x, y)
+            if timed:
+                ev[i][1].record()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    per = {l[0]: 0.0 for l in layers}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        for i, l in enumerate(layers):
+            per[l[0]] += ev[i][0].elapsed_time(ev[i][1])
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    per = {k: v / args.steps for k, v in per.items()}
+    total_bytes = sum(l[8] for l in layers)
+    big = max(layers, key=lambda l: l[8])
+    big_gbs = big[8] / (per[big[0]] * 1e-3) / 1e9
+    result = {
+        "metric": "tokens per second through one OPT-175B block with 3-bit packed weights (batch 1)",
+        "value": 1e3 / ms_step,
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u3 codes -> f32 (fp16 x)",
+        "data": "synthetic packed codes, scales and zero points of the block's shapes",
+        "config": {"workload": "OPT-175B block q, k, v, out (12288x12288), fc1 (49152x12288), fc2 (12288x49152); "
+                               "3-bit g128 packed weights, one token", "block_bytes": total_bytes},
+        "layer_ms": {k: round(v, 5) for k, v in per.items()},
+        "block_gbs": round(total_bytes / (sum(per.values()) * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": f"dq_gemv_kernel<3> ({big[0]})", "achieved": round(big_gbs, 1),
+                     "peak": 8000.0, "unit": "GB/s", "frac": round(big_gbs / 8000.0, 4), "traffic": None,
+                     "per_launch": {"bytes": big[8], "avg_ms": round(per[big[0]], 5)}},
+    }
+    if not args.no_cpu_baseline:
+        _say("timing the oracle on sampled rows of every layer (cpu_baseline)")
+        result["cpu_baseline"] = gemv_cpu_baseline(layers)
+    print(json.dumps(result), flush=True)
+
+
+def gemv_cpu_baseline(layers, rows=32):
+    """The oracle's dequant_matvec on `rows` rows of each block layer (the same
+    packed codes), scaled by m / rows per layer."""
+    import oracle as O
+    total, measured = 0.0, 0.0
+    for name, q, sc, z, bits, group, x, y, nb in layers:
+        m = q.shape[0]
+        qs = q[:rows].cpu().numpy().view(np.uint32)
+        ss, zs, xs = sc[:rows].cpu().numpy(), z[:rows].cpu().numpy(), x.cpu().numpy()
+        t0 = time.perf_counter()
+        O.dequant_matvec(qs, ss, zs, bits, group, xs)
+        dt = time.perf_counter() - t0
+        measured += dt
+        total += dt * m / rows
+    return {"value": 1.0 / total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"dequant_matvec on {rows} rows of each of the 6 layers, scaled by m/{rows}; measured "
+                      f"{measured:.1f} s, extrapolated {total:.1f} s per token",
+            "cpu": platform.processor() or platform.machine()}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -250,6 +345,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding notes in the design "
               "document); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.gemv:
+        G.load_library()
+        gemv_bench(args)
+        return
     cfg = S.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     G.load_library()
