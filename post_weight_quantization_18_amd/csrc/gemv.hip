@@ -26,7 +26,9 @@ __device__ __forceinline__ uint32_t chunk_code(const uint32_t (&w)[BITS], int j)
 // each row (chunk k = words [k BITS, (k + 1) BITS) of the row, which lie in one
 // group because groups are multiples of 32 columns). Per chunk the lane forms
 // cx = sum c_j x_j and sx = sum x_j in fp32 and adds s (cx - z sx); the lanes'
-// sums are added across the wave.
+// sums are added across the wave. The codes, scales, zero points and x of the
+// lane's next chunk are loaded before the current one is used, so that two
+// chunks per row are in flight.
 template <int BITS>
 __global__ __launch_bounds__(256) void dq_gemv_kernel(const uint32_t* q, const float* scales, const uint8_t* zeros,
                                                       int64_t m, int64_t d, int group, int ngroups, const half_t* x,
@@ -38,32 +40,57 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const uint32_t* q, const f
   float acc[GV_ROWS];
 #pragma unroll
   for (int rr = 0; rr < GV_ROWS; ++rr) acc[rr] = 0.0f;
-  for (int64_t k = lane; k < nch; k += 64) {
-    float xf[32];
-    const half8* xp = (const half8*)(x + 32 * k);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const half8 h = xp[v];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xf[8 * v + e] = (float)h[e];
-    }
-    float sx = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) sx += xf[j];
+  uint32_t wc[GV_ROWS][BITS];
+  float sc[GV_ROWS];
+  uint32_t zc[GV_ROWS];
+  half8 xc[4];
+  auto load = [&](int64_t k, uint32_t (&w)[GV_ROWS][BITS], float (&sv)[GV_ROWS], uint32_t (&zv)[GV_ROWS],
+                  half8 (&xv)[4]) {
     const int64_t g = group ? (32 * k) / group : 0;
 #pragma unroll
     for (int rr = 0; rr < GV_ROWS; ++rr) {
-      const int64_t r = r0 + rr;
-      if (r < m) {
-        uint32_t w[BITS];
+      const int64_t r = r0 + rr < m ? r0 + rr : m - 1;  // rows past m repeat the last row, unused
 #pragma unroll
-        for (int b = 0; b < BITS; ++b) w[b] = q[r * wpr + k * BITS + b];
-        float cx = 0.0f;
+      for (int b = 0; b < BITS; ++b) w[rr][b] = q[r * wpr + k * BITS + b];
+      sv[rr] = scales[r * ngroups + g];
+      zv[rr] = zeros[r * ngroups + g];
+    }
+    const half8* xp = (const half8*)(x + 32 * k);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) cx = fmaf((float)chunk_code<BITS>(w, j), xf[j], cx);
-        const float s = scales[r * ngroups + g], z = (float)zeros[r * ngroups + g];
-        acc[rr] = fmaf(s, fmaf(-z, sx, cx), acc[rr]);
+    for (int v = 0; v < 4; ++v) xv[v] = xp[v];
+  };
+  if (lane < nch) load(lane, wc, sc, zc, xc);
+  for (int64_t k = lane; k < nch; k += 64) {
+    uint32_t wn[GV_ROWS][BITS];
+    float sn[GV_ROWS];
+    uint32_t zn[GV_ROWS];
+    half8 xn[4];
+    if (k + 64 < nch) load(k + 64, wn, sn, zn, xn);
+    float xf[32];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xf[8 * v + e] = (float)xc[v][e];
+    float sx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) sx += xf[j];
+#pragma unroll
+    for (int rr = 0; rr < GV_ROWS; ++rr) {
+      float cx = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) cx = fmaf((float)chunk_code<BITS>(wc[rr], j), xf[j], cx);
+      acc[rr] = fmaf(sc[rr], fmaf(-(float)zc[rr], sx, cx), acc[rr]);
+    }
+    if (k + 64 < nch) {
+#pragma unroll
+      for (int rr = 0; rr < GV_ROWS; ++rr) {
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) wc[rr][b] = wn[rr][b];
+        sc[rr] = sn[rr];
+        zc[rr] = zn[rr];
       }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xc[v] = xn[v];
     }
   }
 #pragma unroll
