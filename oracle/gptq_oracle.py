@@ -185,6 +185,26 @@ def boundary_distance(p, maxq: int) -> np.ndarray:
     return np.abs(p - b)
 
 
+def follow_zero_points(v, s, z, fz, band: float):
+    """Follow mode for the integer zero points of asymmetric grids fitted to the
+    rows of v (scales s, the oracle's zero points z) against another
+    implementation's zero points fz. A differing zero point is a band mismatch
+    when it is the adjacent integer and -lo/s lies within `band` of the
+    half-integer between the two (lo as the fit takes it: min(v, 0), or -1 when
+    both ends are 0); anything else is a hard mismatch. Returns (the zero points
+    to continue with, band count, hard count)."""
+    v = np.asarray(v, dtype=np.float64)
+    fz = np.asarray(fz).astype(np.int64).reshape(-1)
+    lo = np.minimum(np.min(v, axis=1), 0.0)
+    hi = np.maximum(np.max(v, axis=1), 0.0)
+    lo = np.where((lo == 0.0) & (hi == 0.0), -1.0, lo)
+    zr = -lo / s
+    diff = fz != z
+    near = np.abs(zr - (np.minimum(fz, z) + 0.5)) < band
+    adj = np.abs(fz - z) == 1
+    return (np.where(diff, fz, z), int(np.sum(diff & near & adj)), int(np.sum(diff & ~(near & adj))))
+
+
 # ---------------------------------------------------------------------------
 # Step 4: the column loop.
 # ---------------------------------------------------------------------------
@@ -247,7 +267,8 @@ def gptq_quantize(w, u, bits: int, grid: str = GRID_ASYM, group: int = 0,
     within `band` grid units of the boundary between the two, else a hard
     mismatch. In both cases the oracle then continues with the given code, so
     that one legitimate choice at a boundary does not cascade down the row.
-    follow_zeros does the same for the per-group integer zero points.
+    follow_zeros does the same for the integer zero points ([m, ngroups]; for
+    one grid per row [m, 1]), see follow_zero_points.
 
     col_grid (optional, (s [m, d], z [m, d])): a fixed grid for every column,
     fitted beforehand (static groups); no grid is fitted in the loop, and
@@ -271,6 +292,10 @@ def gptq_quantize(w, u, bits: int, grid: str = GRID_ASYM, group: int = 0,
         group = 0
     elif group == 0:
         s, z, _ = fit_grid(w, bits, grid)
+        if follow_zeros is not None and grid == GRID_ASYM:
+            z, zb, zh = follow_zero_points(w, s, z, np.asarray(follow_zeros)[:, 0], band)
+            res.zero_band_mismatch += zb
+            res.zero_hard_mismatch += zh
         res.scales[:, 0] = s
         res.zeros[:, 0] = z
     step = block if blocked else d
@@ -280,15 +305,10 @@ def gptq_quantize(w, u, bits: int, grid: str = GRID_ASYM, group: int = 0,
             if group and j % group == 0:
                 s, z, _ = fit_grid(w[:, j:j + group], bits, grid)
                 if follow_zeros is not None and grid == GRID_ASYM:
-                    fz = np.asarray(follow_zeros)[:, j // group].astype(np.int64)
-                    lo = np.minimum(np.min(w[:, j:j + group], axis=1), 0.0)
-                    zr = -lo / s
-                    diff = fz != z
-                    near = np.abs(zr - (np.minimum(fz, z) + 0.5)) < band
-                    adj = np.abs(fz - z) == 1
-                    res.zero_band_mismatch += int(np.sum(diff & near & adj))
-                    res.zero_hard_mismatch += int(np.sum(diff & ~(near & adj)))
-                    z = fz
+                    z, zb, zh = follow_zero_points(w[:, j:j + group], s, z,
+                                                   np.asarray(follow_zeros)[:, j // group], band)
+                    res.zero_band_mismatch += zb
+                    res.zero_hard_mismatch += zh
                 res.scales[:, j // group] = s
                 res.zeros[:, j // group] = z
             if col_grid is not None:
@@ -431,14 +451,10 @@ def gptq_quantize_ordered(w, u_perm, perm, bits: int, grid: str = GRID_ASYM, gro
             # finite precision); anything else is a hard mismatch
             fz = np.asarray(follow_zeros).astype(np.int64)
             for k in range(d // group):
-                lo = np.minimum(np.min(w[:, k * group:(k + 1) * group], axis=1), 0.0)
-                zr = -lo / s_g[:, k]
-                diff = fz[:, k] != z_g[:, k]
-                near = np.abs(zr - (np.minimum(fz[:, k], z_g[:, k]) + 0.5)) < band
-                adj = np.abs(fz[:, k] - z_g[:, k]) == 1
-                zb += int(np.sum(diff & near & adj))
-                zh += int(np.sum(diff & ~(near & adj)))
-                z_g[:, k] = np.where(diff, fz[:, k], z_g[:, k])
+                z_g[:, k], b_k, h_k = follow_zero_points(w[:, k * group:(k + 1) * group], s_g[:, k], z_g[:, k],
+                                                         fz[:, k], band)
+                zb += b_k
+                zh += h_k
         gcol = perm // group  # natural group of the j-th quantized column
         res_p = gptq_quantize(wp, u_perm, bits, grid, 0, block, follow_codes=fc, band=band,
                               blocked=blocked, col_grid=(s_g[:, gcol], z_g[:, gcol]))

@@ -90,8 +90,7 @@ def compare_layer(w: torch.Tensor, x: torch.Tensor, bits, group, grid, gpu: dict
     uu = np.triu(u)
     stats["u_rel"] = float(np.linalg.norm(np.triu(gpu["U"]) - uu) / np.linalg.norm(uu))
     stats["u_lower_zero"] = bool(np.all(np.tril(gpu["U"], -1) == 0))
-    follow = O.gptq_quantize(wn, u, bits, grid, group, follow_codes=gpu["codes"],
-                             follow_zeros=gpu["zeros"] if group else None)
+    follow = O.gptq_quantize(wn, u, bits, grid, group, follow_codes=gpu["codes"], follow_zeros=gpu["zeros"])
     free = O.gptq_quantize(wn, u, bits, grid, group)
     n = wn.size
     stats["band"] = follow.band_mismatch
@@ -115,7 +114,9 @@ def compare_layer(w: torch.Tensor, x: torch.Tensor, bits, group, grid, gpu: dict
     stats["scale_rel"] = float(np.max(np.abs(gpu["scales"] - follow.scales) / follow.scales))
     stats["zeros_equal"] = bool(np.array_equal(gpu["zeros"], follow.zeros))
     stats["pack_exact"] = bool(np.array_equal(gpu["qcodes"], O.pack_codes(gpu["codes"], bits)))
-    stats["obs_rel"] = float(np.max(np.abs(gpu["err_sq"] - follow.obs_loss) / np.maximum(follow.obs_loss, 1e-30)))
+    # rows with (near) zero loss, such as all-zero rows, are measured against 1e-6 of the mean row loss
+    floor = max(1e-6 * float(np.mean(follow.obs_loss)), 1e-30)
+    stats["obs_rel"] = float(np.max(np.abs(gpu["err_sq"] - follow.obs_loss) / np.maximum(follow.obs_loss, floor)))
     stats["oracle_s"] = time.time() - t0
     say(f"[parity] {label}: " + ", ".join(f"{k}={v}" for k, v in stats.items() if k != "label"))
     return stats
@@ -196,7 +197,7 @@ def compare_layer_ordered(w: torch.Tensor, x: torch.Tensor, bits, group, grid, s
     uu = np.triu(u)
     stats["u_rel"] = float(np.linalg.norm(np.triu(gpu["U"]) - uu) / np.linalg.norm(uu))
     stats["u_lower_zero"] = bool(np.all(np.tril(gpu["U"], -1) == 0))
-    fz = gpu["zeros"] if group else None
+    fz = gpu["zeros"]
     follow, g_idx = O.gptq_quantize_ordered(wn, u, perm, bits, grid, group, static_groups,
                                             follow_codes=gpu["codes"], follow_zeros=fz)
     free, _ = O.gptq_quantize_ordered(wn, u, perm, bits, grid, group, static_groups)
@@ -221,7 +222,9 @@ def compare_layer_ordered(w: torch.Tensor, x: torch.Tensor, bits, group, grid, s
     stats["scale_rel"] = float(np.max(np.abs(gpu["scales"] - follow.scales) / follow.scales))
     stats["zeros_equal"] = bool(np.array_equal(gpu["zeros"], follow.zeros))
     stats["pack_exact"] = bool(np.array_equal(gpu["qcodes"], O.pack_codes(gpu["codes"], bits)))
-    stats["obs_rel"] = float(np.max(np.abs(gpu["err_sq"] - follow.obs_loss) / np.maximum(follow.obs_loss, 1e-30)))
+    # rows with (near) zero loss, such as all-zero rows, are measured against 1e-6 of the mean row loss
+    floor = max(1e-6 * float(np.mean(follow.obs_loss)), 1e-30)
+    stats["obs_rel"] = float(np.max(np.abs(gpu["err_sq"] - follow.obs_loss) / np.maximum(follow.obs_loss, floor)))
     stats["oracle_s"] = time.time() - t0
     say(f"[parity] {label}: " + ", ".join(f"{k}={v}" for k, v in stats.items() if k != "label"))
     return stats

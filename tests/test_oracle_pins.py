@@ -361,3 +361,27 @@ def test_pack_round_trip(bits):
     d = 64 if bits != 3 else 96
     codes = RNG.integers(0, 1 << bits, size=(7, d))
     np.testing.assert_array_equal(O.unpack_codes(O.pack_codes(codes, bits), bits, d), codes)
+
+
+@pytest.mark.parametrize("group", [0, 8])
+def test_zero_point_follow_at_the_all_zero_tie(group):
+    """An all-zero row (or group) takes the grid (-1, +1): -lo/s = maxq/2
+    exactly, a half-integer, which finite precision rounds either way. Follow
+    mode takes the other neighbour as a band mismatch (judged with the lo the
+    fit uses, -1, not the raw 0), and a zero point two steps away as hard."""
+    m, d, bits = 3, 16, 4
+    w = RNG.standard_normal((m, d)) * 0.1
+    w[1] = 0.0
+    u = np.eye(d)
+    base = O.gptq_quantize(w, u, bits, "asym", group, block=8)
+    assert base.zeros[1, 0] in (7, 8)
+    other = base.zeros.copy()
+    other[1, :] = 15 - base.zeros[1, :]
+    res = O.gptq_quantize(w, u, bits, "asym", group, block=8, follow_codes=base.codes, follow_zeros=other)
+    ng = other.shape[1]
+    assert (res.zero_band_mismatch, res.zero_hard_mismatch) == (ng, 0)
+    assert np.all(res.zeros[1] == other[1])
+    far = base.zeros.copy()
+    far[0, 0] += 2
+    res2 = O.gptq_quantize(w, u, bits, "asym", group, block=8, follow_zeros=far)
+    assert res2.zero_hard_mismatch == 1
