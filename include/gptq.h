@@ -47,7 +47,7 @@ typedef enum {
   GPTQ_ERR_UNSUPPORTED = 4
 } gptq_status_t;
 
-typedef enum { GPTQ_GRID_ASYM_MINMAX = 0, GPTQ_GRID_TERNARY = 1 } gptq_grid_t;
+typedef enum { GPTQ_GRID_ASYM_MINMAX = 0, GPTQ_GRID_TERNARY = 1, GPTQ_GRID_SYM_MINMAX = 2 } gptq_grid_t;
 
 typedef enum { GPTQ_F16 = 0, GPTQ_F32 = 1, GPTQ_F64 = 2 } gptq_dtype_t;
 
@@ -56,9 +56,11 @@ typedef enum { GPTQ_F16 = 0, GPTQ_F32 = 1, GPTQ_F64 = 2 } gptq_dtype_t;
  *  grid       gptq_grid_t. Asymmetric min-max: lo = min(min v, 0),
  *             hi = max(max v, 0) (both 0 -> -1, +1), s = (hi - lo) / (2^b - 1),
  *             z = rint(-lo / s). Ternary: s = max|v| (0 -> 1), z = 1.
+ *             Symmetric min-max: a = max|v| (0 -> 1), s = 2a / (2^b - 1),
+ *             z = 2^(b-1) (code z is exactly 0).
  *             The pages only name "3/4-bit grids", grouping, 2-bit and ternary
- *             levels (nubint review, "Key findings"); this fit is the reading
- *             the library implements.
+ *             levels and compatibility with various grids (nubint review, "Key
+ *             findings"); these fits are the readings the library implements.
  *  group_size 0 = one grid per output row, fitted on the original row;
  *             32, 64 or 128 = a grid per group of columns, fitted at the group's
  *             first column on the current (error-updated) weights;

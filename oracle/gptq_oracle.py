@@ -52,6 +52,7 @@ import numpy as np
 
 GRID_ASYM = "asym"
 GRID_TERNARY = "ternary"
+GRID_SYM = "sym"
 
 
 # ---------------------------------------------------------------------------
@@ -157,8 +158,11 @@ def fit_grid(v, bits: int, grid: str):
     asym: lo = min(min v, 0), hi = max(max v, 0); lo = hi = 0 -> (-1, +1);
           s = (hi - lo) / maxq; z = rint(-lo / s).
     ternary: a = max|v| (0 -> 1); s = a; z = 1; maxq = 2 (levels -s, 0, +s).
+    sym: a = max|v| (0 -> 1); s = 2a / maxq; z = (maxq + 1) / 2, the integer
+         just above the midpoint of the codes, so that code z is exactly 0.
     [NUB] "Key findings": quantization down to 2-bit or ternary levels, with
-    grouping; [FDE] figure step 1: round to the 3/4-bit grid.
+    grouping, and compatibility with various grids; [FDE] figure step 1: round
+    to the 3/4-bit grid.
     """
     v = np.asarray(v, dtype=np.float64)
     maxq = maxq_of(bits, grid)
@@ -166,6 +170,10 @@ def fit_grid(v, bits: int, grid: str):
         a = np.max(np.abs(v), axis=1)
         a = np.where(a == 0.0, 1.0, a)
         return a, np.ones(v.shape[0], dtype=np.int64), maxq
+    if grid == GRID_SYM:
+        a = np.max(np.abs(v), axis=1)
+        a = np.where(a == 0.0, 1.0, a)
+        return 2.0 * a / maxq, np.full(v.shape[0], (maxq + 1) // 2, dtype=np.int64), maxq
     if grid != GRID_ASYM:
         raise ValueError(f"unknown grid {grid!r}")
     lo = np.minimum(np.min(v, axis=1), 0.0)

@@ -15,7 +15,7 @@ namespace {
 
 bool valid_qcfg(const gptq_qcfg_t& c, int64_t d) {
   if (c.block_size != 128) return false;
-  if (c.grid != GPTQ_GRID_ASYM_MINMAX && c.grid != GPTQ_GRID_TERNARY) return false;
+  if (c.grid != GPTQ_GRID_ASYM_MINMAX && c.grid != GPTQ_GRID_TERNARY && c.grid != GPTQ_GRID_SYM_MINMAX) return false;
   if (c.grid == GPTQ_GRID_TERNARY && c.bits != 2) return false;
   if (c.bits != 2 && c.bits != 3 && c.bits != 4 && c.bits != 8) return false;
   const int g = c.group_size;

@@ -113,13 +113,21 @@ struct GridFit {
 
 // Asymmetric min-max: lo = min(v, 0), hi = max(v, 0) (both 0 -> -1, 1),
 // s = (hi - lo) / maxq, z = rint(-lo / s). Ternary: s = max|v| (0 -> 1), z = 1.
-__device__ inline GridFit fit_grid(float vmin, float vmax, int ternary, float maxq) {
+// Symmetric: a = max|v| (0 -> 1), s = 2a / maxq, z = (maxq + 1) / 2.
+__device__ inline GridFit fit_grid(float vmin, float vmax, int gmode, float maxq) {
   float lo = fminf(vmin, 0.0f), hi = fmaxf(vmax, 0.0f);
   GridFit g;
-  if (ternary) {
+  if (gmode == GPTQ_GRID_TERNARY) {
     float amax = fmaxf(-lo, hi);
     g.s = amax == 0.0f ? 1.0f : amax;
     g.z = 1.0f;
+    return g;
+  }
+  if (gmode == GPTQ_GRID_SYM_MINMAX) {
+    float amax = fmaxf(-lo, hi);
+    if (amax == 0.0f) amax = 1.0f;
+    g.s = 2.0f * amax / maxq;
+    g.z = 0.5f * (maxq + 1.0f);
     return g;
   }
   if (lo == 0.0f && hi == 0.0f) {
@@ -136,7 +144,7 @@ __device__ inline GridFit fit_grid(float vmin, float vmax, int ternary, float ma
 // With perm set, column j of the copy is column perm[j] of W (entries outside
 // [0, d) read column 0).
 __global__ __launch_bounds__(256) void prep_kernel(const void* W, int w_f32, int64_t m, int64_t d, int64_t ldw,
-                                                   const int32_t* perm, float* Wk, int per_row, int ternary,
+                                                   const int32_t* perm, float* Wk, int per_row, int gmode,
                                                    float maxq, float* scales, uint8_t* zeros) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -178,7 +186,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* W, int w_f32, int
     vmax = fmaxf(vmax, __shfl_xor(vmax, off));
   }
   if (lane == 0) {
-    GridFit g = fit_grid(vmin, vmax, ternary, maxq);
+    GridFit g = fit_grid(vmin, vmax, gmode, maxq);
     scales[r] = g.s;
     zeros[r] = (uint8_t)g.z;
   }
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* W, int w_f32, int
 // per row it also fits that grid on the gathered values.
 template <typename T, int CAPB>
 __global__ __launch_bounds__(256) void prep_gather_kernel(const T* W, int64_t m, int64_t d, int64_t ldw,
-                                                          const int32_t* perm, float* Wk, int per_row, int ternary,
+                                                          const int32_t* perm, float* Wk, int per_row, int gmode,
                                                           float maxq, float* scales, uint8_t* zeros, int vec) {
   __shared__ __attribute__((aligned(16))) T row[CAPB / sizeof(T)];
   __shared__ float red[2][4];
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(256) void prep_gather_kernel(const T* W, int64_t m,
   if (tid == 0) {
     vmin = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
     vmax = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-    GridFit g = fit_grid(vmin, vmax, ternary, maxq);
+    GridFit g = fit_grid(vmin, vmax, gmode, maxq);
     scales[r] = g.s;
     zeros[r] = (uint8_t)g.z;
   }
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(256) void prep_gather_kernel(const T* W, int64_t m,
 // Static groups: the grid of every natural group of `group` columns, fitted on
 // the original weights before the column loop. One wave per row.
 __global__ __launch_bounds__(256) void static_fit_kernel(const void* W, int w_f32, int64_t m, int64_t d, int64_t ldw,
-                                                         int group, int ternary, float maxq, float* scales,
+                                                         int group, int gmode, float maxq, float* scales,
                                                          uint8_t* zeros) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -255,7 +263,7 @@ __global__ __launch_bounds__(256) void static_fit_kernel(const void* W, int w_f3
       vmax = fmaxf(vmax, __shfl_xor(vmax, off));
     }
     if (lane == 0) {
-      GridFit g = fit_grid(vmin, vmax, ternary, maxq);
+      GridFit g = fit_grid(vmin, vmax, gmode, maxq);
       scales[r * ng + k] = g.s;
       zeros[r * ng + k] = (uint8_t)g.z;
     }
@@ -291,7 +299,7 @@ struct ColArgs {
   const float* rdiag;
   int64_t ldu, m, d, j0;
   int bw;          // block width (multiple of 32, <= 128)
-  int ternary;
+  int gmode;
   float maxq;
   int group;       // runtime group size (used when G < 0)
   int ngroups;
@@ -385,7 +393,7 @@ __device__ __forceinline__ void col_step(LaneState& st, const ColArgs& a, int64_
       lo = fminf(lo, quad_xor2(lo));
       hi = fmaxf(hi, quad_xor2(hi));
     }
-    GridFit gf = fit_grid(lo, hi, a.ternary, a.maxq);
+    GridFit gf = fit_grid(lo, hi, a.gmode, a.maxq);
     if (g == O) {
       const int64_t gi = (a.j0 + I) / (G > 0 ? G : 1);
       a.scales[r * a.ngroups + gi] = gf.s;
@@ -510,7 +518,7 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
       vmax = fmaxf(vmax, quad_xor1(vmax));
       vmin = fminf(vmin, quad_xor2(vmin));
       vmax = fmaxf(vmax, quad_xor2(vmax));
-      GridFit gf = fit_grid(vmin, vmax, a.ternary, a.maxq);
+      GridFit gf = fit_grid(vmin, vmax, a.gmode, a.maxq);
       if (g == 0 && live) {
         a.scales[r * a.ngroups + gi] = gf.s;
         a.zeros[r * a.ngroups + gi] = (uint8_t)gf.z;
@@ -766,8 +774,8 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   const size_t need = quant_ws_total(m, d, cfg.group_size, u_f64);
   if (ws == nullptr || ws_bytes < need) return GPTQ_ERR_WORKSPACE;
   QuantWs w = quant_ws(ws, m, d, cfg.group_size, u_f64);
-  const int ternary = cfg.grid == GPTQ_GRID_TERNARY;
-  const float maxq = ternary ? 2.0f : (float)((1 << cfg.bits) - 1);
+  const int gmode = cfg.grid;
+  const float maxq = gmode == GPTQ_GRID_TERNARY ? 2.0f : (float)((1 << cfg.bits) - 1);
   const int group = cfg.group_size;
   const int ngroups = group ? (int)(d / group) : 1;
   const bool stat = perm && static_groups && group > 0;
@@ -778,7 +786,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   }
   if (stat) {
     hipLaunchKernelGGL(static_fit_kernel, dim3((unsigned)ceil_div(m, 4)), dim3(256), 0, st, W, w_f32, m, d, ldw,
-                       group, ternary, maxq, scales, zeros);
+                       group, gmode, maxq, scales, zeros);
     GPTQ_CHECK_LAUNCH();
   }
 
@@ -810,7 +818,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
     const int pr = group == 0 ? 1 : 0;
     const dim3 g((unsigned)m), b(256);
 #define GPTQ_GATHER(T, CAPB) \
-  hipLaunchKernelGGL((prep_gather_kernel<T, CAPB>), g, b, 0, st, (const T*)W, m, d, ldw, perm, w.Wk, pr, ternary, \
+  hipLaunchKernelGGL((prep_gather_kernel<T, CAPB>), g, b, 0, st, (const T*)W, m, d, ldw, perm, w.Wk, pr, gmode, \
                      maxq, scales, zeros, vec)
     if (w_f32) {
       if (row_bytes <= 8192) GPTQ_GATHER(float, 8192);
@@ -826,7 +834,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
 #undef GPTQ_GATHER
   } else {
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)ceil_div(m, 4)), dim3(256), 0, st, W, w_f32, m, d, ldw, perm,
-                       w.Wk, group == 0 ? 1 : 0, ternary, maxq, scales, zeros);
+                       w.Wk, group == 0 ? 1 : 0, gmode, maxq, scales, zeros);
   }
   GPTQ_CHECK_LAUNCH();
 
@@ -837,7 +845,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   a.ldu = ldu32;
   a.m = m;
   a.d = d;
-  a.ternary = ternary;
+  a.gmode = gmode;
   a.maxq = maxq;
   a.group = group;
   a.ngroups = ngroups;

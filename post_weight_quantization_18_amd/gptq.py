@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libgptq_mi355x.so")
 
 GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP, GPTQ_ERR_UNSUPPORTED = range(5)
 GPTQ_F16, GPTQ_F32, GPTQ_F64 = 0, 1, 2
-GPTQ_GRID_ASYM_MINMAX, GPTQ_GRID_TERNARY = 0, 1
+GPTQ_GRID_ASYM_MINMAX, GPTQ_GRID_TERNARY, GPTQ_GRID_SYM_MINMAX = 0, 1, 2
 WS_ACCUMULATE_HESSIAN, WS_PREPARE_HINV, WS_QUANTIZE_LAYER = 0, 1, 2
 
 EXPORTED = ["gptq_abi_version", "gptq_status_string", "gptq_workspace_bytes", "gptq_accumulate_hessian",
@@ -117,7 +117,7 @@ def _rowmajor_ld(t, name):
 
 
 def make_qcfg(bits: int, group_size: int = 0, grid: str = "asym", block_size: int = 128) -> QCfg:
-    g = {"asym": GPTQ_GRID_ASYM_MINMAX, "ternary": GPTQ_GRID_TERNARY}[grid]
+    g = {"asym": GPTQ_GRID_ASYM_MINMAX, "ternary": GPTQ_GRID_TERNARY, "sym": GPTQ_GRID_SYM_MINMAX}[grid]
     return QCfg(bits, g, group_size, block_size)
 
 

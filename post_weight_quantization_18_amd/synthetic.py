@@ -47,7 +47,7 @@ class LayerConfig:
     n_tokens: int     # calibration tokens
     w_dtype: str      # "fp32" | "fp16"
     bits: int
-    grid: str         # "asym" | "ternary"
+    grid: str         # "asym" | "ternary" | "sym"
     group: int        # 0 = per output row
     block: int = 128
     damp: float = 0.01

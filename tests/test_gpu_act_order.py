@@ -103,6 +103,7 @@ CASES = [
     ("3b-g256-static", S.scaled(S.CONFIGS["opt13b-attn"], m=256, d=1024, n_tokens=8192, group=256), True),
     ("ternary-g128-static", S.scaled(S.CONFIGS["opt175b-fc1-ternary"], m=512, d=1024, n_tokens=16384), True),
     ("2b-g32-d224", S.scaled(S.CONFIGS["opt175b-fc1-2bit"], m=130, d=224, n_tokens=5000, group=32), False),
+    ("3b-sym-g128-static", S.scaled(S.CONFIGS["opt13b-attn"], m=256, d=1024, n_tokens=8192, grid="sym"), True),
 ]
 
 

@@ -170,6 +170,9 @@ _SCALED = [
     ("3b-row-d96-ragged-n", S.scaled(S.CONFIGS["opt13b-attn"], m=200, d=96, n_tokens=3000, group=0)),
     ("2b-g32-d224", S.scaled(S.CONFIGS["opt175b-fc1-2bit"], m=130, d=224, n_tokens=5000, group=32)),
     ("8b-row", S.scaled(S.CONFIGS["opt2.7b-fc1"], m=128, d=256, n_tokens=4096, bits=8)),
+    ("3b-sym-g128", S.scaled(S.CONFIGS["opt13b-attn"], m=256, d=1024, n_tokens=8192, grid="sym")),
+    ("4b-sym-row", S.scaled(S.CONFIGS["opt2.7b-fc1"], m=300, d=512, n_tokens=8192, grid="sym")),
+    ("4b-sym-g32", S.scaled(S.CONFIGS["opt2.7b-fc1"], m=200, d=512, n_tokens=8192, grid="sym", group=32)),
     # several super-blocks with a ragged last block, and groups of three blocks
     ("3b-g32-d992-ragged", S.scaled(S.CONFIGS["opt13b-attn"], m=300, d=992, n_tokens=8192, group=32)),
     ("4b-g384-d1152", S.scaled(S.CONFIGS["opt2.7b-fc1"], m=192, d=1152, n_tokens=8192, group=384)),

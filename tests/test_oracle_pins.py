@@ -140,7 +140,7 @@ def test_grid_hand_cases(golden_dir):
         assert list(r.codes[0]) == codes
         np.testing.assert_allclose(r.w_hat[0], deq, rtol=1e-14, atol=1e-15)
         n += 1
-    assert n == 5
+    assert n == 8
 
 
 def test_boundary_distance():
@@ -161,7 +161,8 @@ def _correlated_layer(m, d, n, seed, outlier=True):
     return w.astype(np.float64), x
 
 
-@pytest.mark.parametrize("group,grid,bits", [(0, "asym", 4), (8, "asym", 3), (16, "ternary", 2), (0, "asym", 2)])
+@pytest.mark.parametrize("group,grid,bits", [(0, "asym", 4), (8, "asym", 3), (16, "ternary", 2), (0, "asym", 2),
+                                             (8, "sym", 3), (0, "sym", 4)])
 def test_rtn_reduction_when_h_is_scaled_identity(group, grid, bits):
     """XX^T = cI (Hadamard tokens): U is diagonal, nothing propagates, so GPTQ's
     codes equal round-to-nearest exactly, per row and per group."""
