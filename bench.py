@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config opt2.7b-fc1]
                     [--act-order [--static-groups]]
     python bench.py --gemv [--steps K] [--warmup W]
+    python bench.py --block [--steps K] [--warmup W]
 
 One step = the whole hot path on one layer with W and X already resident in
 HBM: H accumulated over all of the layer's calibration tokens in one call
@@ -15,6 +16,9 @@ H into that order before the chain, and runs the column loop in that order
 --gemv times generation with the packed weights instead: one token through the
 six layers of an OPT-175B block (q, k, v, out, fc1, fc2; 3-bit, g128), each a
 dequantizing matrix-vector product that streams its packed codes from HBM.
+--block times the quantization of a whole OPT-175B block, layer by layer: q, k
+and v see the same input, so one Hessian and one factor serve all three; out,
+fc1 and fc2 each have their own (synthetic) input.
 Prints one JSON line (rank 0). The per-stage device times come from HIP events
 recorded on the stream the library launches on (torch's current stream).
 """
@@ -79,6 +83,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--act-order", action="store_true",
                    help="quantize the columns in descending H_jj (desc_act)")
+    p.add_argument("--block", action="store_true",
+                   help="time the quantization of a whole OPT-175B block (q, k, v sharing one Hessian)")
     p.add_argument("--gemv", action="store_true",
                    help="time the dequantizing matrix-vector product over an OPT-175B block instead")
     p.add_argument("--static-groups", action="store_true",
@@ -316,6 +322,104 @@ def gemv_bench(args):
     print(json.dumps(result), flush=True)
 
 
+# Sublayers of an OPT-175B block that see the same input: q, k and v read the
+# attention input; out, fc1 and fc2 read their own.
+BLOCK_GROUPS = [("attn-qkv", ["opt175b-q", "opt175b-k", "opt175b-v"]), ("attn-out", ["opt175b-out"]),
+                ("fc1", ["opt175b-fc1"]), ("fc2", ["opt175b-fc2"])]
+
+
+class BlockGroup:
+    """One input X, its Hessian and factor, and the layers quantized with them."""
+
+    def __init__(self, label, names, dev):
+        self.label = label
+        self.cfgs = [S.CONFIGS[n] for n in names]
+        c0 = self.cfgs[0]
+        d = c0.d
+        self.x = S.make_activations(c0, dev)
+        self.ws = [S.make_weights(c, dev) for c in self.cfgs]
+        self.H = torch.empty(d, d, dtype=torch.float64, device=dev)
+        self.U = torch.empty(d, d, dtype=torch.float32, device=dev)
+        self.ws_h = torch.empty(max(1, G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, d, c0.n_tokens)),
+                                dtype=torch.uint8, device=dev)
+        self.ws_c = torch.empty(G.workspace_bytes(G.WS_PREPARE_HINV, 0, d), dtype=torch.uint8, device=dev)
+        qb = max(G.workspace_bytes(G.WS_QUANTIZE_LAYER, c.m, d, 0, G.make_qcfg(c.bits, c.group, c.grid))
+                 for c in self.cfgs)
+        self.ws_q = torch.empty(qb, dtype=torch.uint8, device=dev)
+        self.outs = []
+        for c in self.cfgs:
+            ng = d // c.group if c.group else 1
+            self.outs.append({
+                "qcodes": torch.empty(c.m, d * c.bits // 32, dtype=torch.int32, device=dev),
+                "scales": torch.empty(c.m, ng, dtype=torch.float32, device=dev),
+                "zeros": torch.empty(c.m, ng, dtype=torch.uint8, device=dev),
+                "w_hat": torch.empty(c.m, d, dtype=torch.float32, device=dev),
+                "err_sq": torch.empty(c.m, dtype=torch.float32, device=dev)})
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 + len(self.cfgs))]
+
+    def step(self):
+        c0 = self.cfgs[0]
+        self.ev[0].record()
+        G.accumulate_hessian(self.H, self.x, accumulate=False, workspace=self.ws_h)
+        self.ev[1].record()
+        _, self.info, _ = G.prepare_hinv(self.H, c0.damp, U=self.U, workspace=self.ws_c)
+        self.ev[2].record()
+        for i, (c, w, o) in enumerate(zip(self.cfgs, self.ws, self.outs)):
+            G.quantize_layer(w, self.U, c.bits, c.group, c.grid, workspace=self.ws_q, out=o)
+            self.ev[3 + i].record()
+
+    def stage_ms(self):
+        st = {"hessian": self.ev[0].elapsed_time(self.ev[1]), "hinv_chain": self.ev[1].elapsed_time(self.ev[2])}
+        for i, c in enumerate(self.cfgs):
+            st["quantize " + c.name] = self.ev[2 + i].elapsed_time(self.ev[3 + i])
+        return st
+
+
+def block_bench(args):
+    dev = torch.device("cuda:0")
+    groups = []
+    for label, names in BLOCK_GROUPS:
+        _say(f"block: drawing {label} ({', '.join(names)})")
+        groups.append(BlockGroup(label, names, dev))
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        for g in groups:
+            g.step()
+        torch.cuda.synchronize()
+        _say(f"block warmup step {i + 1}/{args.warmup} done")
+    if any(int(g.info.item()) != 0 for g in groups):
+        raise RuntimeError("H + lambda I not positive definite")
+    acc = {g.label: {} for g in groups}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for g in groups:
+            g.step()
+        torch.cuda.synchronize()
+        for g in groups:
+            for k, v in g.stage_ms().items():
+                acc[g.label][k] = acc[g.label].get(k, 0.0) + v
+        _say("block timed step done")
+    wall = time.perf_counter() - t0
+    s_block = wall / args.steps
+    n_weights = sum(c.n_weights for g in groups for c in g.cfgs)
+    result = {
+        "metric": "OPT-175B block quantization time (one GPU, whole hot path for the block's six layers)",
+        "value": s_block,
+        "unit": "s/block",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(s_block * 1e3, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16 MFMA->f32/f64 (H), f64 (U), f32 (column loop, trailing GEMM)",
+        "data": "synthetic (seeded inputs and weights of the block's shapes; q, k and v share one input)",
+        "config": {"workload": "OPT-175B block: q, k, v, out 12288x12288, fc1 49152x12288, fc2 12288x49152; "
+                               "3-bit asym g128; 262144 calibration tokens per input; q/k/v share one H and U",
+                   "weights": n_weights},
+        "weights_per_s": n_weights / s_block,
+        "stages_ms": {g.label: {k: round(v / args.steps, 3) for k, v in acc[g.label].items()} for g in groups},
+        "model_projection_96_blocks_min": round(96 * s_block / 60, 2),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def gemv_cpu_baseline(layers, rows=32):
     """The oracle's dequant_matvec on `rows` rows of each block layer (the same
     packed codes), scaled by m / rows per layer."""
@@ -348,6 +452,10 @@ def main():
     if args.gemv:
         G.load_library()
         gemv_bench(args)
+        return
+    if args.block:
+        G.load_library()
+        block_bench(args)
         return
     cfg = S.CONFIGS[args.config]
     dev = torch.device("cuda:0")
