@@ -35,7 +35,13 @@ the design notes of the repository):
   matrix as 2 X X^T with X = [d, N]).
 * Damping is relative: lambda = damp * mean(diag H), added to the diagonal.
 * The grid is asymmetric min-max (range widened to include 0), with an integer
-  zero point z = rint(-lo/s); or ternary {-s, 0, +s} with s = max|v|.
+  zero point z = rint(-lo/s); or ternary {-s, 0, +s} with s = max|v|; or
+  symmetric min-max, s = 2 max|v| / maxq with z = (maxq + 1) / 2.
+* Act-order quantizes the columns in descending H_jj (ties in index order);
+  static groups keep each column on the grid of its natural group, fitted on
+  the original weights before the loop (see the act-order section).
+* Where rounding decides an integer at an exact tie (a zero point at a
+  half-integer), follow mode takes the other implementation's neighbour.
 * A per-row grid is fitted once on the original row; a per-group grid is
   fitted at the group's first column on the current, updated weights.
 * Rounding is IEEE round-half-to-even (numpy.rint).
