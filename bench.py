@@ -51,8 +51,8 @@ CHUNK_TOKENS = 262144         # the whole calibration set (128 sequences of 2048
 SYRK_TRAFFIC = {
     "config": "opt2.7b-fc1",
     "chunk_tokens": 262144,
-    "source_sha256_16": "e0adba0d794b7c74",   # syrk.hip + common.h
-    "fetch_bytes": 3037693.375 * 1024 * 2.0,
+    "source_sha256_16": "a18f5759056f6268",   # syrk.hip + common.h
+    "fetch_bytes": 3001029.0625 * 1024 * 2.0,
     "write_bytes": 56320.0 * 1024 * 1.0,
 }
 
