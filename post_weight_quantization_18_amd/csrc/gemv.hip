@@ -28,7 +28,9 @@ __device__ __forceinline__ uint32_t chunk_code(const uint32_t (&w)[BITS], int j)
 // cx = sum c_j x_j and sx = sum x_j in fp32 and adds s (cx - z sx); the lanes'
 // sums are added across the wave. The codes, scales, zero points and x of the
 // lane's next chunk are loaded before the current one is used, so that two
-// chunks per row are in flight.
+// chunks per row are in flight. The look-ahead load is unconditional (the last
+// chunk loads itself again), so that the wait before each chunk's use counts
+// only the older loads.
 template <int BITS>
 __global__ __launch_bounds__(256) void dq_gemv_kernel(const uint32_t* q, const float* scales, const uint8_t* zeros,
                                                       int64_t m, int64_t d, int group, int ngroups, const half_t* x,
@@ -65,7 +67,8 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const uint32_t* q, const f
     float sn[GV_ROWS];
     uint32_t zn[GV_ROWS];
     half8 xn[4];
-    if (k + 64 < nch) load(k + 64, wn, sn, zn, xn);
+    load(k + 64 < nch ? k + 64 : k, wn, sn, zn, xn);
+    asm volatile("" ::: "memory");  // the look-ahead loads stay ahead of this chunk's arithmetic
     float xf[32];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
@@ -81,17 +84,15 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const uint32_t* q, const f
       for (int j = 0; j < 32; ++j) cx = fmaf((float)chunk_code<BITS>(wc[rr], j), xf[j], cx);
       acc[rr] = fmaf(sc[rr], fmaf(-(float)zc[rr], sx, cx), acc[rr]);
     }
-    if (k + 64 < nch) {
 #pragma unroll
-      for (int rr = 0; rr < GV_ROWS; ++rr) {
+    for (int rr = 0; rr < GV_ROWS; ++rr) {
 #pragma unroll
-        for (int b = 0; b < BITS; ++b) wc[rr][b] = wn[rr][b];
-        sc[rr] = sn[rr];
-        zc[rr] = zn[rr];
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) xc[v] = xn[v];
+      for (int b = 0; b < BITS; ++b) wc[rr][b] = wn[rr][b];
+      sc[rr] = sn[rr];
+      zc[rr] = zn[rr];
     }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xc[v] = xn[v];
   }
 #pragma unroll
   for (int rr = 0; rr < GV_ROWS; ++rr) {
