@@ -446,8 +446,11 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding notes in the design "
+        print("bench.py measures one GPU: the library has no multi-GPU path (see the sharding notes in the design "
               "document); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.static_groups and not args.act_order:
+        print("--static-groups needs --act-order", file=sys.stderr)
         sys.exit(2)
     if args.gemv:
         G.load_library()
@@ -465,8 +468,6 @@ def main():
     x = S.make_activations(cfg, dev)
     torch.cuda.synchronize()
     _say("inputs resident; allocating buffers")
-    if args.static_groups and not args.act_order:
-        raise SystemExit("--static-groups needs --act-order")
     run = LayerRun(cfg, w, x, args.chunk_tokens, args.act_order, args.static_groups)
     for i in range(args.warmup):
         run.step()
