@@ -1,5 +1,5 @@
 """bench.py's command-line contract on the CPU: more than one GPU is refused
-with a message (this build measures one GPU), and --static-groups needs
+with a message (the benchmark measures one GPU), and --static-groups needs
 --act-order. Neither path touches a GPU."""
 
 import os
