@@ -386,3 +386,22 @@ def test_zero_point_follow_at_the_all_zero_tie(group):
     far[0, 0] += 2
     res2 = O.gptq_quantize(w, u, bits, "asym", group, block=8, follow_zeros=far)
     assert res2.zero_hard_mismatch == 1
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_symmetric_grid_properties(bits):
+    """Symmetric grid: the zero point is the integer 2^(b-1), so code z is
+    exactly 0 and 0 rounds to it; every value inside the levels' range rounds
+    to within s/2; the extreme level -z s lies within one step of -max|v|."""
+    rng = np.random.default_rng(bits)
+    v = rng.standard_normal((5, 40)) * 0.3
+    s, z, maxq = O.fit_grid(v, bits, "sym")
+    assert np.all(z == 1 << (bits - 1))
+    a = np.max(np.abs(v), axis=1)
+    np.testing.assert_allclose(s, 2 * a / maxq, rtol=1e-15)
+    r = O.rtn_quantize(np.concatenate([v, np.zeros((5, 8))], axis=1), bits, "sym", 0)
+    assert np.all(r.codes[:, 40:] == z[:, None]) and np.all(r.w_hat[:, 40:] == 0.0)
+    inside = (v >= -z[:, None] * s[:, None]) & (v <= (maxq - z)[:, None] * s[:, None])
+    err = np.abs(r.w_hat[:, :40] - v)
+    assert np.all(err[inside] <= (s[:, None] / 2 * np.ones_like(v))[inside] * (1 + 1e-12))
+    assert np.all(-z * s <= -a) and np.all(-z * s >= -a - s)
