@@ -48,8 +48,10 @@ the design notes of the repository):
 * Codes are packed LSB-first into uint32 words, row by row.
 
 Parity status of each function is stated in its docstring. The grid
-conventions (fit_grid) are "parity unpinned" against the pages: the pages never
-define the grid, so only the stated reading pins them.
+conventions (fit_grid, its asymmetric, ternary and symmetric forms), the
+act-order key (act_order_perm) and the static-group rule (static_group_grids)
+are "parity unpinned" against the pages: the pages never define them, so only
+the stated readings and the invariants the tests check pin them.
 """
 
 from __future__ import annotations
