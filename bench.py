@@ -1,6 +1,6 @@
 """Benchmark of the GPTQ layer-quantization hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config opt2.7b-fc1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config opt175b-fc2]
                     [--act-order [--static-groups]]
     python bench.py --gemv [--steps K] [--warmup W]
     python bench.py --block [--steps K] [--warmup W]
@@ -20,7 +20,13 @@ dequantizing matrix-vector product that streams its packed codes from HBM.
 and v see the same input, so one Hessian and one factor serve all three; out,
 fc1 and fc2 each have their own (synthetic) input.
 Prints one JSON line (rank 0). The per-stage device times come from HIP events
-recorded on the stream the library launches on (torch's current stream).
+recorded on the stream the library launches on (torch's current stream). The
+timed steps also run under the library's trace (gptq_trace_start / stop), which
+brackets every kernel launch with HIP events on its launch stream, so that the
+line reports the device time, launch count and roofline fraction of each kernel
+family (SYRK, trailing GEMM, fp64 chain, column loop) over the timed region.
+The default workload is the OPT-175B fc2 layer (12288 x 49152, 262144
+calibration tokens, 3-bit asymmetric g128).
 """
 
 from __future__ import annotations
@@ -41,6 +47,7 @@ from post_weight_quantization_18_amd import synthetic as S
 PEAK_FP16_TFLOPS = 2516.6     # MI355X dense fp16/bf16 MFMA, fp32 accumulate
 PEAK_FP64_TFLOPS = 78.6       # MI355X fp64 (vector and matrix)
 PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector
 CHUNK_TOKENS = 262144         # the whole calibration set (128 sequences of 2048) per accumulate call
 
 # HBM traffic of one SYRK launch (syrk_kernel) at the default workload, from two
@@ -79,7 +86,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--config", default="opt2.7b-fc1", choices=sorted(S.CONFIGS))
+    p.add_argument("--config", default="opt175b-fc2", choices=sorted(S.CONFIGS))
+    p.add_argument("--no-trace", action="store_true",
+                   help="time the steps without the per-kernel trace (no per-family breakdown)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--act-order", action="store_true",
                    help="quantize the columns in descending H_jj (desc_act)")
@@ -472,18 +481,26 @@ def main():
     for i in range(args.warmup):
         run.step()
         torch.cuda.synchronize()
-        _say(f"warmup step {i + 1}/{args.warmup} done")
+        _say(f"warmup step {i + 1}/{args.warmup} done (untraced): {run.stage_ms()}")
     torch.cuda.synchronize()
     if run.info is not None and int(run.info.item()) != 0:
         raise RuntimeError("H + lambda I not positive definite")
 
     stage_acc = {}
     syrk_calls = []
+    fam = {}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
+        if not args.no_trace:
+            G.trace_start()
         run.step(timed_chunks=True)
         torch.cuda.synchronize()
+        if not args.no_trace:
+            for k, v in G.trace_stop().items():
+                f = fam.setdefault(k, {"launches": 0, "ms": 0.0, "work": 0.0})
+                for q in f:
+                    f[q] += v[q]
         for k, v in run.stage_ms().items():
             stage_acc[k] = stage_acc.get(k, 0.0) + v
         syrk_calls += run.syrk_call_ms()
@@ -498,15 +515,58 @@ def main():
     f_syrk_call = run.chunk * d * (d + 1)                     # lower triangle of 2 X^T X per call
     f_syrk = n * d * (d + 1)
     f_chain = 2 * d ** 3 / 3                                     # Cholesky + triangular inverse
+    f_trail = m * d * max(d - 128, 0)                            # W[:, later] -= E U[blk, later], every block
+    f_loop = m * d * 128                                         # in-block updates (m d B)
     syrk_call_ms = sum(syrk_calls) / len(syrk_calls)
     syrk_tflops = f_syrk_call / (syrk_call_ms * 1e-3) / 1e12
     traffic = syrk_traffic(cfg.name, run.chunk)
-    roofline = {"bound": "mfma", "kernel": "gptq_accumulate_hessian (syrk_kernel + split-K fp64 combine)",
+    kernels = {}
+    if fam:
+        per = {k: {"launches": v["launches"] / args.steps, "ms": v["ms"] / args.steps, "work": v["work"] / args.steps}
+               for k, v in fam.items()}
+
+        def frac(flops, ms, peak):
+            return None if not ms else round(flops / (ms * 1e-3) / 1e12 / peak, 4)
+        sy = per.get("syrk", {"launches": 0, "ms": 0.0, "work": 0.0})
+        tg = per.get("tgemm", {"launches": 0, "ms": 0.0, "work": 0.0})
+        chain_ms = sum(v["ms"] for k, v in per.items() if k.startswith("chain_"))
+        cl = per.get("colloop", {"launches": 0, "ms": 0.0, "work": 0.0})
+        # per launch of the SYRK: the tokens of one launch (the library cuts long calls into launches)
+        sy_tokens = n / sy["launches"] if sy["launches"] else 0
+        kernels = {
+            "syrk_kernel": {"bound": "mfma fp16", "launches": sy["launches"], "ms": round(sy["ms"], 3),
+                            "avg_ms": round(sy["ms"] / max(sy["launches"], 1), 4),
+                            "algorithmic_tflops": round(f_syrk / (sy["ms"] * 1e-3) / 1e12, 2) if sy["ms"] else None,
+                            "frac_algorithmic": frac(f_syrk, sy["ms"], PEAK_FP16_TFLOPS),
+                            "frac_executed": frac(sy["work"], sy["ms"], PEAK_FP16_TFLOPS),
+                            "tokens_per_launch": sy_tokens},
+            "tgemm_kernel": {"bound": "mfma fp16 (three split-fp16 passes)", "launches": tg["launches"],
+                             "ms": round(tg["ms"], 3),
+                             "algorithmic_tflops": round(f_trail / (tg["ms"] * 1e-3) / 1e12, 2) if tg["ms"] else None,
+                             "frac_algorithmic": frac(f_trail, tg["ms"], PEAK_FP16_TFLOPS),
+                             "frac_executed": frac(tg["work"], tg["ms"], PEAK_FP16_TFLOPS)},
+            "chain_fp64": {"bound": "mfma fp64", "ms": round(chain_ms, 3),
+                           "launches": sum(v["launches"] for k, v in per.items() if k.startswith("chain_")),
+                           "flops": "2 d^3 / 3 (Cholesky + triangular inverse)",
+                           "frac": frac(f_chain, chain_ms, PEAK_FP64_TFLOPS),
+                           "by_family_ms": {k: round(v["ms"], 3) for k, v in per.items() if k.startswith("chain_")}},
+            "colloop_kernel": {"bound": "alu fp32 / LDS (d dependent steps)", "launches": cl["launches"],
+                               "ms": round(cl["ms"], 3),
+                               "frac_fp32_vector": frac(f_loop, cl["ms"], PEAK_FP32_VECTOR_TFLOPS)},
+            "other_ms": {k: round(v["ms"], 3) for k, v in per.items()
+                         if k not in ("syrk", "tgemm", "colloop") and not k.startswith("chain_")},
+        }
+        if sy["launches"]:
+            # the roofline is taken per launch of the SYRK kernel itself (the split-K combine is listed apart)
+            syrk_call_ms = sy["ms"] / sy["launches"]
+            f_syrk_call = sy_tokens * d * (d + 1)
+            syrk_tflops = f_syrk_call / (syrk_call_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "syrk_kernel (Hessian SYRK, fp16 MFMA, fp32 accumulate)",
                 "achieved": round(syrk_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(syrk_tflops / PEAK_FP16_TFLOPS, 4),
                 "traffic": None if traffic is None else round(traffic),
                 "traffic_unit": "HBM bytes per syrk_kernel launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-                "per_launch": {"flops": f_syrk_call, "tokens": run.chunk, "avg_ms": round(syrk_call_ms, 4)}}
+                "per_launch": {"flops": f_syrk_call, "avg_ms": round(syrk_call_ms, 4)}}
     result = {
         "metric": "GPTQ layer quantize throughput (weights quantized per second, whole hot path)",
         "value": cfg.n_weights / (ms_per_step * 1e-3),
@@ -518,17 +578,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA->f32/f64 (H), f64 (U), f32 (column loop, trailing GEMM)",
+        "dtype": "f16 MFMA->f32/f64 (H), f64 (U), f32 (column loop), split-f16 MFMA->f32 (trailing GEMM)",
         "data": "synthetic (seeded correlated-Gaussian X with outlier channels, N(0,0.02^2) W with outlier columns)",
         "config": {"workload": f"{cfg.name}: W {m}x{d} {cfg.w_dtype}, X {n}x{d} fp16, {cfg.bits}-bit {cfg.grid} "
                                f"{'per-row' if cfg.group == 0 else 'g' + str(cfg.group)}, block 128, damp {cfg.damp}"
                                + (", act-order" + (" + static groups" if args.static_groups else "")
                                   if args.act_order else ""),
                    "chunk_tokens": run.chunk, "m": m, "d": d, "n_tokens": n},
+        "layer_time_s": round(ms_per_step * 1e-3, 4),
         "stages_ms": {k: round(v, 4) for k, v in stage.items()},
         "mfma_frac": {"syrk_fp16": round(f_syrk / (stage["hessian"] * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
                       "chain_fp64": round(f_chain / (stage["hinv_chain"] * 1e-3) / 1e12 / PEAK_FP64_TFLOPS, 4)},
         "roofline": roofline,
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         _say("timing the oracle on a bounded sample (cpu_baseline)")

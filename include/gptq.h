@@ -224,6 +224,30 @@ gptq_status_t gptq_dequant_gemv(const uint32_t* qcodes, const float* scales, con
 gptq_status_t gptq_pack_codes(const uint8_t* codes, int64_t m, int64_t d, int32_t bits,
                               uint32_t* out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Tracing (instrumentation, not a step of the method): device time per kernel
+ * family. While a trace is active on the calling host thread, every kernel the
+ * library launches from that thread is bracketed by two HIP events recorded on
+ * the stream it is launched on, and the launch's executed work is noted
+ * (floating-point operations the matrix cores execute, padding included, for
+ * the SYRK and the trailing GEMM; 0 for the others).
+ * gptq_trace_start: begins a trace on this thread (GPTQ_ERR_INVALID_ARG if one
+ *           is active). Events are created on first use and kept for reuse.
+ * gptq_trace_stop: ends it, waits for the last recorded event, and writes, for
+ *           the families k < n, launches[k], ms[k] (summed event durations) and
+ *           work[k] (any pointer may be NULL). Returns GPTQ_ERR_HIP when an
+ *           event could not be created, recorded or read.
+ * gptq_trace_family: the name of family k (static storage). */
+enum {
+  GPTQ_TRACE_SYRK = 0, GPTQ_TRACE_SYRK_REDUCE = 1, GPTQ_TRACE_CHAIN_LOAD = 2, GPTQ_TRACE_CHAIN_PANEL = 3,
+  GPTQ_TRACE_CHAIN_UPDATE = 4, GPTQ_TRACE_CHAIN_MERGE = 5, GPTQ_TRACE_CHAIN_STORE = 6, GPTQ_TRACE_QUANT_PREP = 7,
+  GPTQ_TRACE_COLLOOP = 8, GPTQ_TRACE_ESPLIT = 9, GPTQ_TRACE_TGEMM = 10, GPTQ_TRACE_PACK = 11,
+  GPTQ_TRACE_ORDER = 12, GPTQ_TRACE_GEMV = 13, GPTQ_TRACE_FAMILIES = 14
+};
+int32_t gptq_trace_start(void);
+int32_t gptq_trace_stop(int64_t* launches, double* ms, double* work, int32_t n);
+const char* gptq_trace_family(int32_t k);
+
 #ifdef __cplusplus
 }
 #endif

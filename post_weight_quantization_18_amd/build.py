@@ -19,12 +19,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgptq_mi355x.so")
-SOURCES = ["gptq_api.hip", "syrk.hip", "chain.hip", "quant.hip", "trail.hip", "order.hip", "gemv.hip"]
+SOURCES = ["gptq_api.hip", "syrk.hip", "chain.hip", "quant.hip", "trail.hip", "order.hip", "gemv.hip", "trace.hip",
+           "colloop_row.hip", "colloop_g32.hip", "colloop_g64.hip", "colloop_g128.hip", "colloop_wide.hip",
+           "colloop_static.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
+         "-Wno-unused-result", "-Werror=inline-asm", "-I", os.path.join(ROOT, "include")]
 
 
 def _run(cmd):

@@ -724,12 +724,15 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
                             hipStream_t st) {
   (void)ws_bytes;
   ChainWs w = chain_ws(ws, d);
+  {
+  TraceScope tr(st, GPTQ_TRACE_CHAIN_LOAD);
   hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(256), 0, st, H, h_f64, d, ldh, damp, w.lam, lambda_out, info);
   GPTQ_CHECK_LAUNCH();
   const int64_t nt32 = ceil_div(d, 32);
   hipLaunchKernelGGL(load_reversed_kernel, dim3((unsigned)nt32, (unsigned)nt32), dim3(256), 0, st, H, h_f64, d,
                      ldh, (const double*)w.lam, w.A);
   GPTQ_CHECK_LAUNCH();
+  }
   // Blocked right-looking Cholesky in two levels: NB-wide panels are factored
   // (panel_kernel) inside outer panels of CP columns, each NB panel updating
   // only the rest of its outer panel; the trailing matrix receives one update
@@ -749,21 +752,28 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
       const int64_t prev = k0 > p0 ? k0 - NB : -1;
       const int64_t c0 = k0 + NB;
       const int64_t nupd = (prev >= 0 && c0 < pe) ? ceil_div(pe - c0, 64) * ceil_div(d - c0, 64) : 0;
-      hipLaunchKernelGGL(panel_kernel, dim3((unsigned)(rb + nupd)), dim3(256), 0, st, w.A, d, k0, prev, pe,
-                         (int)rb, w.Dinv, info);
-      GPTQ_CHECK_LAUNCH();
+      {
+        TraceScope tr(st, GPTQ_TRACE_CHAIN_PANEL);
+        hipLaunchKernelGGL(panel_kernel, dim3((unsigned)(rb + nupd)), dim3(256), 0, st, w.A, d, k0, prev, pe,
+                           (int)rb, w.Dinv, info);
+        GPTQ_CHECK_LAUNCH();
+      }
       if (rest <= 0) break;
     }
     if (pe < d) {
       const int64_t rb = ceil_div(d - pe, 64);
+      TraceScope tr(st, GPTQ_TRACE_CHAIN_UPDATE);
       hipLaunchKernelGGL(update_f64_kernel, dim3((unsigned)(rb * (rb + 1) / 2)), dim3(256), 0, st, w.A, d, p0,
                          pe - p0, pe, d, 1);
       GPTQ_CHECK_LAUNCH();
     }
   }
-  hipLaunchKernelGGL(put_diag_inverse_kernel, dim3((unsigned)nblk), dim3(256), 0, st, w.A, d,
-                     (const double*)w.Dinv);
-  GPTQ_CHECK_LAUNCH();
+  {
+    TraceScope tr(st, GPTQ_TRACE_CHAIN_MERGE);
+    hipLaunchKernelGGL(put_diag_inverse_kernel, dim3((unsigned)nblk), dim3(256), 0, st, w.A, d,
+                       (const double*)w.Dinv);
+    GPTQ_CHECK_LAUNCH();
+  }
   const int64_t ldt = chain_smax(d);
   for (int64_t s = NB; s < d; s *= 2) {
     const int64_t pairs = ceil_div(d, 2 * s);
@@ -776,6 +786,7 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
       const int64_t c0 = pr * 2 * s + s, c1 = pr * 2 * s + 2 * s < d ? pr * 2 * s + 2 * s : d;
       if (c0 < d) active += (s / 64) * ceil_div(c1 - c0, 64);
     }
+    TraceScope tr(st, GPTQ_TRACE_CHAIN_MERGE);
     if (active < 512) {
       hipLaunchKernelGGL((merge_kernel<0, 2>), grid, dim3(512), 0, st, w.A, d, w.T, ldt, s);
       GPTQ_CHECK_LAUNCH();
@@ -788,6 +799,7 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
       GPTQ_CHECK_LAUNCH();
     }
   }
+  TraceScope tr(st, GPTQ_TRACE_CHAIN_STORE);
   hipLaunchKernelGGL(store_u_kernel, dim3((unsigned)ceil_div(d, 256) < 64 ? (unsigned)ceil_div(d, 256) : 64u,
                                           (unsigned)d),
                      dim3(256), 0, st, (const double*)w.A, d, U, u_f64, ldu);

@@ -40,12 +40,22 @@ __device__ inline int xcd_logical_block(int id, int nblocks) {
 // gfx950 direct global -> LDS DMA of 16 bytes per lane: lane l writes LDS bytes
 // [lds_off + 16 l, lds_off + 16 l + 16) (lds_off wave-uniform). Issued through
 // asm so that the compiler does not insert its conservative "wait for every LDS
-// DMA" before unrelated LDS reads; callers wait on vmcnt themselves. The
-// instruction has no register result, and M0 is set and consumed inside the
-// same asm block.
+// access" (lgkmcnt(0)) around the DMA, which the compiler-managed builtin
+// brings into the stage loops; callers wait on vmcnt themselves. The
+// instruction takes its LDS base from M0 when it issues: the asm saves M0 in a
+// scratch SGPR, sets it, issues the load and restores it, so M0 holds the
+// compiler's value again when the asm ends.
 __device__ inline void dma16(const void* src, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(src)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_off), "v"(src)
+      : "memory");
 }
 
 // Workgroup barrier after this wave's LDS accesses completed; the asm keeps the
@@ -56,6 +66,22 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 constexpr int WAIT_VM0 = 0x0F70;
 constexpr int WAIT_VM4 = 0x0F74;
 constexpr int WAIT_VM6 = 0x0F76;
+
+// Brackets the launches made in its scope with trace events when a trace is
+// active on this thread (gptq_trace_start); `work` is the launch's executed
+// matrix-core flops (0 when not counted).
+class TraceScope {
+ public:
+  TraceScope(hipStream_t st, int family, double work = 0.0);
+  ~TraceScope() { end(); }
+  void end();  // records the closing event now (once)
+  TraceScope(const TraceScope&) = delete;
+  TraceScope& operator=(const TraceScope&) = delete;
+
+ private:
+  hipStream_t st_;
+  int idx_;
+};
 
 // Entry points of the individual kernel families (implemented in the .hip files).
 gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const half_t* X, int64_t n,

@@ -107,6 +107,7 @@ gptq_status_t launch_dq_gemv(const uint32_t* q, const float* scales, const uint8
                              int group, const half_t* x, float* y, hipStream_t st) {
   const int ngroups = group ? (int)(d / group) : 1;
   const dim3 grid((unsigned)ceil_div(m, 4 * GV_ROWS));
+  TraceScope tr(st, GPTQ_TRACE_GEMV);
   hipLaunchKernelGGL(dq_gemv_kernel<BITS>, grid, dim3(256), 0, st, q, scales, zeros, m, d, group, ngroups, x, y);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;

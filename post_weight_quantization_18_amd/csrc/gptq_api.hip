@@ -1,6 +1,8 @@
 // C ABI of the gfx950 GPTQ library: host-side validation, workspace sizing and
 // stream-ordered dispatch to the kernel families. See include/gptq.h for the
 // contract of each entry point.
+#include <atomic>
+#include <cstring>
 #include <new>
 
 #include "common.h"
@@ -13,18 +15,45 @@ using namespace gptq;
 
 namespace {
 
-bool valid_qcfg(const gptq_qcfg_t& c, int64_t d) {
-  if (c.block_size != 128) return false;
-  if (c.grid != GPTQ_GRID_ASYM_MINMAX && c.grid != GPTQ_GRID_TERNARY && c.grid != GPTQ_GRID_SYM_MINMAX) return false;
-  if (c.grid == GPTQ_GRID_TERNARY && c.bits != 2) return false;
-  if (c.bits != 2 && c.bits != 3 && c.bits != 4 && c.bits != 8) return false;
+// GPTQ_OK, GPTQ_ERR_INVALID_ARG for a malformed configuration (bits, grid,
+// block size, a group size that does not divide d), GPTQ_ERR_UNSUPPORTED for a
+// well-formed group size the kernels do not take.
+gptq_status_t check_qcfg(const gptq_qcfg_t& c, int64_t d) {
+  if (c.block_size != 128) return GPTQ_ERR_INVALID_ARG;
+  if (c.grid != GPTQ_GRID_ASYM_MINMAX && c.grid != GPTQ_GRID_TERNARY && c.grid != GPTQ_GRID_SYM_MINMAX)
+    return GPTQ_ERR_INVALID_ARG;
+  if (c.grid == GPTQ_GRID_TERNARY && c.bits != 2) return GPTQ_ERR_INVALID_ARG;
+  if (c.bits != 2 && c.bits != 3 && c.bits != 4 && c.bits != 8) return GPTQ_ERR_INVALID_ARG;
   const int g = c.group_size;
-  if (g < 0) return false;
-  if (g == 0) return true;
-  if (d % g) return false;
-  if (g == 32 || g == 64 || g == 128) return true;
-  return g % 128 == 0 && d % 128 == 0;
+  if (g < 0 || (g > 0 && d % g)) return GPTQ_ERR_INVALID_ARG;
+  if (g == 0 || g == 32 || g == 64 || g == 128) return GPTQ_OK;
+  return (g % 128 == 0 && d % 128 == 0) ? GPTQ_OK : GPTQ_ERR_UNSUPPORTED;
 }
+
+// The kernels are built for gfx950 only. The current device's architecture
+// is read once per device (hipGetDeviceProperties is slow) and cached.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+gptq_status_t check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GPTQ_ERR_HIP;
+  if (dev >= kMaxDevices) return GPTQ_ERR_UNSUPPORTED;
+  int s = g_arch_state[dev].load(std::memory_order_acquire);
+  if (s == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GPTQ_ERR_HIP;
+    s = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_state[dev].store(s, std::memory_order_release);
+  }
+  return s == 1 ? GPTQ_OK : GPTQ_ERR_UNSUPPORTED;
+}
+
+#define GPTQ_CHECK_DEVICE()                       \
+  do {                                            \
+    const gptq_status_t ds_ = check_device();     \
+    if (ds_ != GPTQ_OK) return ds_;               \
+  } while (0)
 
 gptq_qcfg_t default_qcfg() {
   gptq_qcfg_t c;
@@ -75,6 +104,7 @@ gptq_status_t gptq_accumulate_hessian(void* H, int32_t h_dtype, int64_t d, int64
   if (h_dtype != GPTQ_F32 && h_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
   if (n > 0 && (!X || ldx < d || ldx % 8 || !aligned(X, 16))) return GPTQ_ERR_INVALID_ARG;
   if (workspace && !aligned(workspace, 256)) return GPTQ_ERR_INVALID_ARG;
+  GPTQ_CHECK_DEVICE();
   return syrk_enqueue(H, h_dtype == GPTQ_F64, d, ldh, (const half_t*)X, n, ldx, accumulate != 0, workspace,
                       ws_bytes, (hipStream_t)stream);
 }
@@ -86,9 +116,9 @@ gptq_status_t gptq_prepare_hinv(const void* H, int32_t h_dtype, int64_t d, int64
   if (!(damp >= 0.0)) return GPTQ_ERR_INVALID_ARG;
   if (h_dtype != GPTQ_F32 && h_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
   if (u_dtype != GPTQ_F32 && u_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
-  if (H == U) return GPTQ_ERR_INVALID_ARG;
   if (!workspace || ws_bytes < chain_workspace_bytes(d)) return GPTQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return GPTQ_ERR_INVALID_ARG;
+  GPTQ_CHECK_DEVICE();
   return chain_enqueue(H, h_dtype == GPTQ_F64, d, ldh, damp, U, u_dtype == GPTQ_F64, ldu, info, lambda_out,
                        workspace, ws_bytes, (hipStream_t)stream);
 }
@@ -102,8 +132,9 @@ gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int
   if (w_dtype != GPTQ_F16 && w_dtype != GPTQ_F32) return GPTQ_ERR_INVALID_ARG;
   if (u_dtype != GPTQ_F32 && u_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
   if (u_dtype == GPTQ_F32 && (ldu % 4 || !aligned(U, 16))) return GPTQ_ERR_INVALID_ARG;
-  if (!valid_qcfg(*cfg, d)) return GPTQ_ERR_UNSUPPORTED;
+  if (const gptq_status_t cs = check_qcfg(*cfg, d)) return cs;
   if (!workspace || !aligned(workspace, 256)) return GPTQ_ERR_WORKSPACE;
+  GPTQ_CHECK_DEVICE();
   return quant_enqueue(W, w_dtype == GPTQ_F32, m, d, ldw, U, u_dtype == GPTQ_F64, ldu, *cfg, qcodes, scales, zeros,
                        W_hat, err_sq, workspace, ws_bytes, (hipStream_t)stream);
 }
@@ -112,6 +143,7 @@ gptq_status_t gptq_act_order(const void* H, int32_t h_dtype, int64_t d, int64_t 
   if (!H || !perm || d <= 0 || ldh < d) return GPTQ_ERR_INVALID_ARG;
   if (d > INT32_MAX) return GPTQ_ERR_INVALID_ARG;
   if (h_dtype != GPTQ_F32 && h_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
+  GPTQ_CHECK_DEVICE();
   return act_order_enqueue(H, h_dtype == GPTQ_F64, d, ldh, perm, (hipStream_t)stream);
 }
 
@@ -120,6 +152,7 @@ gptq_status_t gptq_permute_hessian(const void* H, int32_t h_dtype, int64_t d, in
   if (!H || !perm || !Hp || d <= 0 || ldh < d || ldhp < d) return GPTQ_ERR_INVALID_ARG;
   if (h_dtype != GPTQ_F32 && h_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
   if (H == Hp) return GPTQ_ERR_INVALID_ARG;
+  GPTQ_CHECK_DEVICE();
   return permute_hessian_enqueue(H, h_dtype == GPTQ_F64, d, ldh, perm, Hp, ldhp, (hipStream_t)stream);
 }
 
@@ -134,8 +167,9 @@ gptq_status_t gptq_quantize_layer_ordered(const void* W, int32_t w_dtype, int64_
   if (w_dtype != GPTQ_F16 && w_dtype != GPTQ_F32) return GPTQ_ERR_INVALID_ARG;
   if (u_dtype != GPTQ_F32 && u_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
   if (u_dtype == GPTQ_F32 && (ldu % 4 || !aligned(U, 16))) return GPTQ_ERR_INVALID_ARG;
-  if (!valid_qcfg(*cfg, d)) return GPTQ_ERR_UNSUPPORTED;
+  if (const gptq_status_t cs = check_qcfg(*cfg, d)) return cs;
   if (!workspace || !aligned(workspace, 256)) return GPTQ_ERR_WORKSPACE;
+  GPTQ_CHECK_DEVICE();
   return quant_enqueue(W, w_dtype == GPTQ_F32, m, d, ldw, U, u_dtype == GPTQ_F64, ldu, *cfg, qcodes, scales, zeros,
                        W_hat, err_sq, workspace, ws_bytes, (hipStream_t)stream, perm, static_groups, g_idx);
 }
@@ -146,6 +180,7 @@ gptq_status_t gptq_dequant_gemv(const uint32_t* qcodes, const float* scales, con
   if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_INVALID_ARG;
   if (group_size < 0 || (group_size && (group_size % 32 || d % group_size))) return GPTQ_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(qcodes, 4)) return GPTQ_ERR_INVALID_ARG;
+  GPTQ_CHECK_DEVICE();
   return dq_gemv_enqueue(qcodes, scales, zeros, m, d, bits, group_size, (const half_t*)x, y, (hipStream_t)stream);
 }
 
@@ -154,6 +189,7 @@ gptq_status_t gptq_pack_codes(const uint8_t* codes, int64_t m, int64_t d, int32_
   if (!codes || !out || m <= 0 || d <= 0) return GPTQ_ERR_INVALID_ARG;
   if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_INVALID_ARG;
   if ((d * bits) % 32) return GPTQ_ERR_INVALID_ARG;
+  GPTQ_CHECK_DEVICE();
   return pack_enqueue(codes, d, m, d, bits, out, (hipStream_t)stream);
 }
 

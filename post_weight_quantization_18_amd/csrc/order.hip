@@ -76,6 +76,7 @@ __global__ __launch_bounds__(256) void permute_h_kernel(const T* H, int64_t d, i
 }  // namespace
 
 gptq_status_t act_order_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, int32_t* perm, hipStream_t st) {
+  TraceScope tr(st, GPTQ_TRACE_ORDER);
   const dim3 grid((unsigned)ceil_div(d, 64));
   if (h_f64)
     hipLaunchKernelGGL(order_rank_kernel<double>, grid, dim3(256), 0, st, (const double*)H, d, ldh, perm);
@@ -88,6 +89,7 @@ gptq_status_t act_order_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh
 gptq_status_t permute_hessian_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, const int32_t* perm,
                                       void* Hp, int64_t ldp, hipStream_t st) {
   const dim3 grid((unsigned)(d < 16384 ? d : 16384));
+  TraceScope tr(st, GPTQ_TRACE_ORDER);
   if (h_f64)
     hipLaunchKernelGGL(permute_h_kernel<double>, grid, dim3(256), 0, st, (const double*)H, d, ldh, perm,
                        (double*)Hp, ldp);

@@ -590,6 +590,7 @@ gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const hal
   const int nt = syrk_ntiles(d);
   if (n == 0) {
     if (!accumulate) {
+      TraceScope tr(st, GPTQ_TRACE_SYRK_REDUCE);
       hipLaunchKernelGGL(syrk_zero_kernel, dim3(1024), dim3(256), 0, st, H, d, ldh, h_f64);
       GPTQ_CHECK_LAUNCH();
     }
@@ -630,8 +631,16 @@ gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const hal
   a.ldh = ldh;
   a.h_f64 = h_f64;
   a.accumulate = accumulate;
-  hipLaunchKernelGGL(syrk_kernel, dim3(p.nsplit > 0 ? p.nsplit * nt : p.dp_tiles + p.nsk), dim3(NT), 0, st, a);
-  GPTQ_CHECK_LAUNCH();
+  {
+    // executed: every non-empty tile over the launch's stages (diagonal tiles whole)
+    const int64_t T = ceil_div(d, TI), Tj = ceil_div(d, TJ);
+    int64_t live = 0;
+    for (int64_t bi = 0; bi < T; ++bi) live += (2 * bi + 2 < Tj ? 2 * bi + 2 : Tj);
+    TraceScope tr(st, GPTQ_TRACE_SYRK, 2.0 * TI * TJ * (double)(p.S * KS) * (double)live);
+    hipLaunchKernelGGL(syrk_kernel, dim3(p.nsplit > 0 ? p.nsplit * nt : p.dp_tiles + p.nsk), dim3(NT), 0, st, a);
+    GPTQ_CHECK_LAUNCH();
+  }
+  TraceScope tr_reduce(st, GPTQ_TRACE_SYRK_REDUCE);
   if (p.nsplit > 0) {
     const int64_t total = (int64_t)nt * TI * TJ;
     int blocks = (int)ceil_div(total, 256 * 4);

@@ -229,6 +229,8 @@ gptq_status_t tgemm_enqueue(const TgemmArgs& a, hipStream_t st) {
   if (a.K % KS) return GPTQ_ERR_INVALID_ARG;
   const int64_t ntm = ceil_div(a.M, TM), ntn = ceil_div(a.N, TN);
   if (ntm * ntn > 0x7fffffff) return GPTQ_ERR_UNSUPPORTED;
+  // executed: three fp16 passes over the padded tiles
+  TraceScope tr(st, GPTQ_TRACE_TGEMM, 3.0 * 2.0 * (double)(ntm * TM) * (double)(ntn * TN) * (double)a.K);
   hipLaunchKernelGGL(tgemm_kernel, dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a, (int)ntm, (int)ntn);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;

@@ -13,6 +13,7 @@ Entry points (same names as include/gptq.h):
     quantize_layer_ordered(W, U, perm, bits, group_size, grid, static_groups)
     dequant_gemv(qcodes, scales, zeros, bits, group_size, x)   y = W_hat x, one token
     pack_codes(codes, bits)
+    trace_start(), trace_stop()                device time per kernel family (instrumentation)
 and quantize(W, x_chunks, ...) which runs the stages of one layer (natural
 order, or act-order with act_order=True).
 """
@@ -34,7 +35,9 @@ WS_ACCUMULATE_HESSIAN, WS_PREPARE_HINV, WS_QUANTIZE_LAYER = 0, 1, 2
 
 EXPORTED = ["gptq_abi_version", "gptq_status_string", "gptq_workspace_bytes", "gptq_accumulate_hessian",
             "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_act_order", "gptq_permute_hessian",
-            "gptq_quantize_layer_ordered", "gptq_dequant_gemv", "gptq_pack_codes"]
+            "gptq_quantize_layer_ordered", "gptq_dequant_gemv", "gptq_pack_codes", "gptq_trace_start",
+            "gptq_trace_stop", "gptq_trace_family"]
+TRACE_FAMILIES = 14
 
 
 class QCfg(ctypes.Structure):
@@ -78,6 +81,12 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_dequant_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp]
     lib.gptq_pack_codes.restype = i32
     lib.gptq_pack_codes.argtypes = [vp, i64, i64, i32, vp, vp]
+    lib.gptq_trace_start.restype = i32
+    lib.gptq_trace_start.argtypes = []
+    lib.gptq_trace_stop.restype = i32
+    lib.gptq_trace_stop.argtypes = [vp, vp, vp, i32]
+    lib.gptq_trace_family.restype = ctypes.c_char_p
+    lib.gptq_trace_family.argtypes = [i32]
     _lib = lib
     return lib
 
@@ -293,6 +302,26 @@ def pack_codes(codes: torch.Tensor, bits: int) -> torch.Tensor:
     out = torch.empty(m, d * bits // 32, dtype=torch.int32, device=codes.device)
     _check(lib.gptq_pack_codes(_ptr(codes), m, d, bits, _ptr(out), _stream(codes.device)), "gptq_pack_codes")
     return out
+
+
+def trace_start():
+    """Start recording HIP events around every library launch from this thread."""
+    _check(load_library().gptq_trace_start(), "gptq_trace_start")
+
+
+def trace_stop() -> dict:
+    """End the trace; {family: {"launches": n, "ms": summed device ms, "work": executed
+    matrix-core flops}} for the families that launched anything."""
+    lib = load_library()
+    n = TRACE_FAMILIES
+    launches = (ctypes.c_int64 * n)()
+    ms = (ctypes.c_double * n)()
+    work = (ctypes.c_double * n)()
+    _check(lib.gptq_trace_stop(ctypes.cast(launches, ctypes.c_void_p), ctypes.cast(ms, ctypes.c_void_p),
+                               ctypes.cast(work, ctypes.c_void_p), n), "gptq_trace_stop")
+    return {lib.gptq_trace_family(k).decode(): {"launches": int(launches[k]), "ms": float(ms[k]),
+                                                   "work": float(work[k])}
+            for k in range(n) if launches[k]}
 
 
 def quantize(W: torch.Tensor, x_chunks, bits: int, group_size: int = 0, grid: str = "asym", damp: float = 0.01,

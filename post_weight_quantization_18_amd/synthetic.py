@@ -24,9 +24,16 @@ Recipe (all seeds derive from (config, layer, stream, chunk)):
   Haar blocks of 4096, P1, P2 random permutations. The spectrum s is the same,
   so the conditioning of H is too; only the mixing pattern is structured.
 
-Small configurations are drawn on the CPU (fp64, torch's CPU generator);
-large ones on the GPU (fp32 GEMM), which is fast and deterministic for a given
-device type. Either way the same fp16 X goes to both sides of a parity test.
+The orthogonal factors (Q, or the Haar blocks of the structured Q) are
+always drawn on the CPU in fp64 (torch's CPU generator and LAPACK QR), whatever
+the device, so they do not depend on the GPU or its solver libraries. Small
+configurations then form X on the CPU in fp64; large ones form it on the GPU
+(Q cast to fp32, fp32 GEMM per sequence), which is fast and deterministic for a
+given device type. Either way the same fp16 X goes to both sides of a parity
+test.
+
+The two grids of the extreme regime (2-bit and ternary on the OPT-175B fc1
+shape) quantize one layer: they share W and X (the same seeds).
 """
 
 from __future__ import annotations
@@ -81,7 +88,7 @@ CONFIGS = {
     "opt175b-fc2": _cfg("opt175b-fc2", 12288, 49152, _N, "fp16", 3, "asym", 128, 4, 5),
     # extreme regime on the OPT-175B fc1 shape
     "opt175b-fc1-2bit": _cfg("opt175b-fc1-2bit", 49152, 12288, _N, "fp16", 2, "asym", 128, 5, 0),
-    "opt175b-fc1-ternary": _cfg("opt175b-fc1-ternary", 49152, 12288, _N, "fp16", 2, "ternary", 128, 5, 1),
+    "opt175b-fc1-ternary": _cfg("opt175b-fc1-ternary", 49152, 12288, _N, "fp16", 2, "ternary", 128, 5, 0),
 }
 
 OPT175B_BLOCK = ["opt175b-q", "opt175b-k", "opt175b-v", "opt175b-out", "opt175b-fc1", "opt175b-fc2"]
@@ -123,9 +130,13 @@ BLOCK_Q = 4096
 
 
 def _haar(n, gen, dev, work):
-    g = torch.randn(n, n, generator=gen, device=dev, dtype=work)
+    """Haar-distributed orthogonal n x n matrix: QR of an fp64 Gaussian drawn
+    with the CPU generator `gen`, columns sign-fixed by diag(R); computed on
+    the CPU, then moved to `dev` in `work` precision."""
+    g = torch.randn(n, n, generator=gen, dtype=torch.float64)
     q, r = torch.linalg.qr(g)
-    return q * torch.sign(torch.diagonal(r)).unsqueeze(0)
+    q = q * torch.sign(torch.diagonal(r)).unsqueeze(0)
+    return q.to(device=dev, dtype=work)
 
 
 def _spectrum(d, dev, work):
@@ -146,7 +157,7 @@ def mixing_matrix(cfg: LayerConfig, device="cpu") -> torch.Tensor:
     work = torch.float64 if dev.type == "cpu" else torch.float32
     d = cfg.d
     assert d <= STRUCTURED_D, "the dense mixing matrix is only drawn up to d = 16384"
-    q = _haar(d, _gen(dev, _seed(cfg, 2)), dev, work)
+    q = _haar(d, _gen(torch.device("cpu"), _seed(cfg, 2)), dev, work)
     a = _spectrum(d, dev, work).unsqueeze(1) * q.t()
     a[:, _outlier_channels(cfg, dev)] *= 20.0
     return a.contiguous()
@@ -160,7 +171,7 @@ class _StructuredMix:
         d = cfg.d
         assert d % BLOCK_Q == 0
         nb = d // BLOCK_Q
-        gq = _gen(dev, _seed(cfg, 2))
+        gq = _gen(torch.device("cpu"), _seed(cfg, 2))
         self.b1 = torch.stack([_haar(BLOCK_Q, gq, dev, work) for _ in range(nb)])
         self.b2 = torch.stack([_haar(BLOCK_Q, gq, dev, work) for _ in range(nb)])
         gp = _gen(torch.device("cpu"), _seed(cfg, 5))

@@ -78,19 +78,20 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert lib.gptq_accumulate_hessian(fake, 0, 64, 64, fake, 10, 64, 0, None, 0, None) == G.GPTQ_ERR_INVALID_ARG
     assert lib.gptq_accumulate_hessian(fake, 2, 64, 64, _vp((1 << 20) + 2), 10, 64, 0, None, 0, None) == G.GPTQ_ERR_INVALID_ARG
     assert lib.gptq_accumulate_hessian(fake, 2, 64, 64, fake, 10, 66, 0, None, 0, None) == G.GPTQ_ERR_INVALID_ARG
-    # prepare_hinv: aliasing, negative damp, missing workspace
-    assert lib.gptq_prepare_hinv(fake, 2, 64, 64, 0.01, fake, 1, 64, fake, None, fake, 1 << 30, None) == G.GPTQ_ERR_INVALID_ARG
+    # prepare_hinv: null U, negative damp, missing workspace (U may alias H)
+    assert lib.gptq_prepare_hinv(fake, 2, 64, 64, 0.01, None, 1, 64, fake, None, fake, 1 << 30, None) == G.GPTQ_ERR_INVALID_ARG
     assert lib.gptq_prepare_hinv(fake, 2, 64, 64, -1.0, _vp(1 << 24), 1, 64, fake, None, fake, 1 << 30, None) == G.GPTQ_ERR_INVALID_ARG
     assert lib.gptq_prepare_hinv(fake, 2, 64, 64, 0.01, _vp(1 << 24), 1, 64, fake, None, None, 0, None) == G.GPTQ_ERR_WORKSPACE
     # quantize_layer: unsupported configurations
     def q(cfg, d=256, ws=fake, wsb=1 << 40):
         return lib.gptq_quantize_layer(fake, 1, 8, d, d, fake, 1, d, ctypes.byref(cfg), fake, fake, fake, None, None,
                                        ws, wsb, None)
-    assert q(G.make_qcfg(5)) == G.GPTQ_ERR_UNSUPPORTED                       # bits
-    assert q(G.make_qcfg(3, grid="ternary")) == G.GPTQ_ERR_UNSUPPORTED       # ternary needs 2 bits
-    assert q(G.make_qcfg(4, block_size=64)) == G.GPTQ_ERR_UNSUPPORTED        # block 128 only
-    assert q(G.make_qcfg(4, group_size=48)) == G.GPTQ_ERR_UNSUPPORTED        # group must divide 128 or be k*128
-    assert q(G.make_qcfg(4, group_size=384), d=512) == G.GPTQ_ERR_UNSUPPORTED  # must divide d
+    assert q(G.make_qcfg(5)) == G.GPTQ_ERR_INVALID_ARG                       # bits
+    assert q(G.make_qcfg(3, grid="ternary")) == G.GPTQ_ERR_INVALID_ARG       # ternary needs 2 bits
+    assert q(G.make_qcfg(4, block_size=64)) == G.GPTQ_ERR_INVALID_ARG        # block 128 only
+    assert q(G.make_qcfg(4, group_size=48)) == G.GPTQ_ERR_INVALID_ARG        # group must divide d
+    assert q(G.make_qcfg(4, group_size=384), d=512) == G.GPTQ_ERR_INVALID_ARG  # group must divide d
+    assert q(G.make_qcfg(4, group_size=24), d=480) == G.GPTQ_ERR_UNSUPPORTED  # not 16 nor a multiple of 32
     assert q(G.make_qcfg(4), d=200) == G.GPTQ_ERR_INVALID_ARG                # d % 32
     assert q(G.make_qcfg(4), ws=None) == G.GPTQ_ERR_WORKSPACE
     # act_order / permute_hessian: null, ldh < d, bad dtype, aliasing
@@ -106,7 +107,7 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
                                                fake, fake, None, None, None, fake, 1 << 40, None)
     assert qo(G.make_qcfg(4), perm=None) == G.GPTQ_ERR_INVALID_ARG
     assert qo(G.make_qcfg(4, group_size=128), static=2) == G.GPTQ_ERR_INVALID_ARG
-    assert qo(G.make_qcfg(5)) == G.GPTQ_ERR_UNSUPPORTED
+    assert qo(G.make_qcfg(5)) == G.GPTQ_ERR_INVALID_ARG
     assert qo(G.make_qcfg(4), d=200) == G.GPTQ_ERR_INVALID_ARG
     # dequant_gemv: d % 32, bits, group not a multiple of 32, misaligned x
     assert lib.gptq_dequant_gemv(fake, fake, fake, 4, 40, 4, 0, fake, fake, None) == G.GPTQ_ERR_INVALID_ARG

@@ -248,3 +248,28 @@ def test_layer_parity_opt27b_fc1_full():
     in the launch configuration the benchmark times (one call over all 262144
     tokens)."""
     _layer_case(S.CONFIGS["opt2.7b-fc1"], chunk_tokens=262144)
+
+
+def test_prepare_hinv_u_may_alias_h():
+    """U written over H's own buffer (the chain copies H into its workspace
+    before U is stored) equals U in a separate buffer, bit for bit, for fp64
+    and fp32 outputs."""
+    say("[case] U aliasing H")
+    cfg = S.scaled(S.CONFIGS["opt13b-attn"], m=64, d=416, n_tokens=4096)
+    x = S.make_activations(cfg).to(DEV)
+    d = cfg.d
+    H = torch.empty(d, d, dtype=torch.float64, device=DEV)
+    G.accumulate_hessian(H, x, accumulate=False)
+    for u_dtype in (torch.float64, torch.float32):
+        U_sep, info, lam = G.prepare_hinv(H, 0.01, u_dtype=u_dtype)
+        torch.cuda.synchronize()
+        assert int(info.item()) == 0
+        Hc = H.clone()
+        if u_dtype == torch.float64:
+            U_al = Hc
+        else:
+            U_al = Hc.view(torch.float32)[:, :d]  # fp32 rows over the fp64 rows, ld = 2 d
+        _, info2, lam2 = G.prepare_hinv(Hc, 0.01, U=U_al)
+        torch.cuda.synchronize()
+        assert int(info2.item()) == 0 and float(lam2.item()) == float(lam.item())
+        assert torch.equal(U_al, U_sep), u_dtype

@@ -1,11 +1,19 @@
 """Full-size layers through the C ABI, in the launch configuration the
-benchmark times (one gptq_accumulate_hessian call over all 262144 tokens).
+benchmark times (one gptq_accumulate_hessian call over all 262144 tokens, fp64
+H, fp32 U).
 
 * OPT-13B attention projection (5120 x 5120, 262144 tokens, 3-bit g128): the
-  whole oracle runs, and the usual parity gates apply.
-* OPT-175B shapes (d = 12288 and d = 49152): the oracle cannot run whole, so the
-  checks are on sampled outputs the oracle computes one by one, and on
-  properties that hold at any size:
+  whole oracle runs on every row, and the usual parity gates apply.
+* OPT-175B q (12288 x 12288), fc1 (49152 x 12288, 3-bit g128) and the extreme
+  regime on the fc1 shape (2-bit and ternary g128, one W and one X): the GPU
+  quantizes the whole layer; the oracle builds its own fp64 H from all 262144
+  tokens, damps it and factors it, then runs follow mode and a free run on
+  258 sampled rows (rows are independent given U, and every grid is fitted
+  within its row). The usual gates apply to those rows.
+* OPT-175B fc2 (12288 x 49152): the oracle's own H would cost 6.3e14 fp64
+  flops on the host, about 20 minutes on 16 cores, more than a test may take;
+  its code parity is not measured. The checks there are on sampled outputs the
+  oracle computes one by one, and on properties that hold at any size:
   - sampled entries of H against the oracle's fp64 Hessian of those columns;
   - lambda against damp * mean(diag H) (diag in fp64 from X);
   - U upper with a positive diagonal, and U^T U H_d e_j = e_j on sampled
@@ -19,6 +27,8 @@ benchmark times (one gptq_accumulate_hessian call over all 262144 tokens).
 
 from __future__ import annotations
 
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -27,7 +37,7 @@ import oracle as O
 from post_weight_quantization_18_amd import gptq as G
 from post_weight_quantization_18_amd import synthetic as S
 
-from parity_util import assert_gates, compare_layer, gpu_layer, say
+from parity_util import assert_gates, compare_layer, compare_rows, gpu_layer, oracle_factor, say
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +53,78 @@ def test_layer_parity_opt13b_attn_full():
     w, x = w.cpu(), x.cpu()
     gpu = gpu_layer(w, x, cfg.bits, cfg.group, cfg.grid, cfg.damp, chunk_tokens=CHUNK)
     assert_gates(compare_layer(w, x, cfg.bits, cfg.group, cfg.grid, gpu, cfg.damp, cfg.name))
+
+
+N_SAMPLE_ROWS = 256
+
+
+def _sample_rows(m, seed):
+    """256 distinct random rows plus the first and the last, sorted."""
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([rng.choice(m, N_SAMPLE_ROWS, replace=False), [0, m - 1]]))
+
+
+def _device_factor(cfg, x):
+    """H over all tokens in one call (fp64), then U (fp32), as the benchmark runs them."""
+    d = cfg.d
+    H = torch.empty(d, d, dtype=torch.float64, device=DEV)
+    G.accumulate_hessian(H, x, accumulate=False)
+    U, info, lam = G.prepare_hinv(H, cfg.damp, u_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    return H, U, float(lam.item())
+
+
+def _rows_of(res, rows, bits, d):
+    rt = torch.as_tensor(rows, device=DEV)
+    q = res["qcodes"][rt].cpu().numpy().view(np.uint32)
+    return {"codes": O.unpack_codes(q, bits, d), "qcodes": q,
+            "scales": res["scales"][rt].cpu().numpy(),
+            "zeros": res["zeros"][rt].cpu().numpy().astype(np.int64),
+            "w_hat": res["w_hat"][rt].cpu().numpy(),
+            "err_sq": res["err_sq"][rt].cpu().numpy()}
+
+
+_CODE_PARITY = [("opt175b-q", ["opt175b-q"]), ("opt175b-fc1", ["opt175b-fc1"]),
+                ("opt175b-fc1-extreme", ["opt175b-fc1-2bit", "opt175b-fc1-ternary"])]
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("label,names", _CODE_PARITY, ids=[c[0] for c in _CODE_PARITY])
+def test_code_parity_full_size_sampled_rows(label, names):
+    """The whole layer on the GPU; the oracle's own H, lambda and U from all
+    262144 tokens; follow mode on 258 sampled rows with every gate."""
+    cfgs = [S.CONFIGS[n] for n in names]
+    c0 = cfgs[0]
+    assert all((c.m, c.d, c.n_tokens, c.config_id, c.layer_id) == (c0.m, c0.d, c0.n_tokens, c0.config_id,
+                                                                      c0.layer_id) for c in cfgs)
+    say(f"[case] full-size code parity {label} m={c0.m} d={c0.d} n={c0.n_tokens} grids="
+        f"{[(c.bits, c.grid, c.group) for c in cfgs]}")
+    t0 = time.time()
+    w = S.make_weights(c0, DEV)
+    x = S.make_activations(c0, DEV)
+    H, U, lam = _device_factor(c0, x)
+    rows = _sample_rows(c0.m, 21)
+    gpu_rows = []
+    for c in cfgs:
+        res = G.quantize_layer(w, U, c.bits, c.group, c.grid)
+        torch.cuda.synchronize()
+        gpu_rows.append(_rows_of(res, rows, c.bits, c.d))
+        del res
+    factor = {"H": H.cpu().numpy(), "U": U.cpu().double().numpy(), "lam": lam, "u_eps": 2.0 ** -24}
+    wn = w[torch.as_tensor(rows, device=DEV)].double().cpu().numpy()
+    xh = x.cpu().numpy()
+    del H, U, x
+    torch.cuda.empty_cache()
+    say(f"[step] {label}: GPU layer(s) done in {time.time() - t0:.1f} s; oracle H over {xh.shape[0]} tokens")
+    t1 = time.time()
+    h, lam_o, u, hd = oracle_factor(xh, c0.damp)
+    del xh
+    say(f"[step] {label}: oracle H, lambda, U in {time.time() - t1:.1f} s")
+    for c, gr in zip(cfgs, gpu_rows):
+        gr.update(factor)
+        stats = compare_rows(wn, gr, h, lam_o, u, hd, c.bits, c.group, c.grid, f"{c.name} ({len(rows)} rows)")
+        assert_gates(stats)
 
 
 def _run_full(cfg):
@@ -98,7 +180,7 @@ def _row_losses(x, delta):
     return out
 
 
-_FULL = ["opt175b-q", "opt175b-fc1-ternary", "opt175b-fc2"]
+_FULL = ["opt175b-fc2"]
 
 
 @pytest.mark.timeout(1200)

@@ -405,3 +405,40 @@ def test_symmetric_grid_properties(bits):
     err = np.abs(r.w_hat[:, :40] - v)
     assert np.all(err[inside] <= (s[:, None] / 2 * np.ones_like(v))[inside] * (1 + 1e-12))
     assert np.all(-z * s <= -a) and np.all(-z * s >= -a - s)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_asymmetric_grid_properties(bits):
+    """Asymmetric min-max grid, checked by what a uniform grid over the widened
+    range [min(v, 0), max(v, 0)] must satisfy rather than by its formula: the
+    zero point is an integer code in [0, maxq] and that code is exactly 0; the
+    lowest and highest levels lie within half a step of the range's ends; every
+    value in the range rounds to within half a step; the step is the smallest
+    that covers the range with maxq + 1 levels (s maxq = range); and when both
+    ends are levels of such a grid (lo = -k t, hi = (maxq - k) t) they are
+    reproduced exactly."""
+    rng = np.random.default_rng(100 + bits)
+    v = rng.standard_normal((6, 48)) * 0.05
+    v[1] = np.abs(v[1])          # all >= 0: lo = 0
+    v[2] = -np.abs(v[2])         # all <= 0: hi = 0
+    v[3, :4] = [3.0, -0.1, 0.2, -0.4]   # a strong outlier
+    s, z, maxq = O.fit_grid(v, bits, "asym")
+    assert np.all((z >= 0) & (z <= maxq)) and z.dtype.kind == "i"
+    lo = np.minimum(v.min(axis=1), 0.0)
+    hi = np.maximum(v.max(axis=1), 0.0)
+    np.testing.assert_allclose(s * maxq, hi - lo, rtol=1e-14)
+    assert np.all(np.abs(-z * s - lo) <= s / 2 * (1 + 1e-12))
+    assert np.all(np.abs((maxq - z) * s - hi) <= s / 2 * (1 + 1e-12))
+    assert z[1] == 0 and z[2] == maxq
+    r = O.rtn_quantize(np.concatenate([v, np.zeros((6, 8))], axis=1), bits, "asym", 0)
+    assert np.all(r.codes[:, 48:] == z[:, None]) and np.all(r.w_hat[:, 48:] == 0.0)
+    err = np.abs(r.w_hat[:, :48] - v)
+    assert np.all(err <= s[:, None] / 2 * (1 + 1e-12))
+    # ends on the grid: lo = -k t, hi = (maxq - k) t with t a power of two
+    for k in (0, 1, maxq // 2, maxq - 1):
+        t = 2.0 ** -6
+        vv = np.array([[-k * t, (maxq - k) * t, 0.3 * t]])
+        s1, z1, _ = O.fit_grid(vv, bits, "asym")
+        q = O.rtn_quantize(vv, bits, "asym", 0)
+        assert s1[0] == t and z1[0] == k
+        assert q.w_hat[0, 0] == -k * t and q.w_hat[0, 1] == (maxq - k) * t
