@@ -108,6 +108,24 @@ gptq_status_t gptq_accumulate_hessian(void* H, int32_t h_dtype, int64_t d, int64
                                       const void* X, int64_t n, int64_t ldx, int32_t accumulate,
                                       void* workspace, size_t ws_bytes, void* stream);
 
+/* gptq_accumulate_hessian for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results, with the split-K partial tiles in a static device
+ * array of the library (192 MiB, one per GPU it runs on, held until the process
+ * ends) instead of a workspace. The call allocates nothing: no hipMalloc, no
+ * hipFree, no event (a trace active on the thread is paused for the call).
+ * Arguments, layout and errors as gptq_accumulate_hessian, plus
+ * GPTQ_ERR_WORKSPACE when (d, n) would need more partial tiles than the array
+ * holds (gptq_workspace_bytes(GPTQ_WS_ACCUMULATE_HESSIAN, 0, d, n, NULL) >
+ * 192 MiB; no call of up to 262144 tokens with d <= 65536 does). Every call
+ * on one GPU shares that GPU's array and leaves its contents behind; the
+ * kernels write every partial they read, so nothing needs clearing. Calls that
+ * overlap on one GPU (other streams, other host threads) race on the array:
+ * serialize them. */
+gptq_status_t gptq_accumulate_hessian_noalloc(void* H, int32_t h_dtype, int64_t d, int64_t ldh,
+                                              const void* X, int64_t n, int64_t ldx, int32_t accumulate,
+                                              void* stream);
+
 /* Inverse-Hessian factor: U (upper, row-major, zeros below the diagonal) with
  * U^T U = (H + lambda I)^-1, lambda = damp * mean(diag H).
  * FDE breakdown, figure step 2: U = chol(H^-1); section 01: the rows of the

@@ -70,6 +70,17 @@ constexpr int WAIT_VM6 = 0x0F76;
 // Brackets the launches made in its scope with trace events when a trace is
 // active on this thread (gptq_trace_start); `work` is the launch's executed
 // matrix-core flops (0 when not counted).
+// Turns the trace off on this thread for its lifetime (entry points that must
+// not create events), restoring it afterwards.
+class TracePause {
+ public:
+  TracePause();
+  ~TracePause();
+
+ private:
+  bool was_on_;
+};
+
 class TraceScope {
  public:
   TraceScope(hipStream_t st, int family, double work = 0.0);
@@ -87,6 +98,14 @@ class TraceScope {
 gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const half_t* X, int64_t n,
                            int64_t ldx, int accumulate, void* ws, size_t ws_bytes, hipStream_t st);
 size_t syrk_workspace_bytes(int64_t d, int64_t n);
+
+// Size of the SYRK's static scratch array (gptq_accumulate_hessian_noalloc):
+// 768 fp64 partial tiles of 256 x 128 (192 MiB): the most a launch's split-K
+// plan uses for any d <= 65536 over 262144 tokens (182 MiB at d = 3104..3328).
+constexpr size_t kStaticScratchBytes = (size_t)768 * 256 * 128 * sizeof(double);
+// The current device's address of that array (hipGetSymbolAddress, taken once
+// per device and kept).
+gptq_status_t static_scratch(void** ptr);
 
 gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, double damp, void* U,
                             int u_f64, int64_t ldu, int32_t* info, double* lambda_out, void* ws,

@@ -21,9 +21,17 @@
 //    MFMA accumulator, so the partial sum is carried to ~2^-48 relative; the
 //    final value is outer + acc in fp64, and split-K partials are summed in a
 //    fixed order in fp64 (deterministic).
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
+
+// Scratch of gptq_accumulate_hessian_noalloc: the split-K partial tiles live in
+// this file-scope device array instead of a caller workspace. Every GPU the
+// library runs on holds its own copy until the process ends. In host code the
+// name is only a stand-in for the symbol: kernels get the device address that
+// hipGetSymbolAddress returns for the current device (see static_scratch).
+static __device__ __align__(256) double scratch[gptq::kStaticScratchBytes / sizeof(double)];
 
 namespace gptq {
 
@@ -583,6 +591,26 @@ size_t syrk_workspace_bytes(int64_t d, int64_t n) {
   const SkPlan p = sk_plan(d, syrk_launch_tokens(d, n));
   if (p.nsplit > 0) return (size_t)p.nsplit * syrk_ntiles(d) * TI * TJ * sizeof(double);
   return (size_t)p.nsk * 2 * TI * TJ * sizeof(double);
+}
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];  // device address of `scratch` per device, 0 until first use
+}  // namespace
+
+gptq_status_t static_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GPTQ_ERR_HIP;
+  if (dev >= kScratchDevices) return GPTQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GPTQ_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return GPTQ_OK;
 }
 
 gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const half_t* X, int64_t n,

@@ -66,6 +66,9 @@ void TraceScope::end() {
   idx_ = -1;
 }
 
+TracePause::TracePause() : was_on_(g_trace.on) { g_trace.on = false; }
+TracePause::~TracePause() { g_trace.on = was_on_; }
+
 }  // namespace gptq
 
 using namespace gptq;

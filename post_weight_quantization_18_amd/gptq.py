@@ -36,7 +36,7 @@ WS_ACCUMULATE_HESSIAN, WS_PREPARE_HINV, WS_QUANTIZE_LAYER = 0, 1, 2
 EXPORTED = ["gptq_abi_version", "gptq_status_string", "gptq_workspace_bytes", "gptq_accumulate_hessian",
             "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_act_order", "gptq_permute_hessian",
             "gptq_quantize_layer_ordered", "gptq_dequant_gemv", "gptq_pack_codes", "gptq_trace_start",
-            "gptq_trace_stop", "gptq_trace_family"]
+            "gptq_trace_stop", "gptq_trace_family", "gptq_accumulate_hessian_noalloc"]
 TRACE_FAMILIES = 14
 
 
@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_dequant_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp]
     lib.gptq_pack_codes.restype = i32
     lib.gptq_pack_codes.argtypes = [vp, i64, i64, i32, vp, vp]
+    lib.gptq_accumulate_hessian_noalloc.restype = i32
+    lib.gptq_accumulate_hessian_noalloc.argtypes = [vp, i32, i64, i64, vp, i64, i64, i32, vp]
     lib.gptq_trace_start.restype = i32
     lib.gptq_trace_start.argtypes = []
     lib.gptq_trace_stop.restype = i32
