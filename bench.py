@@ -87,6 +87,9 @@ def parse():
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--config", default="opt175b-fc2", choices=sorted(S.CONFIGS))
+    p.add_argument("--factor", choices=["R", "U"], default="R",
+                   help="R: the Cholesky factor of H_d (gptq_prepare_hchol, no inverse); "
+                        "U: chol(H_d^-1) (gptq_prepare_hinv)")
     p.add_argument("--no-trace", action="store_true",
                    help="time the steps without the per-kernel trace (no per-family breakdown)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -120,15 +123,18 @@ class LayerRun:
     """Preallocated buffers for one layer; step() enqueues the whole hot path."""
 
     def __init__(self, cfg: S.LayerConfig, w: torch.Tensor, x: torch.Tensor, chunk: int = CHUNK_TOKENS,
-                 act_order: bool = False, static_groups: bool = False):
+                 act_order: bool = False, static_groups: bool = False, factor: str = "R"):
         chunk = min(chunk, cfg.n_tokens)
         self.cfg = cfg
+        self.factor = factor
         self.act_order, self.static_groups = act_order, static_groups
         self.w, self.x = w, x
         dev = w.device
         d, m = cfg.d, cfg.m
         self.H = torch.empty(d, d, dtype=torch.float64, device=dev)
-        self.U = torch.empty(d, d, dtype=torch.float32, device=dev)
+        # U = chol(H_d^-1) in fp32, or R (R R^T = H_d) in fp64: the quantizer inverts
+        # R's diagonal blocks from it
+        self.U = torch.empty(d, d, dtype=torch.float64 if factor == "R" else torch.float32, device=dev)
         if act_order:
             self.perm = torch.empty(d, dtype=torch.int32, device=dev)
             self.Hp = torch.empty(d, d, dtype=torch.float64, device=dev)
@@ -136,7 +142,7 @@ class LayerRun:
         self.ws_h = torch.empty(max(1, G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, d, chunk)),
                                 dtype=torch.uint8, device=dev)
         self.ws_c = torch.empty(G.workspace_bytes(G.WS_PREPARE_HINV, 0, d), dtype=torch.uint8, device=dev)
-        qcfg = G.make_qcfg(cfg.bits, cfg.group, cfg.grid)
+        qcfg = G.make_qcfg(cfg.bits, cfg.group, cfg.grid, factor=factor)
         self.ws_q = torch.empty(G.workspace_bytes(G.WS_QUANTIZE_LAYER, m, d, 0, qcfg), dtype=torch.uint8, device=dev)
         ng = d // cfg.group if cfg.group else 1
         self.out = {
@@ -171,13 +177,17 @@ class LayerRun:
             G.act_order(self.H, self.perm)
             h = G.permute_hessian(self.H, self.perm, self.Hp)
         self.ev[4].record()
-        _, self.info, self.lam = G.prepare_hinv(h, cfg.damp, U=self.U, workspace=self.ws_c)
+        if self.factor == "R":
+            _, self.info, self.lam = G.prepare_hchol(h, cfg.damp, R=self.U, workspace=self.ws_c)
+        else:
+            _, self.info, self.lam = G.prepare_hinv(h, cfg.damp, U=self.U, workspace=self.ws_c)
         self.ev[2].record()
         if self.act_order:
             G.quantize_layer_ordered(self.w, self.U, self.perm, cfg.bits, cfg.group, cfg.grid, self.static_groups,
-                                     workspace=self.ws_q, out=self.out)
+                                     workspace=self.ws_q, out=self.out, factor=self.factor)
         else:
-            G.quantize_layer(self.w, self.U, cfg.bits, cfg.group, cfg.grid, workspace=self.ws_q, out=self.out)
+            G.quantize_layer(self.w, self.U, cfg.bits, cfg.group, cfg.grid, workspace=self.ws_q, out=self.out,
+                             factor=self.factor)
         self.ev[3].record()
 
     def stage_ms(self):
@@ -477,7 +487,10 @@ def main():
     x = S.make_activations(cfg, dev)
     torch.cuda.synchronize()
     _say("inputs resident; allocating buffers")
-    run = LayerRun(cfg, w, x, args.chunk_tokens, args.act_order, args.static_groups)
+    factor = args.factor
+    if factor == "R" and cfg.group > 128 and not (args.act_order and args.static_groups):
+        factor = "U"  # groups wider than a block are refitted in the U form only
+    run = LayerRun(cfg, w, x, args.chunk_tokens, args.act_order, args.static_groups, factor)
     for i in range(args.warmup):
         run.step()
         torch.cuda.synchronize()
@@ -514,7 +527,7 @@ def main():
     # algorithmic work
     f_syrk_call = run.chunk * d * (d + 1)                     # lower triangle of 2 X^T X per call
     f_syrk = n * d * (d + 1)
-    f_chain = 2 * d ** 3 / 3                                     # Cholesky + triangular inverse
+    f_chain = (d ** 3 / 3 if run.factor == "R" else 2 * d ** 3 / 3)  # Cholesky (+ triangular inverse for U)
     f_trail = m * d * max(d - 128, 0)                            # W[:, later] -= E U[blk, later], every block
     f_loop = m * d * 128                                         # in-block updates (m d B)
     syrk_call_ms = sum(syrk_calls) / len(syrk_calls)
@@ -547,7 +560,8 @@ def main():
                              "frac_executed": frac(tg["work"], tg["ms"], PEAK_FP16_TFLOPS)},
             "chain_fp64": {"bound": "mfma fp64", "ms": round(chain_ms, 3),
                            "launches": sum(v["launches"] for k, v in per.items() if k.startswith("chain_")),
-                           "flops": "2 d^3 / 3 (Cholesky + triangular inverse)",
+                           "flops": ("d^3 / 3 (Cholesky of H_d; R form)" if run.factor == "R"
+                                     else "2 d^3 / 3 (Cholesky + triangular inverse)"),
                            "frac": frac(f_chain, chain_ms, PEAK_FP64_TFLOPS),
                            "by_family_ms": {k: round(v["ms"], 3) for k, v in per.items() if k.startswith("chain_")}},
             "colloop_kernel": {"bound": "alu fp32 / LDS (d dependent steps)", "launches": cl["launches"],
@@ -584,7 +598,9 @@ def main():
                                f"{'per-row' if cfg.group == 0 else 'g' + str(cfg.group)}, block 128, damp {cfg.damp}"
                                + (", act-order" + (" + static groups" if args.static_groups else "")
                                   if args.act_order else ""),
-                   "chunk_tokens": run.chunk, "m": m, "d": d, "n_tokens": n},
+                   "chunk_tokens": run.chunk, "m": m, "d": d, "n_tokens": n,
+                   "factor": ("R (Cholesky factor of H_d, gptq_prepare_hchol)" if run.factor == "R"
+                              else "U (chol(H_d^-1), gptq_prepare_hinv)")},
         "layer_time_s": round(ms_per_step * 1e-3, 4),
         "stages_ms": {k: round(v, 4) for k, v in stage.items()},
         "mfma_frac": {"syrk_fp16": round(f_syrk / (stage["hessian"] * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),

@@ -51,6 +51,12 @@ typedef enum { GPTQ_GRID_ASYM_MINMAX = 0, GPTQ_GRID_TERNARY = 1, GPTQ_GRID_SYM_M
 
 typedef enum { GPTQ_F16 = 0, GPTQ_F32 = 1, GPTQ_F64 = 2 } gptq_dtype_t;
 
+/* Which factor of the damped Hessian H_d the quantizer is given. */
+typedef enum {
+  GPTQ_FACTOR_HINV_CHOL = 0, /* U, upper, U^T U = H_d^-1 (gptq_prepare_hinv) */
+  GPTQ_FACTOR_H_CHOL = 1     /* R, upper, R R^T = H_d, R = U^-1 (gptq_prepare_hchol) */
+} gptq_factor_t;
+
 /* Quantizer configuration (host struct).
  *  bits       2, 3, 4 or 8 (ternary: 2; codes 0, 1, 2 stand for -s, 0, +s).
  *  grid       gptq_grid_t. Asymmetric min-max: lo = min(min v, 0),
@@ -65,18 +71,27 @@ typedef enum { GPTQ_F16 = 0, GPTQ_F32 = 1, GPTQ_F64 = 2 } gptq_dtype_t;
  *             32, 64 or 128 = a grid per group of columns, fitted at the group's
  *             first column on the current (error-updated) weights;
  *             k * 128 = the same, for groups spanning k blocks.
- *  block_size must be 128 (the lazy-update block of the figure's step 4). */
+ *  block_size must be 128 (the lazy-update block of the figure's step 4).
+ *  factor     gptq_factor_t: the matrix passed as `U` to the quantize calls.
+ *             GPTQ_FACTOR_H_CHOL takes R = U^-1 and never forms U: since the
+ *             errors are e = (w - q) R for the original weights w, the pushes of
+ *             earlier blocks sum to A = sum_l (w_l - q_l) R[l, .], and a block's
+ *             true state is w + A_blk (R_bb)^-1 with R_bb its diagonal block;
+ *             the steps inside the block are the figure's, with (R_bb)^-1.
+ *             Group sizes above 128 need GPTQ_FACTOR_HINV_CHOL. */
 typedef struct {
   int32_t bits;
   int32_t grid;
   int32_t group_size;
   int32_t block_size;
+  int32_t factor;
 } gptq_qcfg_t;
 
 /* Which call a workspace is sized for. */
 enum { GPTQ_WS_ACCUMULATE_HESSIAN = 0, GPTQ_WS_PREPARE_HINV = 1, GPTQ_WS_QUANTIZE_LAYER = 2 };
 
-/* ABI version of this header (incremented on incompatible changes). */
+/* ABI version of this header (incremented on incompatible changes; 2 added the
+ * `factor` field of gptq_qcfg_t and gptq_prepare_hchol). */
 int32_t gptq_abi_version(void);
 
 /* Human-readable text for a status code (static storage, never NULL). */
@@ -135,7 +150,8 @@ gptq_status_t gptq_accumulate_hessian_noalloc(void* H, int32_t h_dtype, int64_t 
  * permutation), the same unique factor in half the flops of
  * Cholesky -> inverse -> Cholesky.
  *  H        device [d][ldh] (lower triangle read), h_dtype GPTQ_F32 | GPTQ_F64.
- *  U        device [d][ldu], u_dtype GPTQ_F32 | GPTQ_F64. May not alias H.
+ *  U        device [d][ldu], u_dtype GPTQ_F32 | GPTQ_F64. May alias H (H is
+ *           read into the workspace before U is written).
  *  damp     relative dampening (0.01 in the pages' defaults), >= 0.
  *  info     device int32: 0 = success, k > 0 = the reversed leading minor of
  *           order k is not positive definite (U is then undefined).
@@ -145,6 +161,21 @@ gptq_status_t gptq_prepare_hinv(const void* H, int32_t h_dtype, int64_t d, int64
                                 void* U, int32_t u_dtype, int64_t ldu, int32_t* info,
                                 double* lambda_out, void* workspace, size_t ws_bytes, void* stream);
 
+/* The Cholesky factor of the damped Hessian itself: R (upper, row-major, zeros
+ * below the diagonal) with R R^T = H + lambda I, lambda as gptq_prepare_hinv;
+ * R = U^-1 for the U that gptq_prepare_hinv returns. FDE breakdown, section 01:
+ * the inverse Hessian's rows are taken from a Cholesky decomposition (figure
+ * step 2: U = chol(H^-1)); the quantize calls take R with cfg->factor =
+ * GPTQ_FACTOR_H_CHOL and apply U = R^-1 without forming it (see gptq_qcfg_t).
+ * Computed in fp64 as R = J L J with L L^T = J H_d J (J the reversal), the
+ * Cholesky alone: d^3 / 3 flops, half of gptq_prepare_hinv's.
+ * Arguments, workspace, info and errors as gptq_prepare_hinv (R in place of U;
+ * R may alias H). For the quantize calls R should be GPTQ_F64: they invert R's
+ * 128 x 128 diagonal blocks from it. */
+gptq_status_t gptq_prepare_hchol(const void* H, int32_t h_dtype, int64_t d, int64_t ldh, double damp,
+                                 void* R, int32_t r_dtype, int64_t ldr, int32_t* info,
+                                 double* lambda_out, void* workspace, size_t ws_bytes, void* stream);
+
 /* Column-by-column quantization in natural order with lazy 128-column blocks.
  * FDE breakdown, figure steps 1-4, for column i: round w_i to the grid (q_i);
  * err = (w_i - q_i) / U_ii; W[:, i+1:] -= err x U[i, i+1:]; updates applied in
@@ -152,7 +183,8 @@ gptq_status_t gptq_prepare_hinv(const void* H, int32_t h_dtype, int64_t d, int64
  *  W        device [m][ldw], w_dtype GPTQ_F16 | GPTQ_F32. Read only (the library
  *           works on an fp32 copy in the workspace).
  *  U        device [d][ldu] upper factor from gptq_prepare_hinv, u_dtype
- *           GPTQ_F32 | GPTQ_F64 (GPTQ_F64 is converted to fp32 per block).
+ *           GPTQ_F32 | GPTQ_F64 (GPTQ_F64 is converted to fp32 per block); with
+ *           cfg->factor = GPTQ_FACTOR_H_CHOL, R from gptq_prepare_hchol instead.
  *  cfg      host pointer to the quantizer configuration.
  *  qcodes   device uint32 [m][d * bits / 32]: row-wise LSB-first bitstream,
  *           code j at bits [j*bits, (j+1)*bits) of its row. d * bits % 32 == 0.

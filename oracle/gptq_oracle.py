@@ -148,6 +148,23 @@ def inverse_hessian_factor(h_damped) -> np.ndarray:
     return np.triu(lower.T)
 
 
+def hessian_factor(h_damped) -> np.ndarray:
+    """R upper triangular with positive diagonal and R R^T = H_d, so that
+    R^-1 is the factor U of inverse_hessian_factor (U^T U = H_d^-1 gives
+    H_d = U^-1 U^-T).
+
+    [FDE] section 01: the needed rows of the inverse Hessian are taken from a
+    Cholesky decomposition of the Hessian. The definition is written out with
+    the reversal permutation J: L = chol(J H_d J) (lower), R = J L J.
+    Raises numpy.linalg.LinAlgError when H_d is not positive definite.
+    """
+    hd = np.asarray(h_damped, dtype=np.float64)
+    d = hd.shape[0]
+    rev = np.arange(d)[::-1]
+    lower = np.linalg.cholesky(hd[np.ix_(rev, rev)])
+    return np.triu(lower[np.ix_(rev, rev)])
+
+
 # ---------------------------------------------------------------------------
 # Grid (quantizer). The pages only say "3/4-bit grid" and "ternary": the fit
 # below is the stated reading (parity unpinned against the pages).

@@ -314,7 +314,7 @@ __device__ __forceinline__ void store16(double* P, double4v v, int li, int lk) {
 }
 
 __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_t k0, int64_t prev, int64_t pe,
-                                                   int rb, double* Dinv, int32_t* info) {
+                                                   int rb, double* Dinv, int32_t* info, double* Ldiag) {
   __shared__ double L[NB * LP];
   __shared__ double Li[NB * LP];
   __shared__ double Pd[NB * LP];  // panel prev's rows of the block: A[k0 + r][prev + c]
@@ -539,6 +539,9 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
     for (int q = 0; q < NB / 4; ++q) {
       const int r = w + 4 * q, c = lane;
       if (r < nb) Dinv[(k0 + r) * NB + c] = (c < nb && c <= r) ? Li[r * LP + c] : 0.0;
+      // the factored block itself (A's diagonal block is still being read by
+      // the other workgroups of this launch, so it goes to the side)
+      if (Ldiag && r < nb) Ldiag[(k0 + r) * NB + c] = (c < nb && c <= r) ? L[r * LP + c] : 0.0;
     }
   }
   if (!has_slab) return;  // uniform over the workgroup
@@ -575,7 +578,8 @@ __global__ __launch_bounds__(256) void panel_kernel(double* A, int64_t d, int64_
   }
 }
 
-// Every diagonal NB-block of A <- its inverse (lower, zero upper).
+// Every diagonal NB-block of A <- its inverse (lower, zero upper); with the
+// factored blocks in place of the inverses, A becomes L itself.
 __global__ __launch_bounds__(256) void put_diag_inverse_kernel(double* A, int64_t d, const double* Dinv) {
   const int64_t k0 = (int64_t)blockIdx.x * NB;
   const int nb = (int)((d - k0) < NB ? (d - k0) : NB);
@@ -700,7 +704,8 @@ __global__ __launch_bounds__(256 * KG) void merge_kernel(double* A, int64_t d, d
       }
 }
 
-// U[i][j] = A[d-1-i][d-1-j] for j >= i, else 0 (A lower holds L^-1).
+// U[i][j] = A[d-1-i][d-1-j] for j >= i, else 0 (A lower holds L^-1; or L, which
+// gives R = J L J instead).
 __global__ __launch_bounds__(256) void store_u_kernel(const double* A, int64_t d, void* U, int u_f64, int64_t ldu) {
   const int64_t i = blockIdx.y;
   for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < d; j += (int64_t)gridDim.x * 256) {
@@ -721,7 +726,7 @@ size_t chain_workspace_bytes(int64_t d) {
 
 gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, double damp, void* U, int u_f64,
                             int64_t ldu, int32_t* info, double* lambda_out, void* ws, size_t ws_bytes,
-                            hipStream_t st) {
+                            hipStream_t st, int inverse) {
   (void)ws_bytes;
   ChainWs w = chain_ws(ws, d);
   {
@@ -755,7 +760,7 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
       {
         TraceScope tr(st, GPTQ_TRACE_CHAIN_PANEL);
         hipLaunchKernelGGL(panel_kernel, dim3((unsigned)(rb + nupd)), dim3(256), 0, st, w.A, d, k0, prev, pe,
-                           (int)rb, w.Dinv, info);
+                           (int)rb, w.Dinv, info, inverse ? (double*)nullptr : w.T);
         GPTQ_CHECK_LAUNCH();
       }
       if (rest <= 0) break;
@@ -768,37 +773,48 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
       GPTQ_CHECK_LAUNCH();
     }
   }
-  {
-    TraceScope tr(st, GPTQ_TRACE_CHAIN_MERGE);
-    hipLaunchKernelGGL(put_diag_inverse_kernel, dim3((unsigned)nblk), dim3(256), 0, st, w.A, d,
-                       (const double*)w.Dinv);
+  if (!inverse) {
+    // R = J L J: put the factored diagonal blocks (kept in T) into A
+    TraceScope tr(st, GPTQ_TRACE_CHAIN_PANEL);
+    hipLaunchKernelGGL(put_diag_inverse_kernel, dim3((unsigned)nblk), dim3(256), 0, st, w.A, d, (const double*)w.T);
     GPTQ_CHECK_LAUNCH();
   }
-  const int64_t ldt = chain_smax(d);
-  for (int64_t s = NB; s < d; s *= 2) {
-    const int64_t pairs = ceil_div(d, 2 * s);
-    dim3 grid((unsigned)(s / 64), (unsigned)(s / 64), (unsigned)pairs);
-    // a grid that cannot fill the GPU splits each tile's K range over 2 wave
-    // groups; counted are the tiles that have work (the last pair may be
-    // partial or past d)
-    int64_t active = 0;
-    for (int64_t pr = 0; pr < pairs; ++pr) {
-      const int64_t c0 = pr * 2 * s + s, c1 = pr * 2 * s + 2 * s < d ? pr * 2 * s + 2 * s : d;
-      if (c0 < d) active += (s / 64) * ceil_div(c1 - c0, 64);
+  // the triangular inverse (only for U): the diagonal blocks' inverses, then
+  // recursive doubling
+  if (inverse) {
+    {
+      TraceScope tr(st, GPTQ_TRACE_CHAIN_MERGE);
+      hipLaunchKernelGGL(put_diag_inverse_kernel, dim3((unsigned)nblk), dim3(256), 0, st, w.A, d,
+                         (const double*)w.Dinv);
+      GPTQ_CHECK_LAUNCH();
     }
-    TraceScope tr(st, GPTQ_TRACE_CHAIN_MERGE);
-    if (active < 512) {
-      hipLaunchKernelGGL((merge_kernel<0, 2>), grid, dim3(512), 0, st, w.A, d, w.T, ldt, s);
-      GPTQ_CHECK_LAUNCH();
-      hipLaunchKernelGGL((merge_kernel<1, 2>), grid, dim3(512), 0, st, w.A, d, w.T, ldt, s);
-      GPTQ_CHECK_LAUNCH();
-    } else {
-      hipLaunchKernelGGL((merge_kernel<0, 1>), grid, dim3(256), 0, st, w.A, d, w.T, ldt, s);
-      GPTQ_CHECK_LAUNCH();
-      hipLaunchKernelGGL((merge_kernel<1, 1>), grid, dim3(256), 0, st, w.A, d, w.T, ldt, s);
-      GPTQ_CHECK_LAUNCH();
+    const int64_t ldt = chain_smax(d);
+    for (int64_t s = NB; s < d; s *= 2) {
+      const int64_t pairs = ceil_div(d, 2 * s);
+      dim3 grid((unsigned)(s / 64), (unsigned)(s / 64), (unsigned)pairs);
+      // a grid that cannot fill the GPU splits each tile's K range over 2 wave
+      // groups; counted are the tiles that have work (the last pair may be
+      // partial or past d)
+      int64_t active = 0;
+      for (int64_t pr = 0; pr < pairs; ++pr) {
+        const int64_t c0 = pr * 2 * s + s, c1 = pr * 2 * s + 2 * s < d ? pr * 2 * s + 2 * s : d;
+        if (c0 < d) active += (s / 64) * ceil_div(c1 - c0, 64);
+      }
+      TraceScope tr(st, GPTQ_TRACE_CHAIN_MERGE);
+      if (active < 512) {
+        hipLaunchKernelGGL((merge_kernel<0, 2>), grid, dim3(512), 0, st, w.A, d, w.T, ldt, s);
+        GPTQ_CHECK_LAUNCH();
+        hipLaunchKernelGGL((merge_kernel<1, 2>), grid, dim3(512), 0, st, w.A, d, w.T, ldt, s);
+        GPTQ_CHECK_LAUNCH();
+      } else {
+        hipLaunchKernelGGL((merge_kernel<0, 1>), grid, dim3(256), 0, st, w.A, d, w.T, ldt, s);
+        GPTQ_CHECK_LAUNCH();
+        hipLaunchKernelGGL((merge_kernel<1, 1>), grid, dim3(256), 0, st, w.A, d, w.T, ldt, s);
+        GPTQ_CHECK_LAUNCH();
+      }
     }
   }
+  // U = J L^-1 J, or without the inverse pass R = J L J (upper, H_d = R R^T)
   TraceScope tr(st, GPTQ_TRACE_CHAIN_STORE);
   hipLaunchKernelGGL(store_u_kernel, dim3((unsigned)ceil_div(d, 256) < 64 ? (unsigned)ceil_div(d, 256) : 64u,
                                           (unsigned)d),

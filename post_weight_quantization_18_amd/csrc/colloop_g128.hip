@@ -2,5 +2,6 @@
 #include "colloop_impl.h"
 
 namespace gptq {
-template gptq_status_t launch_colloop<128>(const ColArgs& a, hipStream_t st);
+template gptq_status_t launch_colloop<128, false>(const ColArgs& a, hipStream_t st);
+template gptq_status_t launch_colloop<128, true>(const ColArgs& a, hipStream_t st);
 }  // namespace gptq

@@ -6,6 +6,19 @@
 // err = (w_i - q_i) / U_ii; the block's later columns -= err x U[i, ...].
 // Rows are independent given U: four lanes (a DPP quad) own one row's 128
 // block columns in registers; the block's U is in LDS and read as broadcasts.
+//
+// Two forms of the lazy updates between blocks:
+//  * U form (RF = false): the factor is U = chol(H_d^-1). The working weights
+//    W[:, later] carry every earlier push (-= e U[blk, later]); the block reads
+//    its columns and runs steps 1-3 with the block's diagonal block of U.
+//  * R form (RF = true): the factor is R with H_d = R R^T (R = U^-1, what the
+//    Cholesky gives without any inverse). Since e = (w - q) R for the original
+//    weights w, the pushes from earlier blocks sum to a term of the
+//    accumulator A = sum_l (w_l - q_l) R[l, .]: the true state of the block's
+//    columns at its start is w + A_blk U_bb with U_bb = (R_bb)^-1, the inverse
+//    of R's diagonal block only. The block rebuilds that state in a first pass
+//    over U_bb, runs the same steps 1-3, and hands (q - w) to the trailing GEMM
+//    (A[:, later] -= (q - w)_blk R[blk, later]).
 #pragma once
 
 #include "quant_shared.h"
@@ -27,7 +40,8 @@ constexpr int UGS = CPL + 4;     // LDS stride of a lane group's slice (floats):
 constexpr int UPITCH = QL * UGS; // LDS row pitch of the U block (floats)
 
 struct LaneState {
-  float w[CPL];         // the lane's 32 working weights, then its 32 errors
+  float w[CPL];         // the lane's 32 working weights, then its 32 errors (R form: q - w)
+  float w0[CPL];        // R form: the original weights of its 32 columns
   uint32_t cw[CPL / 4]; // its 32 codes, one byte each
   float s, rs, zf, esum;
   float cs[CPL], crs[CPL], cz[CPL];  // static groups: the grid of each of its 32 columns
@@ -75,7 +89,7 @@ __device__ __forceinline__ void load_urow(URow& ur, const float (*Us)[UPITCH], c
   ur.rd = rdiag[i];
 }
 
-template <int G, int I>
+template <int G, bool RF, int I>
 __device__ __forceinline__ void col_step(LaneState& st, const ColArgs& a, int64_t r, int g, const URow& ur) {
   const float rd = ur.rd;
   constexpr int O = I / CPL, LI = I % CPL;
@@ -120,7 +134,12 @@ __device__ __forceinline__ void col_step(LaneState& st, const ColArgs& a, int64_
   if (owner) {
     st.esum += e_own * e_own;
     st.cw[LI >> 2] |= ((uint32_t)c) << (8 * (LI & 3));
-    st.w[LI] = e_own;  // the register now carries the error of column I
+    // the register now carries the error of column I (R form: q - w, the
+    // trailing GEMM's operand; e itself only enters the OBS loss)
+    if constexpr (RF)
+      st.w[LI] = qv - st.w0[LI];
+    else
+      st.w[LI] = e_own;
   }
   const float e = quad_bcast<O>(e_own);
 #pragma unroll
@@ -135,7 +154,7 @@ __device__ __forceinline__ void col_step(LaneState& st, const ColArgs& a, int64_
 
 // Steps I .. BLK-1 of the block: row I + 1 of U is read from LDS before step I
 // runs, so its latency hides behind the step's arithmetic.
-template <int G, int I>
+template <int G, bool RF, int I>
 struct Steps {
   __device__ __forceinline__ static void run(LaneState& st, const ColArgs& a, int64_t r, int g,
                                              const float (*Us)[UPITCH], const float* rdiag, int bw, const URow& cur) {
@@ -143,8 +162,33 @@ struct Steps {
     URow nxt;
     if constexpr (I + 1 < BLK) load_urow(nxt, Us, rdiag, I + 1, g);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this step's work
-    col_step<G, I>(st, a, r, g, cur);
-    if constexpr (I + 1 < BLK) Steps<G, I + 1>::run(st, a, r, g, Us, rdiag, bw, nxt);
+    col_step<G, RF, I>(st, a, r, g, cur);
+    if constexpr (I + 1 < BLK) Steps<G, RF, I + 1>::run(st, a, r, g, Us, rdiag, bw, nxt);
+  }
+};
+
+// R form, first pass: w += A_blk U_bb (the lane's 32 columns; U_bb's strictly
+// upper part from LDS, its diagonal 1 / R_ii from rdiag). The accumulator
+// values are known up front, so the steps carry no dependency but the sums.
+template <int I>
+struct StateSteps {
+  __device__ __forceinline__ static void run(LaneState& st, const float* acc, int g, const float (*Us)[UPITCH],
+                                             const float* rdiag, int bw, const URow& cur) {
+    if (I >= bw) return;
+    constexpr int O = I / CPL, LI = I % CPL;
+    URow nxt;
+    if constexpr (I + 1 < BLK) load_urow(nxt, Us, rdiag, I + 1, g);
+    const float av = quad_bcast<O>(acc[LI]);
+#pragma unroll
+    for (int k4 = 0; k4 < CPL / 4; ++k4) {
+      const float4 u = cur.u[k4];
+      st.w[4 * k4] = fmaf(av, u.x, st.w[4 * k4]);
+      st.w[4 * k4 + 1] = fmaf(av, u.y, st.w[4 * k4 + 1]);
+      st.w[4 * k4 + 2] = fmaf(av, u.z, st.w[4 * k4 + 2]);
+      st.w[4 * k4 + 3] = fmaf(av, u.w, st.w[4 * k4 + 3]);
+    }
+    if (g == O) st.w[LI] += acc[LI] / cur.rd;
+    if constexpr (I + 1 < BLK) StateSteps<I + 1>::run(st, acc, g, Us, rdiag, bw, nxt);
   }
 };
 
@@ -153,17 +197,20 @@ struct Steps {
 // group's first block from the current working weights; G = -2: static groups,
 // every column takes the grid of its natural group perm[j] / group (fitted
 // before the loop).
-template <int G>
+template <int G, bool RF>
 __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
   __shared__ __attribute__((aligned(16))) float Us[BLK][UPITCH];
   __shared__ float rdiag[BLK];
+  static_assert(!RF || G != -1, "the R form fits groups within a block or from the original weights");
   const int tid = threadIdx.x;
   const int bw = a.bw;
-  // strictly upper part of the block's U (zeros on and below the diagonal)
+  // strictly upper part of the block's U (zeros on and below the diagonal);
+  // R form: U_bb from the compact block inverses (row pitch BLK)
   for (int idx = tid; idx < BLK * BLK / 4; idx += CL_THREADS) {
     const int i = idx / (BLK / 4), k4 = (idx % (BLK / 4)) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < bw && k4 < bw) v = *(const float4*)(a.U + (a.j0 + i) * a.ldu + a.j0 + k4);
+    if (i < bw && k4 < bw)
+      v = RF ? *(const float4*)(a.Ublk + i * BLK + k4) : *(const float4*)(a.U + (a.j0 + i) * a.ldu + a.j0 + k4);
     if (k4 + 0 <= i) v.x = 0.f;
     if (k4 + 1 <= i) v.y = 0.f;
     if (k4 + 2 <= i) v.z = 0.f;
@@ -189,6 +236,25 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
     st.w[k + 1] = v.y;
     st.w[k + 2] = v.z;
     st.w[k + 3] = v.w;
+  }
+  if constexpr (RF) {
+    // the block's true state: original weights plus A_blk U_bb
+    float acc[CPL];
+    const float* arow = a.Acc + rr * a.d + a.j0 + g * CPL;
+#pragma unroll
+    for (int k = 0; k < CPL; k += 4) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (cols_ok) v = *(const float4*)(arow + k);
+      acc[k] = v.x;
+      acc[k + 1] = v.y;
+      acc[k + 2] = v.z;
+      acc[k + 3] = v.w;
+    }
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) st.w0[k] = st.w[k];
+    URow first;
+    load_urow(first, Us, rdiag, 0, g);
+    StateSteps<0>::run(st, acc, g, Us, rdiag, bw, first);
   }
 #pragma unroll
   for (int k = 0; k < CPL / 4; ++k) st.cw[k] = 0;
@@ -244,7 +310,7 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
   if (live) {
     URow first;
     load_urow(first, Us, rdiag, 0, g);
-    Steps<G, 0>::run(st, a, r, g, Us, rdiag, bw, first);
+    Steps<G, RF, 0>::run(st, a, r, g, Us, rdiag, bw, first);
   }
 
   if (a.Eh) {
@@ -293,10 +359,10 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
 
 }  // namespace
 
-template <int G>
+template <int G, bool RF>
 gptq_status_t launch_colloop(const ColArgs& a, hipStream_t st) {
   TraceScope tr(st, GPTQ_TRACE_COLLOOP);
-  hipLaunchKernelGGL(colloop_kernel<G>, dim3((unsigned)ceil_div(a.m, CL_THREADS / 4)), dim3(CL_THREADS), 0, st, a);
+  hipLaunchKernelGGL((colloop_kernel<G, RF>), dim3((unsigned)ceil_div(a.m, CL_THREADS / 4)), dim3(CL_THREADS), 0, st, a);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }

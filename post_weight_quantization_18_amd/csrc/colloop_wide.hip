@@ -2,5 +2,5 @@
 #include "colloop_impl.h"
 
 namespace gptq {
-template gptq_status_t launch_colloop<-1>(const ColArgs& a, hipStream_t st);
+template gptq_status_t launch_colloop<-1, false>(const ColArgs& a, hipStream_t st);
 }  // namespace gptq

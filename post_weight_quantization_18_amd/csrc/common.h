@@ -107,9 +107,11 @@ constexpr size_t kStaticScratchBytes = (size_t)768 * 256 * 128 * sizeof(double);
 // per device and kept).
 gptq_status_t static_scratch(void** ptr);
 
+// inverse = 1: U = chol_upper(H_d^-1) = J L^-1 J; inverse = 0: R = J L J, the
+// upper factor with H_d = R R^T (R = U^-1), without the triangular inverse.
 gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, double damp, void* U,
                             int u_f64, int64_t ldu, int32_t* info, double* lambda_out, void* ws,
-                            size_t ws_bytes, hipStream_t st);
+                            size_t ws_bytes, hipStream_t st, int inverse = 1);
 size_t chain_workspace_bytes(int64_t d);
 
 // perm (optional): the quantization order, W and the outputs staying in natural

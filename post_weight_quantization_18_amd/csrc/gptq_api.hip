@@ -16,9 +16,10 @@ using namespace gptq;
 namespace {
 
 // GPTQ_OK, GPTQ_ERR_INVALID_ARG for a malformed configuration (bits, grid,
-// block size, a group size that does not divide d), GPTQ_ERR_UNSUPPORTED for a
-// well-formed group size the kernels do not take.
-gptq_status_t check_qcfg(const gptq_qcfg_t& c, int64_t d) {
+// block size, factor, a group size that does not divide d),
+// GPTQ_ERR_UNSUPPORTED for a well-formed group size the kernels do not take
+// (static: grids fitted on the original weights, any group size).
+gptq_status_t check_qcfg(const gptq_qcfg_t& c, int64_t d, bool stat = false) {
   if (c.block_size != 128) return GPTQ_ERR_INVALID_ARG;
   if (c.grid != GPTQ_GRID_ASYM_MINMAX && c.grid != GPTQ_GRID_TERNARY && c.grid != GPTQ_GRID_SYM_MINMAX)
     return GPTQ_ERR_INVALID_ARG;
@@ -26,7 +27,9 @@ gptq_status_t check_qcfg(const gptq_qcfg_t& c, int64_t d) {
   if (c.bits != 2 && c.bits != 3 && c.bits != 4 && c.bits != 8) return GPTQ_ERR_INVALID_ARG;
   const int g = c.group_size;
   if (g < 0 || (g > 0 && d % g)) return GPTQ_ERR_INVALID_ARG;
+  if (c.factor != GPTQ_FACTOR_HINV_CHOL && c.factor != GPTQ_FACTOR_H_CHOL) return GPTQ_ERR_INVALID_ARG;
   if (g == 0 || g == 32 || g == 64 || g == 128) return GPTQ_OK;
+  if (c.factor == GPTQ_FACTOR_H_CHOL && !stat) return GPTQ_ERR_UNSUPPORTED;  // wide dynamic groups: U form only
   return (g % 128 == 0 && d % 128 == 0) ? GPTQ_OK : GPTQ_ERR_UNSUPPORTED;
 }
 
@@ -61,6 +64,7 @@ gptq_qcfg_t default_qcfg() {
   c.grid = GPTQ_GRID_ASYM_MINMAX;
   c.group_size = 0;
   c.block_size = 128;
+  c.factor = GPTQ_FACTOR_HINV_CHOL;
   return c;
 }
 
@@ -70,7 +74,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 extern "C" {
 
-int32_t gptq_abi_version(void) { return 1; }
+int32_t gptq_abi_version(void) { return 2; }
 
 const char* gptq_status_string(int32_t s) {
   switch (s) {
@@ -137,6 +141,20 @@ gptq_status_t gptq_prepare_hinv(const void* H, int32_t h_dtype, int64_t d, int64
                        workspace, ws_bytes, (hipStream_t)stream);
 }
 
+gptq_status_t gptq_prepare_hchol(const void* H, int32_t h_dtype, int64_t d, int64_t ldh, double damp, void* R,
+                                 int32_t r_dtype, int64_t ldr, int32_t* info, double* lambda_out, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  if (!H || !R || !info || d <= 0 || ldh < d || ldr < d) return GPTQ_ERR_INVALID_ARG;
+  if (!(damp >= 0.0)) return GPTQ_ERR_INVALID_ARG;
+  if (h_dtype != GPTQ_F32 && h_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
+  if (r_dtype != GPTQ_F32 && r_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < chain_workspace_bytes(d)) return GPTQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return GPTQ_ERR_INVALID_ARG;
+  GPTQ_CHECK_DEVICE();
+  return chain_enqueue(H, h_dtype == GPTQ_F64, d, ldh, damp, R, r_dtype == GPTQ_F64, ldr, info, lambda_out,
+                       workspace, ws_bytes, (hipStream_t)stream, 0);
+}
+
 gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int64_t d, int64_t ldw, const void* U,
                                   int32_t u_dtype, int64_t ldu, const gptq_qcfg_t* cfg, uint32_t* qcodes,
                                   float* scales, uint8_t* zeros, float* W_hat, float* err_sq, void* workspace,
@@ -181,7 +199,7 @@ gptq_status_t gptq_quantize_layer_ordered(const void* W, int32_t w_dtype, int64_
   if (w_dtype != GPTQ_F16 && w_dtype != GPTQ_F32) return GPTQ_ERR_INVALID_ARG;
   if (u_dtype != GPTQ_F32 && u_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
   if (u_dtype == GPTQ_F32 && (ldu % 4 || !aligned(U, 16))) return GPTQ_ERR_INVALID_ARG;
-  if (const gptq_status_t cs = check_qcfg(*cfg, d)) return cs;
+  if (const gptq_status_t cs = check_qcfg(*cfg, d, static_groups != 0)) return cs;
   if (!workspace || !aligned(workspace, 256)) return GPTQ_ERR_WORKSPACE;
   GPTQ_CHECK_DEVICE();
   return quant_enqueue(W, w_dtype == GPTQ_F32, m, d, ldw, U, u_dtype == GPTQ_F64, ldu, *cfg, qcodes, scales, zeros,

@@ -46,6 +46,8 @@ struct QuantWs {
   half_t* Utl;      //                                                         fp16 low
   float* U32;       // d x d (only when U is fp64)
   int32_t* inv;     // d: position of every natural column in the quantization order
+  float* Acc;       // R form: m x d accumulator of the pushes from earlier blocks
+  float* Ubb;       // R form: nblocks x BLK x BLK inverses of R's diagonal blocks
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -66,7 +68,7 @@ int64_t sb_width(int64_t d, int group) {
   return s;
 }
 
-QuantWs quant_ws(void* ws, int64_t m, int64_t d, int group, int u_f64) {
+QuantWs quant_ws(void* ws, int64_t m, int64_t d, int group, int u_f64, int rform) {
   QuantWs w;
   char* p = (char*)ws;
   const int64_t nb = nblocks_of(d), S = sb_width(d, group);
@@ -91,16 +93,19 @@ QuantWs quant_ws(void* ws, int64_t m, int64_t d, int group, int u_f64) {
   w.Utl = (half_t*)take((size_t)nb * d * BLK * sizeof(half_t));
   w.U32 = u_f64 ? (float*)take((size_t)d * d * sizeof(float)) : nullptr;
   w.inv = (int32_t*)take((size_t)d * sizeof(int32_t));
+  w.Acc = rform ? (float*)take((size_t)m * d * sizeof(float)) : nullptr;
+  w.Ubb = rform ? (float*)take((size_t)nb * BLK * BLK * sizeof(float)) : nullptr;
   return w;
 }
 
-size_t quant_ws_total(int64_t m, int64_t d, int group, int u_f64) {
+size_t quant_ws_total(int64_t m, int64_t d, int group, int u_f64, int rform) {
   const int64_t nb = nblocks_of(d), S = sb_width(d, group);
   size_t b = align256((size_t)m * d * 4) + align256((size_t)m * S * 4) + 2 * align256((size_t)m * BLK * 2) +
              2 * align256((size_t)m * S * 2) + 2 * align256((size_t)m * 4) + align256((size_t)m * d) +
              align256((size_t)d * 4) + 2 * align256(4) + 2 * align256((size_t)nb * d * BLK * 2);
   if (u_f64) b += align256((size_t)d * d * 4);
   b += align256((size_t)d * 4);
+  if (rform) b += align256((size_t)m * d * 4) + align256((size_t)nb * BLK * BLK * 4);
   return b;
 }
 
@@ -254,9 +259,53 @@ __global__ void f64_to_f32_kernel(const double* U, int64_t d, int64_t ldu, float
     U32[i * d + j] = (float)U[i * ldu + j];
 }
 
-__global__ void rdiag_kernel(const float* U, int64_t d, int64_t ldu, float* rdiag) {
+// rdiag[j] = 1 / U_jj; in the R form U_jj = 1 / R_jj, so rdiag[j] = R_jj.
+__global__ void rdiag_kernel(const float* U, int64_t d, int64_t ldu, int rform, float* rdiag) {
   for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < d; j += (int64_t)gridDim.x * blockDim.x)
-    rdiag[j] = 1.0f / U[j * ldu + j];
+    rdiag[j] = rform ? U[j * ldu + j] : 1.0f / U[j * ldu + j];
+}
+
+// x[0 .. n) = 0 (a kernel, not a memset: safe to capture in a graph).
+__global__ void fill_zero_kernel(float* x, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n / 4; i += (int64_t)gridDim.x * blockDim.x)
+    ((float4*)x)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) x[n - 1 - threadIdx.x] = 0.0f;
+}
+
+// R form: Ubb[b] = (R[b0:b1, b0:b1])^-1 for every 128-column block b (upper
+// triangular; fp64 arithmetic from R as given, fp32 result, rows and columns
+// past the block's width zero). One workgroup per block; the inverse X is
+// built row by row from the bottom: X_ii = 1 / R_ii and, for c > i,
+// X_ic = -(sum_{i < k <= c} R_ik X_kc) / R_ii, thread c owning column c.
+__global__ __launch_bounds__(BLK) void rblock_inverse_kernel(const void* R, int r_f64, int64_t d, int64_t ldr,
+                                                             float* Ubb) {
+  __shared__ double X[BLK][BLK];
+  __shared__ double Ti[BLK];
+  const int64_t b0 = (int64_t)blockIdx.x * BLK;
+  const int bw = (int)((d - b0) < BLK ? (d - b0) : BLK);
+  const int c = threadIdx.x;
+  auto rv = [&](int i, int k) -> double {
+    const int64_t o = (b0 + i) * ldr + b0 + k;
+    return r_f64 ? ((const double*)R)[o] : (double)((const float*)R)[o];
+  };
+  for (int i = bw - 1; i >= 0; --i) {
+    Ti[c] = (c >= i && c < bw) ? rv(i, c) : 0.0;
+    __syncthreads();
+    if (c < bw) {
+      double v = 0.0;
+      if (c == i) {
+        v = 1.0 / Ti[i];
+      } else if (c > i) {
+        double sacc = 0.0;
+        for (int k = i + 1; k <= c; ++k) sacc = fma(Ti[k], X[k][c], sacc);
+        v = -sacc / Ti[i];
+      }
+      X[i][c] = v;
+    }
+    __syncthreads();
+  }
+  float* out = Ubb + (int64_t)blockIdx.x * BLK * BLK;
+  for (int i = 0; i < BLK; ++i) out[i * BLK + c] = (i < bw && c < bw && c >= i) ? (float)X[i][c] : 0.0f;
 }
 
 
@@ -425,16 +474,17 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* codes, int64_t
 }  // namespace
 
 size_t quant_workspace_bytes(int64_t m, int64_t d, const gptq_qcfg_t& cfg) {
-  return quant_ws_total(m, d, cfg.group_size, 0);
+  return quant_ws_total(m, d, cfg.group_size, 0, cfg.factor == GPTQ_FACTOR_H_CHOL);
 }
 
 gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int64_t ldw, const void* U, int u_f64,
                             int64_t ldu, const gptq_qcfg_t& cfg, uint32_t* qcodes, float* scales, uint8_t* zeros,
                             float* W_hat, float* err_sq, void* ws, size_t ws_bytes, hipStream_t st,
                             const int32_t* perm, int static_groups, int32_t* g_idx) {
-  const size_t need = quant_ws_total(m, d, cfg.group_size, u_f64);
+  const int rform = cfg.factor == GPTQ_FACTOR_H_CHOL;
+  const size_t need = quant_ws_total(m, d, cfg.group_size, u_f64, rform);
   if (ws == nullptr || ws_bytes < need) return GPTQ_ERR_WORKSPACE;
-  QuantWs w = quant_ws(ws, m, d, cfg.group_size, u_f64);
+  QuantWs w = quant_ws(ws, m, d, cfg.group_size, u_f64, rform);
   const int gmode = cfg.grid;
   const float maxq = gmode == GPTQ_GRID_TERNARY ? 2.0f : (float)((1 << cfg.bits) - 1);
   const int group = cfg.group_size;
@@ -461,9 +511,20 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
     U32 = w.U32;
     ldu32 = d;
   }
-  hipLaunchKernelGGL(rdiag_kernel, dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, st, U32, d, ldu32, w.rdiag);
+  hipLaunchKernelGGL(rdiag_kernel, dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, st, U32, d, ldu32, rform,
+                     w.rdiag);
   GPTQ_CHECK_LAUNCH();
   const int64_t nblk = nblocks_of(d);
+  if (rform) {
+    // the inverses of R's diagonal blocks (from the factor as given, in fp64)
+    // and a zero accumulator
+    hipLaunchKernelGGL(rblock_inverse_kernel, dim3((unsigned)nblk), dim3(BLK), 0, st, U, u_f64, d, ldu, w.Ubb);
+    GPTQ_CHECK_LAUNCH();
+    const int64_t n = m * d;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)(ceil_div(n / 4 + 1, 256) < 8192 ? ceil_div(n / 4 + 1, 256) : 8192)),
+                       dim3(256), 0, st, w.Acc, n);
+    GPTQ_CHECK_LAUNCH();
+  }
   if (nblk > 1) {
     hipLaunchKernelGGL(umax_zero_kernel, dim3(1), dim3(64), 0, st, w.umax);
     GPTQ_CHECK_LAUNCH();
@@ -503,6 +564,8 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
 
   ColArgs a;
   a.Wk = w.Wk;
+  a.Acc = w.Acc;
+  a.Ublk = nullptr;
   a.U = U32;
   a.rdiag = w.rdiag;
   a.ldu = ldu32;
@@ -545,20 +608,34 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
     a.El = inner ? w.Elb : nullptr;
     a.einv = inner ? w.einv_b : nullptr;
     gptq_status_t s;
-    if (stat)
-      s = launch_colloop<-2>(a, st);
-    else switch (group) {
-      case 0: s = launch_colloop<0>(a, st); break;
-      case 32: s = launch_colloop<32>(a, st); break;
-      case 64: s = launch_colloop<64>(a, st); break;
-      case 128: s = launch_colloop<128>(a, st); break;
-      default: s = launch_colloop<-1>(a, st); break;
+    if (rform) {
+      a.Ublk = w.Ubb + b * BLK * BLK;
+      if (stat)
+        s = launch_colloop<-2, true>(a, st);
+      else switch (group) {
+        case 0: s = launch_colloop<0, true>(a, st); break;
+        case 32: s = launch_colloop<32, true>(a, st); break;
+        case 64: s = launch_colloop<64, true>(a, st); break;
+        case 128: s = launch_colloop<128, true>(a, st); break;
+        default: return GPTQ_ERR_UNSUPPORTED;  // rejected by the entry point already
+      }
+    } else if (stat) {
+      s = launch_colloop<-2, false>(a, st);
+    } else switch (group) {
+      case 0: s = launch_colloop<0, false>(a, st); break;
+      case 32: s = launch_colloop<32, false>(a, st); break;
+      case 64: s = launch_colloop<64, false>(a, st); break;
+      case 128: s = launch_colloop<128, false>(a, st); break;
+      default: s = launch_colloop<-1, false>(a, st); break;
     }
     if (s != GPTQ_OK) return s;
+    // the trailing updates go to the working weights (U form) or to the
+    // accumulator (R form, whose column loop hands over q - w)
+    float* const tgt = rform ? w.Acc : w.Wk;
     const int64_t j1 = a.j0 + a.bw;
     if (j1 < sb1) {
       // the rest of the super-block: K = this block (split by the column loop)
-      t.C = w.Wk + j1;
+      t.C = tgt + j1;
       t.Ah = w.Ehb;
       t.Al = w.Elb;
       t.rowscale = w.einv_b;
@@ -575,7 +652,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
                            (int)(sb1 - sb0), w.Ehs, w.Els, m * 32, w.einv_s);
         GPTQ_CHECK_LAUNCH();
       }
-      t.C = w.Wk + sb1;
+      t.C = tgt + sb1;
       t.Ah = w.Ehs;
       t.Al = w.Els;
       t.rowscale = w.einv_s;
@@ -617,7 +694,7 @@ gptq_status_t pack_enqueue(const uint8_t* codes, int64_t ldc, int64_t m, int64_t
 }
 
 size_t quant_workspace_bytes_u64(int64_t m, int64_t d, const gptq_qcfg_t& cfg) {
-  return quant_ws_total(m, d, cfg.group_size, 1);
+  return quant_ws_total(m, d, cfg.group_size, 1, cfg.factor == GPTQ_FACTOR_H_CHOL);
 }
 
 }  // namespace gptq

@@ -63,6 +63,11 @@ struct ColArgs {
   float* err_sq;
   const int32_t* perm;  // quantization order (static groups: grids by natural group)
   int first;
+  // R form: Wk holds the original weights (in the quantization order), Acc the
+  // accumulator A of the pushes from earlier blocks, Ublk this block's U_bb
+  // (the inverse of R's diagonal block, row pitch BLK)
+  const float* Acc;
+  const float* Ublk;
 };
 
 // The column loop over one block of a.bw columns starting at a.j0, for the
@@ -72,7 +77,8 @@ struct ColArgs {
 // that are multiples of 128 or that do not divide 128: the blocks are cut at
 // group starts), refitted at the group's first block from the working weights;
 // -2 = static groups (grids fitted before the loop, per natural group).
-template <int G>
+// RF: the factor is R (H_d = R R^T) instead of U = R^-1 (not with G = -1).
+template <int G, bool RF>
 gptq_status_t launch_colloop(const ColArgs& a, hipStream_t st);
 
 }  // namespace gptq

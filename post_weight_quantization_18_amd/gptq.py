@@ -36,13 +36,17 @@ WS_ACCUMULATE_HESSIAN, WS_PREPARE_HINV, WS_QUANTIZE_LAYER = 0, 1, 2
 EXPORTED = ["gptq_abi_version", "gptq_status_string", "gptq_workspace_bytes", "gptq_accumulate_hessian",
             "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_act_order", "gptq_permute_hessian",
             "gptq_quantize_layer_ordered", "gptq_dequant_gemv", "gptq_pack_codes", "gptq_trace_start",
-            "gptq_trace_stop", "gptq_trace_family", "gptq_accumulate_hessian_noalloc"]
+            "gptq_trace_stop", "gptq_trace_family", "gptq_accumulate_hessian_noalloc", "gptq_prepare_hchol"]
 TRACE_FAMILIES = 14
+
+
+GPTQ_FACTOR_HINV_CHOL, GPTQ_FACTOR_H_CHOL = 0, 1
+_FACTOR = {"U": GPTQ_FACTOR_HINV_CHOL, "R": GPTQ_FACTOR_H_CHOL}
 
 
 class QCfg(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("grid", ctypes.c_int32), ("group_size", ctypes.c_int32),
-                ("block_size", ctypes.c_int32)]
+                ("block_size", ctypes.c_int32), ("factor", ctypes.c_int32)]
 
 
 _lib = None
@@ -67,6 +71,8 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_accumulate_hessian.argtypes = [vp, i32, i64, i64, vp, i64, i64, i32, vp, sz, vp]
     lib.gptq_prepare_hinv.restype = i32
     lib.gptq_prepare_hinv.argtypes = [vp, i32, i64, i64, ctypes.c_double, vp, i32, i64, vp, vp, vp, sz, vp]
+    lib.gptq_prepare_hchol.restype = i32
+    lib.gptq_prepare_hchol.argtypes = [vp, i32, i64, i64, ctypes.c_double, vp, i32, i64, vp, vp, vp, sz, vp]
     lib.gptq_quantize_layer.restype = i32
     lib.gptq_quantize_layer.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, ctypes.POINTER(QCfg), vp, vp, vp, vp,
                                         vp, vp, sz, vp]
@@ -127,9 +133,10 @@ def _rowmajor_ld(t, name):
     return t.stride(0)
 
 
-def make_qcfg(bits: int, group_size: int = 0, grid: str = "asym", block_size: int = 128) -> QCfg:
+def make_qcfg(bits: int, group_size: int = 0, grid: str = "asym", block_size: int = 128,
+              factor: str = "U") -> QCfg:
     g = {"asym": GPTQ_GRID_ASYM_MINMAX, "ternary": GPTQ_GRID_TERNARY, "sym": GPTQ_GRID_SYM_MINMAX}[grid]
-    return QCfg(bits, g, group_size, block_size)
+    return QCfg(bits, g, group_size, block_size, _FACTOR[factor])
 
 
 def workspace_bytes(which: int, m: int = 0, d: int = 0, n: int = 0, cfg: QCfg | None = None) -> int:
@@ -182,15 +189,34 @@ def prepare_hinv(H: torch.Tensor, damp: float = 0.01, U: torch.Tensor | None = N
     return U, info, lam
 
 
+def prepare_hchol(H: torch.Tensor, damp: float = 0.01, R: torch.Tensor | None = None,
+                  r_dtype: torch.dtype = torch.float64, workspace=None):
+    """Returns (R, info, lam): R upper [d, d] with R R^T = H + lam I (R = U^-1), info
+    and lam as prepare_hinv. Pass R to the quantize calls with factor="R"."""
+    lib = load_library()
+    _need_cuda(H, "H")
+    d = H.shape[0]
+    if R is None:
+        R = torch.empty(d, d, dtype=r_dtype, device=H.device)
+    info = torch.empty(1, dtype=torch.int32, device=H.device)
+    lam = torch.empty(1, dtype=torch.float64, device=H.device)
+    ws = _workspace(workspace_bytes(WS_PREPARE_HINV, 0, d), H.device, workspace)
+    _check(lib.gptq_prepare_hchol(_ptr(H), _DT[H.dtype], d, _rowmajor_ld(H, "H"), float(damp), _ptr(R), _DT[R.dtype],
+                                  _rowmajor_ld(R, "R"), _ptr(info), _ptr(lam), _ptr(ws), ws.numel(),
+                                  _stream(H.device)), "gptq_prepare_hchol")
+    return R, info, lam
+
+
 def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, group_size: int = 0, grid: str = "asym",
-                   block_size: int = 128, want_w_hat: bool = True, workspace=None, out=None):
+                   block_size: int = 128, want_w_hat: bool = True, workspace=None, out=None, factor: str = "U"):
     """Returns dict(qcodes uint32 [m, d*bits/32] (as int32 storage), scales fp32 [m, ng],
-    zeros uint8 [m, ng], w_hat fp32 [m, d] or None, err_sq fp32 [m])."""
+    zeros uint8 [m, ng], w_hat fp32 [m, d] or None, err_sq fp32 [m]). factor "U": U =
+    chol(H_d^-1) from prepare_hinv; "R": R from prepare_hchol (passed as U)."""
     lib = load_library()
     _need_cuda(W, "W")
     _need_cuda(U, "U")
     m, d = W.shape
-    cfg = make_qcfg(bits, group_size, grid, block_size)
+    cfg = make_qcfg(bits, group_size, grid, block_size, factor)
     ng = d // group_size if group_size else 1
     dev = W.device
     if out is None:
@@ -243,7 +269,7 @@ def permute_hessian(H: torch.Tensor, perm: torch.Tensor, Hp: torch.Tensor | None
 
 def quantize_layer_ordered(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, bits: int, group_size: int = 0,
                            grid: str = "asym", static_groups: bool = False, block_size: int = 128,
-                           want_w_hat: bool = True, workspace=None, out=None):
+                           want_w_hat: bool = True, workspace=None, out=None, factor: str = "U"):
     """quantize_layer with the columns quantized in the order perm (U: the factor of
     the Hessian in that order). Outputs in natural column order, plus g_idx int32 [d]."""
     lib = load_library()
@@ -253,7 +279,7 @@ def quantize_layer_ordered(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor,
     if perm.dtype != torch.int32 or not perm.is_contiguous():
         raise ValueError("perm must be contiguous int32")
     m, d = W.shape
-    cfg = make_qcfg(bits, group_size, grid, block_size)
+    cfg = make_qcfg(bits, group_size, grid, block_size, factor)
     ng = d // group_size if group_size else 1
     dev = W.device
     if out is None:
@@ -328,7 +354,7 @@ def trace_stop() -> dict:
 
 def quantize(W: torch.Tensor, x_chunks, bits: int, group_size: int = 0, grid: str = "asym", damp: float = 0.01,
              h_dtype: torch.dtype = torch.float64, u_dtype: torch.dtype = torch.float32, want_w_hat: bool = True,
-             act_order: bool = False, static_groups: bool = False):
+             act_order: bool = False, static_groups: bool = False, factor: str = "U"):
     """The whole hot path of one layer: H over the chunks, U, then the column loop.
     Returns (result dict, H, U, lam). Raises when H + lam I is not positive definite.
     With act_order the columns go in descending diag(H) (result["perm"]), U is the
@@ -340,17 +366,20 @@ def quantize(W: torch.Tensor, x_chunks, bits: int, group_size: int = 0, grid: st
     for i, xc in enumerate(x_chunks):
         accumulate_hessian(H, xc, accumulate=i > 0)
     perm = None
+    prep = prepare_hchol if factor == "R" else prepare_hinv
+    kw = {"r_dtype": torch.float64} if factor == "R" else {"u_dtype": u_dtype}
     if act_order:
         perm = _act_order(H)
-        U, info, lam = prepare_hinv(permute_hessian(H, perm), damp, u_dtype=u_dtype)
+        U, info, lam = prep(permute_hessian(H, perm), damp, **kw)
     else:
-        U, info, lam = prepare_hinv(H, damp, u_dtype=u_dtype)
+        U, info, lam = prep(H, damp, **kw)
     bad = int(info.item())
     if bad:
         raise GPTQError(GPTQ_ERR_INVALID_ARG, f"H + lambda I is not positive definite (reversed minor {bad})")
     if act_order:
-        res = quantize_layer_ordered(W, U, perm, bits, group_size, grid, static_groups, want_w_hat=want_w_hat)
+        res = quantize_layer_ordered(W, U, perm, bits, group_size, grid, static_groups, want_w_hat=want_w_hat,
+                                     factor=factor)
         res["perm"] = perm
     else:
-        res = quantize_layer(W, U, bits, group_size, grid, want_w_hat=want_w_hat)
+        res = quantize_layer(W, U, bits, group_size, grid, want_w_hat=want_w_hat, factor=factor)
     return res, H, U, lam

@@ -65,8 +65,10 @@ def lower_rel_fro(h_gpu: np.ndarray, h_orc: np.ndarray) -> float:
 
 
 def gpu_layer(w: torch.Tensor, x: torch.Tensor, bits, group, grid, damp=0.01, chunk_tokens=None,
-              h_dtype=torch.float64, u_dtype=torch.float32):
-    """Runs the three entry points on cuda:0; returns host numpy results."""
+              h_dtype=torch.float64, u_dtype=torch.float32, factor="U"):
+    """Runs the three entry points on cuda:0; returns host numpy results.
+    factor "U": gptq_prepare_hinv (U, u_dtype); "R": gptq_prepare_hchol (R, fp64)
+    and the quantizer in the R form."""
     dev = torch.device("cuda:0")
     wd = w.to(dev)
     xd = x.to(dev)
@@ -77,10 +79,14 @@ def gpu_layer(w: torch.Tensor, x: torch.Tensor, bits, group, grid, damp=0.01, ch
     else:
         for i, t0 in enumerate(range(0, xd.shape[0], chunk_tokens)):
             G.accumulate_hessian(H, xd[t0:t0 + chunk_tokens], accumulate=i > 0)
-    U, info, lam = G.prepare_hinv(H, damp, u_dtype=u_dtype)
+    if factor == "R":
+        u_dtype = torch.float64
+        U, info, lam = G.prepare_hchol(H, damp, r_dtype=u_dtype)
+    else:
+        U, info, lam = G.prepare_hinv(H, damp, u_dtype=u_dtype)
     torch.cuda.synchronize()
     assert int(info.item()) == 0, "H + lambda I reported not positive definite"
-    res = G.quantize_layer(wd, U, bits, group, grid)
+    res = G.quantize_layer(wd, U, bits, group, grid, factor=factor)
     torch.cuda.synchronize()
     m = w.shape[0]
     codes = O.unpack_codes(res["qcodes"].cpu().numpy().view(np.uint32), bits, d)
@@ -96,6 +102,7 @@ def gpu_layer(w: torch.Tensor, x: torch.Tensor, bits, group, grid, damp=0.01, ch
         "err_sq": res["err_sq"].cpu().numpy(),
         "m": m,
         "u_eps": 2.0 ** -24 if u_dtype == torch.float32 else 2.0 ** -53,
+        "factor": factor,
     }
 
 
@@ -173,10 +180,13 @@ def _row_stats(stats, wn, gpu, follow, free, h, bits, grid, group, g_idx=None, s
 
 
 def _factor_stats(stats, gpu, h, lam, u, hd):
+    """H, lambda and the factor the GPU path used (U, or R = U^-1 with factor "R")
+    against the oracle's."""
     d = h.shape[0]
     stats["h_rel"] = lower_rel_fro(gpu["H"], h)
     stats["lam_rel"] = abs(gpu["lam"] - lam) / lam
-    uu = np.triu(u)
+    stats["factor"] = gpu.get("factor", "U")
+    uu = np.triu(O.hessian_factor(hd) if stats["factor"] == "R" else u)
     stats["u_rel"] = float(np.linalg.norm(np.triu(gpu["U"]) - uu) / np.linalg.norm(uu))
     stats["kappa_bound"] = kappa_bound(hd, lam)
     # plus the rounding of U to its output precision (fp32 or fp64)
@@ -227,7 +237,7 @@ def assert_gates(stats, h_tol=H_TOL, code_frac=CODE_FRAC, loss_tol=LOSS_TOL):
 
 
 def gpu_layer_ordered(w: torch.Tensor, x: torch.Tensor, bits, group, grid, static_groups, damp=0.01,
-                      h_dtype=torch.float64, u_dtype=torch.float32):
+                      h_dtype=torch.float64, u_dtype=torch.float32, factor="U"):
     """Act-order through the C ABI on cuda:0: H, the order, the permuted H, its
     factor, the ordered column loop. Host numpy results."""
     dev = torch.device("cuda:0")
@@ -237,10 +247,14 @@ def gpu_layer_ordered(w: torch.Tensor, x: torch.Tensor, bits, group, grid, stati
     G.accumulate_hessian(H, x.to(dev), accumulate=False)
     perm = G.act_order(H)
     Hp = G.permute_hessian(H, perm)
-    U, info, lam = G.prepare_hinv(Hp, damp, u_dtype=u_dtype)
+    if factor == "R":
+        u_dtype = torch.float64
+        U, info, lam = G.prepare_hchol(Hp, damp, r_dtype=u_dtype)
+    else:
+        U, info, lam = G.prepare_hinv(Hp, damp, u_dtype=u_dtype)
     torch.cuda.synchronize()
     assert int(info.item()) == 0, "H + lambda I reported not positive definite"
-    res = G.quantize_layer_ordered(wd, U, perm, bits, group, grid, static_groups)
+    res = G.quantize_layer_ordered(wd, U, perm, bits, group, grid, static_groups, factor=factor)
     torch.cuda.synchronize()
     return {
         "H": H.cpu().double().numpy(),
@@ -256,6 +270,7 @@ def gpu_layer_ordered(w: torch.Tensor, x: torch.Tensor, bits, group, grid, stati
         "w_hat": res["w_hat"].cpu().numpy(),
         "err_sq": res["err_sq"].cpu().numpy(),
         "u_eps": 2.0 ** -24 if u_dtype == torch.float32 else 2.0 ** -53,
+        "factor": factor,
     }
 
 

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.gptq_abi_version() == 1
+    assert lib.gptq_abi_version() == 2
     for s in range(5):
         assert lib.gptq_status_string(s).decode().startswith("GPTQ_")
     assert b"unknown" in lib.gptq_status_string(99)
@@ -92,6 +92,14 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert q(G.make_qcfg(4, group_size=48)) == G.GPTQ_ERR_INVALID_ARG        # group must divide d
     assert q(G.make_qcfg(4, group_size=384), d=512) == G.GPTQ_ERR_INVALID_ARG  # group must divide d
     assert q(G.make_qcfg(4, group_size=24), d=480) == G.GPTQ_ERR_UNSUPPORTED  # not 16 nor a multiple of 32
+    assert q(G.make_qcfg(4, group_size=256, factor="R"), d=512) == G.GPTQ_ERR_UNSUPPORTED  # R form: groups <= 128
+    bad = G.make_qcfg(4)
+    bad.factor = 7
+    assert q(bad) == G.GPTQ_ERR_INVALID_ARG
+    # prepare_hchol: null R, negative damp, missing workspace
+    assert lib.gptq_prepare_hchol(fake, 2, 64, 64, 0.01, None, 2, 64, fake, None, fake, 1 << 30, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_prepare_hchol(fake, 2, 64, 64, -1.0, fake, 2, 64, fake, None, fake, 1 << 30, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_prepare_hchol(fake, 2, 64, 64, 0.01, fake, 2, 64, fake, None, None, 0, None) == G.GPTQ_ERR_WORKSPACE
     assert q(G.make_qcfg(4), d=200) == G.GPTQ_ERR_INVALID_ARG                # d % 32
     assert q(G.make_qcfg(4), ws=None) == G.GPTQ_ERR_WORKSPACE
     # act_order / permute_hessian: null, ldh < d, bad dtype, aliasing

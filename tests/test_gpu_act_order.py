@@ -115,3 +115,16 @@ def test_act_order_layer_parity(label, cfg, static):
     gpu = gpu_layer_ordered(w, x, cfg.bits, cfg.group, cfg.grid, static)
     stats = compare_layer_ordered(w, x, cfg.bits, cfg.group, cfg.grid, static, gpu, label=label)
     assert_ordered_gates(stats, static, cfg.group)
+
+
+# the R form takes static groups of any size and dynamic groups up to 128
+CASES_R = [c for c in CASES if c[2] or c[1].group <= 128]
+
+
+@pytest.mark.parametrize("label,cfg,static", CASES_R, ids=[c[0] for c in CASES_R])
+def test_act_order_layer_parity_rform(label, cfg, static):
+    say(f"[case] act-order layer R form {label} m={cfg.m} d={cfg.d} group={cfg.group} static={static}")
+    w, x = S.make_layer(cfg)
+    gpu = gpu_layer_ordered(w, x, cfg.bits, cfg.group, cfg.grid, static, factor="R")
+    stats = compare_layer_ordered(w, x, cfg.bits, cfg.group, cfg.grid, static, gpu, label=label + " [R]")
+    assert_ordered_gates(stats, static, cfg.group)

@@ -53,12 +53,13 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("factor", ["U", "R"])
 @pytest.mark.parametrize("label,m,d,n,bits,group,grid", CASES, ids=[c[0] for c in CASES])
-def test_degenerate_layer_natural(label, m, d, n, bits, group, grid):
-    say(f"[case] degenerate natural {label}")
+def test_degenerate_layer_natural(label, m, d, n, bits, group, grid, factor):
+    say(f"[case] degenerate natural {label} factor={factor}")
     w, x = _degenerate(m, d, n, seed=d + n)
-    gpu = gpu_layer(w, x, bits, group, grid)
-    assert_gates(compare_layer(w, x, bits, group, grid, gpu, label=label))
+    gpu = gpu_layer(w, x, bits, group, grid, factor=factor)
+    assert_gates(compare_layer(w, x, bits, group, grid, gpu, label=label + f" [{factor}]"))
 
 
 @pytest.mark.parametrize("label,m,d,n,bits,group,grid", CASES, ids=[c[0] for c in CASES])

@@ -126,6 +126,34 @@ def test_chain_parity(d, u_dtype):
     assert abs(float(lam.item()) - lam_o) <= 1e-12 * lam_o
 
 
+@pytest.mark.parametrize("d,r_dtype", [(768, torch.float64), (768, torch.float32), (40, torch.float64),
+                                       (1000, torch.float64), (8256, torch.float64)])
+def test_hchol_parity(d, r_dtype):
+    """gptq_prepare_hchol: R (R R^T = H_d) against the oracle's hessian_factor."""
+    say(f"[case] hchol d={d} r_dtype={r_dtype}")
+    rng = np.random.default_rng(d + 7)
+    a = rng.standard_normal((4 * d, d)) @ np.diag(1.0 / np.arange(1, d + 1)) @ np.linalg.qr(rng.standard_normal((d, d)))[0]
+    h = 2 * a.T @ a
+    R, info, lam = G.prepare_hchol(torch.from_numpy(h).to(DEV), 0.01, r_dtype=r_dtype)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    hd_o, lam_o = O.damp(h, 0.01)
+    ro = O.hessian_factor(hd_o)
+    rg = R.cpu().double().numpy()
+    rel = np.linalg.norm(rg - ro) / np.linalg.norm(ro)
+    say(f"  R rel={rel:.3e}")
+    assert np.all(np.tril(rg, -1) == 0)
+    assert rel <= (1e-12 if r_dtype == torch.float64 else 2e-7)
+    assert abs(float(lam.item()) - lam_o) <= 1e-12 * lam_o
+    # diagonal H_d: R = diag(sqrt(h)); H = 0 without damping is not positive definite
+    dg = np.linspace(1.0, 9.0, 128)
+    R2, info2, _ = G.prepare_hchol(torch.from_numpy(np.diag(dg)).to(DEV), 0.0)
+    Z, info3, _ = G.prepare_hchol(torch.zeros(128, 128, dtype=torch.float64, device=DEV), 0.0)
+    torch.cuda.synchronize()
+    assert int(info2.item()) == 0 and int(info3.item()) > 0
+    np.testing.assert_allclose(R2.cpu().numpy(), np.diag(np.sqrt(dg)), rtol=1e-15, atol=0)
+
+
 def test_chain_diagonal_and_not_positive_definite():
     say("[case] chain diagonal / non-PD")
     d = 128
@@ -145,19 +173,20 @@ def test_chain_diagonal_and_not_positive_definite():
 # ---------------------------------------------------------------------------
 # whole layer
 # ---------------------------------------------------------------------------
-def _layer_case(cfg, chunk_tokens=None, label=None):
+def _layer_case(cfg, chunk_tokens=None, label=None, factor="U"):
     say(f"[case] layer {label or cfg.name} m={cfg.m} d={cfg.d} n={cfg.n_tokens} bits={cfg.bits} "
-        f"grid={cfg.grid} group={cfg.group}")
+        f"grid={cfg.grid} group={cfg.group} factor={factor}")
     w, x = S.make_layer(cfg, device=S.default_device_for(cfg))
     w, x = w.cpu(), x.cpu()
-    gpu = gpu_layer(w, x, cfg.bits, cfg.group, cfg.grid, cfg.damp, chunk_tokens=chunk_tokens)
-    stats = compare_layer(w, x, cfg.bits, cfg.group, cfg.grid, gpu, cfg.damp, label or cfg.name)
+    gpu = gpu_layer(w, x, cfg.bits, cfg.group, cfg.grid, cfg.damp, chunk_tokens=chunk_tokens, factor=factor)
+    stats = compare_layer(w, x, cfg.bits, cfg.group, cfg.grid, gpu, cfg.damp, (label or cfg.name) + f" [{factor}]")
     assert_gates(stats)
     return stats
 
 
-def test_layer_parity_toy768():
-    _layer_case(S.CONFIGS["toy768"])
+@pytest.mark.parametrize("factor", ["U", "R"])
+def test_layer_parity_toy768(factor):
+    _layer_case(S.CONFIGS["toy768"], factor=factor)
 
 
 _SCALED = [
@@ -184,11 +213,35 @@ def test_layer_parity_scaled(label, cfg):
     _layer_case(cfg, label=label)
 
 
-def test_layer_parity_d12288_slice():
+# the R form (factor R = U^-1): every group size it takes (groups above 128 need U)
+_SCALED_R = [(label, cfg) for label, cfg in _SCALED if cfg.group <= 128]
+
+
+@pytest.mark.parametrize("label,cfg", _SCALED_R, ids=[c[0] for c in _SCALED_R])
+def test_layer_parity_scaled_rform(label, cfg):
+    _layer_case(cfg, label=label, factor="R")
+
+
+def test_rform_rejects_groups_wider_than_a_block():
+    lib = G.load_library()
+    import ctypes
+    cfg = G.make_qcfg(4, group_size=256, factor="R")
+    w = torch.zeros(8, 512, dtype=torch.float16, device=DEV)
+    R = torch.eye(512, dtype=torch.float64, device=DEV)
+    out = torch.empty(8, 64, dtype=torch.int32, device=DEV)
+    sc = torch.empty(8, 2, dtype=torch.float32, device=DEV)
+    zz = torch.empty(8, 2, dtype=torch.uint8, device=DEV)
+    st = lib.gptq_quantize_layer(G._ptr(w), G.GPTQ_F16, 8, 512, 512, G._ptr(R), G.GPTQ_F64, 512, ctypes.byref(cfg),
+                                 G._ptr(out), G._ptr(sc), G._ptr(zz), None, None, G._ptr(w), 1 << 20, G._stream(DEV))
+    assert st == G.GPTQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("factor", ["U", "R"])
+def test_layer_parity_d12288_slice(factor):
     """OPT-175B q/k/v/out width (d = 12288) on 64 rows and 16384 tokens: the
     conditioning of the full layer, at a size the oracle finishes quickly."""
     cfg = S.scaled(S.CONFIGS["opt175b-q"], m=64, n_tokens=16384)
-    _layer_case(cfg, chunk_tokens=8192, label="opt175b-q-slice")
+    _layer_case(cfg, chunk_tokens=8192, label="opt175b-q-slice", factor=factor)
 
 
 def test_rtn_reduction_on_gpu():
@@ -243,11 +296,12 @@ def _call_with_small_ws(w, U):
 
 
 @pytest.mark.timeout(900)
-def test_layer_parity_opt27b_fc1_full():
+@pytest.mark.parametrize("factor", ["U", "R"])
+def test_layer_parity_opt27b_fc1_full(factor):
     """OPT-2.7B fc1 at full size (10240 x 2560, 262144 tokens, 4-bit per row),
     in the launch configuration the benchmark times (one call over all 262144
     tokens)."""
-    _layer_case(S.CONFIGS["opt2.7b-fc1"], chunk_tokens=262144)
+    _layer_case(S.CONFIGS["opt2.7b-fc1"], chunk_tokens=262144, factor=factor)
 
 
 def test_prepare_hinv_u_may_alias_h():

@@ -6,7 +6,8 @@ H, fp32 U).
   whole oracle runs on every row, and the usual parity gates apply.
 * OPT-175B q (12288 x 12288), fc1 (49152 x 12288, 3-bit g128) and the extreme
   regime on the fc1 shape (2-bit and ternary g128, one W and one X): the GPU
-  quantizes the whole layer; the oracle builds its own fp64 H from all 262144
+  quantizes the whole layer from R, the Cholesky factor of H_d (the benchmark's
+  path); the oracle builds its own fp64 H from all 262144
   tokens, damps it and factors it, then runs follow mode and a free run on
   258 sampled rows (rows are independent given U, and every grid is fitted
   within its row). The usual gates apply to those rows.
@@ -65,14 +66,15 @@ def _sample_rows(m, seed):
 
 
 def _device_factor(cfg, x):
-    """H over all tokens in one call (fp64), then U (fp32), as the benchmark runs them."""
+    """H over all tokens in one call (fp64), then R = U^-1 (fp64, the Cholesky factor
+    of H_d), as the benchmark runs them."""
     d = cfg.d
     H = torch.empty(d, d, dtype=torch.float64, device=DEV)
     G.accumulate_hessian(H, x, accumulate=False)
-    U, info, lam = G.prepare_hinv(H, cfg.damp, u_dtype=torch.float32)
+    R, info, lam = G.prepare_hchol(H, cfg.damp, r_dtype=torch.float64)
     torch.cuda.synchronize()
     assert int(info.item()) == 0
-    return H, U, float(lam.item())
+    return H, R, float(lam.item())
 
 
 def _rows_of(res, rows, bits, d):
@@ -107,11 +109,11 @@ def test_code_parity_full_size_sampled_rows(label, names):
     rows = _sample_rows(c0.m, 21)
     gpu_rows = []
     for c in cfgs:
-        res = G.quantize_layer(w, U, c.bits, c.group, c.grid)
+        res = G.quantize_layer(w, U, c.bits, c.group, c.grid, factor="R")
         torch.cuda.synchronize()
         gpu_rows.append(_rows_of(res, rows, c.bits, c.d))
         del res
-    factor = {"H": H.cpu().numpy(), "U": U.cpu().double().numpy(), "lam": lam, "u_eps": 2.0 ** -24}
+    factor = {"H": H.cpu().numpy(), "U": U.cpu().double().numpy(), "lam": lam, "u_eps": 2.0 ** -53, "factor": "R"}
     wn = w[torch.as_tensor(rows, device=DEV)].double().cpu().numpy()
     xh = x.cpu().numpy()
     del H, U, x

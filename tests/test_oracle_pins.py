@@ -442,3 +442,26 @@ def test_asymmetric_grid_properties(bits):
         q = O.rtn_quantize(vv, bits, "asym", 0)
         assert s1[0] == t and z1[0] == k
         assert q.w_hat[0, 0] == -k * t and q.w_hat[0, 1] == (maxq - k) * t
+
+
+def test_hessian_factor_definition_and_relations():
+    """R upper with a positive diagonal and R R^T = H_d; R^-1 equals the
+    inverse-Hessian factor U (both are the unique positive-diagonal triangular
+    factors); a diagonal H_d gives R = diag(sqrt(h)); the 2 x 2 closed form
+    R = [[sqrt(a - b^2/c), b/sqrt(c)], [0, sqrt(c)]] for H_d = [[a, b], [b, c]]."""
+    rng = np.random.default_rng(31)
+    for d in (1, 2, 7, 40):
+        x = rng.standard_normal((3 * d + 5, d)) @ rng.standard_normal((d, d))
+        hd, _ = O.damp(O.hessian(x), 0.01)
+        r = O.hessian_factor(hd)
+        assert np.allclose(np.tril(r, -1), 0.0) and np.all(np.diag(r) > 0)
+        np.testing.assert_allclose(r @ r.T, hd, rtol=1e-12, atol=1e-12 * np.abs(hd).max())
+        u = O.inverse_hessian_factor(hd)
+        np.testing.assert_allclose(np.linalg.inv(r), u, rtol=1e-9, atol=1e-12 * np.abs(u).max())
+    h = np.diag([4.0, 9.0, 0.25])
+    np.testing.assert_array_equal(O.hessian_factor(h), np.diag([2.0, 3.0, 0.5]))
+    a, b, c = 5.0, 2.0, 4.0
+    r2 = O.hessian_factor(np.array([[a, b], [b, c]]))
+    np.testing.assert_allclose(r2, [[np.sqrt(a - b * b / c), b / np.sqrt(c)], [0.0, np.sqrt(c)]], rtol=1e-15)
+    with pytest.raises(np.linalg.LinAlgError):
+        O.hessian_factor(np.array([[1.0, 2.0], [2.0, 1.0]]))
