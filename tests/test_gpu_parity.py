@@ -106,7 +106,7 @@ def test_hessian_accumulate_and_empty():
                                        (200, torch.float64), (1000, torch.float64), (4160, torch.float64),
                                        (64, torch.float64), (40, torch.float64),
                                        # large enough for the 128-tile trailing updates, ragged at 128
-                                       (8256, torch.float64)])
+                                       (8256, torch.float64), (2049, torch.float64)])
 def test_chain_parity(d, u_dtype):
     say(f"[case] chain d={d} u_dtype={u_dtype}")
     rng = np.random.default_rng(d)
@@ -127,7 +127,7 @@ def test_chain_parity(d, u_dtype):
 
 
 @pytest.mark.parametrize("d,r_dtype", [(768, torch.float64), (768, torch.float32), (40, torch.float64),
-                                       (1000, torch.float64), (8256, torch.float64)])
+                                       (1000, torch.float64), (8256, torch.float64), (1537, torch.float64)])
 def test_hchol_parity(d, r_dtype):
     """gptq_prepare_hchol: R (R R^T = H_d) against the oracle's hessian_factor."""
     say(f"[case] hchol d={d} r_dtype={r_dtype}")
