@@ -68,9 +68,12 @@ typedef enum {
  *             levels and compatibility with various grids (nubint review, "Key
  *             findings"); these fits are the readings the library implements.
  *  group_size 0 = one grid per output row, fitted on the original row;
- *             32, 64 or 128 = a grid per group of columns, fitted at the group's
- *             first column on the current (error-updated) weights;
- *             k * 128 = the same, for groups spanning k blocks.
+ *             16, 32, 64 or 128 = a grid per group of columns, fitted at the
+ *             group's first column on the current (error-updated) weights;
+ *             any other multiple of 32 dividing d (96, 192, 256, 1024, ...) =
+ *             the same, fitted over the whole group with every earlier update
+ *             applied (the lazy blocks are then also cut at group starts).
+ *             Other sizes: GPTQ_ERR_UNSUPPORTED; not dividing d: INVALID_ARG.
  *  block_size must be 128 (the lazy-update block of the figure's step 4).
  *  factor     gptq_factor_t: the matrix passed as `U` to the quantize calls.
  *             GPTQ_FACTOR_H_CHOL takes R = U^-1 and never forms U: since the
@@ -78,7 +81,8 @@ typedef enum {
  *             earlier blocks sum to A = sum_l (w_l - q_l) R[l, .], and a block's
  *             true state is w + A_blk (R_bb)^-1 with R_bb its diagonal block;
  *             the steps inside the block are the figure's, with (R_bb)^-1.
- *             Group sizes above 128 need GPTQ_FACTOR_HINV_CHOL. */
+ *             Group sizes other than 16, 32, 64 and 128 need
+ *             GPTQ_FACTOR_HINV_CHOL unless the groups are static. */
 typedef struct {
   int32_t bits;
   int32_t grid;
@@ -193,7 +197,7 @@ gptq_status_t gptq_prepare_hchol(const void* H, int32_t h_dtype, int64_t d, int6
  *  W_hat    device float [m][d] = s * (code - z), may be NULL.
  *  err_sq   device float [m]: sum over the row of err^2 / 2 (the optimal-brain-
  *           surgeon loss increments), may be NULL.
- *  Sizes: m >= 1, d % 128 == 0 when group_size > 128, else d % 32 == 0. */
+ *  Sizes: m >= 1, d % 32 == 0, group_size dividing d. */
 gptq_status_t gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int64_t d, int64_t ldw,
                                   const void* U, int32_t u_dtype, int64_t ldu, const gptq_qcfg_t* cfg,
                                   uint32_t* qcodes, float* scales, uint8_t* zeros, float* W_hat,

@@ -270,8 +270,6 @@ def _check_group(d, group, block):
         raise ValueError("group must be >= 0")
     if group and d % group:
         raise ValueError("group must divide d")
-    if group and not (block % group == 0 or group % block == 0):
-        raise ValueError("group must divide the block or be a multiple of it")
 
 
 def gptq_quantize(w, u, bits: int, grid: str = GRID_ASYM, group: int = 0,
@@ -292,7 +290,12 @@ def gptq_quantize(w, u, bits: int, grid: str = GRID_ASYM, group: int = 0,
     blocked=True applies step 3 inside a block immediately and to the columns
     after the block once, at the block's end (W[:, end:] -= E_blk U[blk, end:]);
     blocked=False applies step 3 to all later columns at every column. Both
-    give the same result in exact arithmetic.
+    give the same result in exact arithmetic. A group grid is fitted at the
+    group's first column j on the current weights, i.e. with every update of
+    the columns before j applied: where the group reaches past the block, the
+    block's updates of columns b0 .. j-1, which the blocked form applies only
+    at the block's end, are added for the fit (W[:, end:j+g] - E[:, b0:j]
+    U[b0:j, end:j+g]).
 
     follow_codes (optional, [m, d]): the codes of another implementation. At
     every element the oracle computes its own pre-round value p and code; a
@@ -336,9 +339,14 @@ def gptq_quantize(w, u, bits: int, grid: str = GRID_ASYM, group: int = 0,
         b1 = min(b0 + step, d)
         for j in range(b0, b1):
             if group and j % group == 0:
-                s, z, _ = fit_grid(w[:, j:j + group], bits, grid)
+                cur = w[:, j:j + group]
+                if j + group > b1 and j > b0:
+                    # the part past the block still lacks this block's updates of columns b0 .. j-1
+                    cur = cur.copy()
+                    cur[:, b1 - j:] -= res.err[:, b0:j] @ u[b0:j, b1:j + group]
+                s, z, _ = fit_grid(cur, bits, grid)
                 if follow_zeros is not None and grid == GRID_ASYM:
-                    z, zb, zh = follow_zero_points(w[:, j:j + group], s, z,
+                    z, zb, zh = follow_zero_points(cur, s, z,
                                                    np.asarray(follow_zeros)[:, j // group], band)
                     res.zero_band_mismatch += zb
                     res.zero_hard_mismatch += zh

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgptq_mi355x.so")
 SOURCES = ["gptq_api.hip", "syrk.hip", "chain.hip", "quant.hip", "trail.hip", "order.hip", "gemv.hip", "trace.hip",
-           "colloop_row.hip", "colloop_g32.hip", "colloop_g64.hip", "colloop_g128.hip", "colloop_wide.hip",
+           "colloop_row.hip", "colloop_g16.hip", "colloop_g32.hip", "colloop_g64.hip", "colloop_g128.hip", "colloop_wide.hip",
            "colloop_static.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -28,9 +28,12 @@ gptq_status_t check_qcfg(const gptq_qcfg_t& c, int64_t d, bool stat = false) {
   const int g = c.group_size;
   if (g < 0 || (g > 0 && d % g)) return GPTQ_ERR_INVALID_ARG;
   if (c.factor != GPTQ_FACTOR_HINV_CHOL && c.factor != GPTQ_FACTOR_H_CHOL) return GPTQ_ERR_INVALID_ARG;
-  if (g == 0 || g == 32 || g == 64 || g == 128) return GPTQ_OK;
-  if (c.factor == GPTQ_FACTOR_H_CHOL && !stat) return GPTQ_ERR_UNSUPPORTED;  // wide dynamic groups: U form only
-  return (g % 128 == 0 && d % 128 == 0) ? GPTQ_OK : GPTQ_ERR_UNSUPPORTED;
+  if (g == 0 || g == 16 || g == 32 || g == 64 || g == 128) return GPTQ_OK;
+  if (g % 32) return GPTQ_ERR_UNSUPPORTED;  // other groups: multiples of 32
+  // groups wider than a block or cutting blocks are fitted over columns past the
+  // block, whose state the R form does not carry (static grids need none)
+  if (c.factor == GPTQ_FACTOR_H_CHOL && !stat) return GPTQ_ERR_UNSUPPORTED;
+  return GPTQ_OK;
 }
 
 // The kernels are built for gfx950 only. The current device's architecture

@@ -64,7 +64,17 @@ int64_t sb_width(int64_t d, int group) {
   int64_t s = (int64_t)(sqrt(128.0 * (double)d) / BLK + 0.5) * BLK;
   if (s < 2 * BLK) s = 2 * BLK;
   if (s > 16 * BLK) s = 16 * BLK;
-  if (group > BLK) s = ceil_div(s, group) * group;
+  if (group > 0 && BLK % group != 0) {
+    // a group must never straddle two super-blocks: S a multiple of lcm(BLK, group)
+    int64_t a = BLK, bb = group;
+    while (bb) {
+      const int64_t t = a % bb;
+      a = bb;
+      bb = t;
+    }
+    const int64_t l = BLK / a * group;
+    s = ceil_div(s, l) * l;
+  }
   return s;
 }
 
@@ -353,11 +363,14 @@ __global__ __launch_bounds__(256) void umax_zero_kernel(uint32_t* umax) {
   if (threadIdx.x == 0) umax[0] = 0u;
 }
 
-__global__ __launch_bounds__(256) void umax_kernel(const float* U, int64_t ldu, int64_t d, uint32_t* umax) {
-  const int64_t b = blockIdx.y, j0 = b * BLK, j1 = j0 + BLK;
+// With cut set (lazy blocks also cut at group starts), the block's own strictly
+// upper part is included: a sub-block [j0', j1') of the 128-block updates the
+// columns [j1', ...) of its own block too.
+__global__ __launch_bounds__(256) void umax_kernel(const float* U, int64_t ldu, int64_t d, int cut, uint32_t* umax) {
+  const int64_t b = blockIdx.y, j0 = b * BLK, c_from = cut ? j0 : j0 + BLK;
   float mx = 0.0f;
-  for (int64_t c = j1 + (int64_t)blockIdx.x * 256 + threadIdx.x; c < d; c += (int64_t)gridDim.x * 256)
-    for (int k = 0; k < BLK; ++k) mx = fmaxf(mx, fabsf(U[(j0 + k) * ldu + c]));
+  for (int64_t c = c_from + (int64_t)blockIdx.x * 256 + threadIdx.x; c < d; c += (int64_t)gridDim.x * 256)
+    for (int k = 0; k < BLK && j0 + k < c; ++k) mx = fmaxf(mx, fabsf(U[(j0 + k) * ldu + c]));
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if ((threadIdx.x & 63) == 0 && mx > 0.0f) atomicMax(&umax[0], __float_as_uint(mx));
 }
@@ -371,21 +384,22 @@ __device__ inline float u_scale(const uint32_t* umax) {
 
 // Transposed, scaled fp16 hi/lo panels of the far part of each block row of U,
 // K-tiled in slabs of 32 for the trailing GEMM:
-//   Ut{h,l}[b][k / 32][c][k % 32] = split(U[j0 + k][c] * 2^s),  c >= j0 + BLK, k < BLK,
+//   Ut{h,l}[b][k / 32][c][k % 32] = split(U[j0 + k][c] * 2^s),  c >= j0 + BLK, k < BLK
+// (with cut: c > j0 + k, the block's own strictly upper part too),
 // with 2^s the power of two that puts max |U| of all far parts in [2^14, 2^15)
 // (uinv = 2^-s). One 64-column chunk per workgroup, transposed through LDS.
-__global__ __launch_bounds__(256) void usplit_kernel(const float* U, int64_t ldu, int64_t d, const uint32_t* umax,
-                                                     half_t* Uth, half_t* Utl, float* uinv) {
+__global__ __launch_bounds__(256) void usplit_kernel(const float* U, int64_t ldu, int64_t d, int cut,
+                                                     const uint32_t* umax, half_t* Uth, half_t* Utl, float* uinv) {
   __shared__ float tile[BLK][64 + 1];
-  const int64_t b = blockIdx.y, j0 = b * BLK, j1 = j0 + BLK;
-  const int64_t c0 = j1 + (int64_t)blockIdx.x * 64;
+  const int64_t b = blockIdx.y, j0 = b * BLK;
+  const int64_t c0 = (cut ? j0 : j0 + BLK) + (int64_t)blockIdx.x * 64;
   const float sc = u_scale(umax);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) uinv[0] = 1.0f / sc;
   if (c0 >= d) return;
   const int tid = threadIdx.x;
   for (int idx = tid; idx < BLK * 64; idx += 256) {
     const int k = idx / 64, c = idx % 64;
-    tile[k][c] = (c0 + c < d) ? U[(j0 + k) * ldu + c0 + c] * sc : 0.0f;
+    tile[k][c] = (c0 + c < d && j0 + k < d && c0 + c > j0 + k) ? U[(j0 + k) * ldu + c0 + c] * sc : 0.0f;
   }
   __syncthreads();
   // each thread writes 8 consecutive k of one column: 64 cols x 16 chunks
@@ -490,6 +504,11 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   const int group = cfg.group_size;
   const int ngroups = group ? (int)(d / group) : 1;
   const bool stat = perm && static_groups && group > 0;
+  // groups that neither divide the block nor are multiples of it (96, 160, ...):
+  // the lazy blocks are also cut at group starts, so that every group starts at
+  // a block start with all earlier updates applied, and is fitted there over
+  // its whole width (the U form's wide-group path)
+  const bool cut = !stat && group > 0 && BLK % group != 0 && group % BLK != 0;
   TraceScope tr_prep(st, GPTQ_TRACE_QUANT_PREP);
   if (perm) {
     hipLaunchKernelGGL(order_index_kernel, dim3((unsigned)(ceil_div(d, 256) < 1024 ? ceil_div(d, 256) : 1024)),
@@ -525,14 +544,16 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
                        dim3(256), 0, st, w.Acc, n);
     GPTQ_CHECK_LAUNCH();
   }
-  if (nblk > 1) {
+  const int64_t nsplit_blk = cut ? nblk : nblk - 1;  // block rows whose far part the GEMMs read
+  if (nsplit_blk > 0) {
     hipLaunchKernelGGL(umax_zero_kernel, dim3(1), dim3(64), 0, st, w.umax);
     GPTQ_CHECK_LAUNCH();
     const unsigned cgroups = (unsigned)(ceil_div(d, 256) < 16 ? ceil_div(d, 256) : 16);
-    hipLaunchKernelGGL(umax_kernel, dim3(cgroups, (unsigned)(nblk - 1)), dim3(256), 0, st, U32, ldu32, d, w.umax);
+    hipLaunchKernelGGL(umax_kernel, dim3(cgroups, (unsigned)nsplit_blk), dim3(256), 0, st, U32, ldu32, d, cut ? 1 : 0,
+                       w.umax);
     GPTQ_CHECK_LAUNCH();
-    hipLaunchKernelGGL(usplit_kernel, dim3((unsigned)ceil_div(d, 64), (unsigned)(nblk - 1)), dim3(256), 0, st, U32,
-                       ldu32, d, (const uint32_t*)w.umax, w.Uth, w.Utl, w.uinv);
+    hipLaunchKernelGGL(usplit_kernel, dim3((unsigned)ceil_div(d, 64), (unsigned)nsplit_blk), dim3(256), 0, st, U32,
+                       ldu32, d, cut ? 1 : 0, (const uint32_t*)w.umax, w.Uth, w.Utl, w.uinv);
     GPTQ_CHECK_LAUNCH();
   }
   const int64_t row_bytes = d * (w_f32 ? 4 : 2);
@@ -583,7 +604,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   const int64_t S = sb_width(d, group);
   a.E = w.Esb;
   a.lde = S;
-  const int64_t nblocks = ceil_div(d, BLK);
+  int first = 1;
   TgemmArgs t;
   t.C = nullptr;
   t.ldc = d;
@@ -595,10 +616,18 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   t.cscale = w.uinv;
   t.M = m;
   const unsigned egrid = (unsigned)ceil_div(m, 4);
-  for (int64_t b = 0; b < nblocks; ++b) {
-    a.j0 = b * BLK;
-    a.bw = (int)((d - a.j0) < BLK ? (d - a.j0) : BLK);
-    a.first = b == 0;
+  for (int64_t j0 = 0; j0 < d;) {
+    // the next block: up to the next multiple of 128 (and, cut, of the group)
+    int64_t jn = (j0 / BLK + 1) * BLK;
+    if (cut && (j0 / group + 1) * group < jn) jn = (j0 / group + 1) * group;
+    if (jn > d) jn = d;
+    const int64_t b = j0 / BLK;                       // its 128-block
+    const int64_t kslab0 = ((j0 % BLK) / 32) * d * 32;  // its first K-slab in the split panels of that block
+    a.j0 = j0;
+    a.bw = (int)(jn - j0);
+    a.first = first;
+    first = 0;
+    j0 = jn;
     const int64_t sb0 = (a.j0 / S) * S;
     const int64_t sb1 = (sb0 + S) < d ? (sb0 + S) : d;
     a.ecol = a.j0 - sb0;
@@ -614,6 +643,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
         s = launch_colloop<-2, true>(a, st);
       else switch (group) {
         case 0: s = launch_colloop<0, true>(a, st); break;
+        case 16: s = launch_colloop<16, true>(a, st); break;
         case 32: s = launch_colloop<32, true>(a, st); break;
         case 64: s = launch_colloop<64, true>(a, st); break;
         case 128: s = launch_colloop<128, true>(a, st); break;
@@ -623,6 +653,7 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
       s = launch_colloop<-2, false>(a, st);
     } else switch (group) {
       case 0: s = launch_colloop<0, false>(a, st); break;
+      case 16: s = launch_colloop<16, false>(a, st); break;
       case 32: s = launch_colloop<32, false>(a, st); break;
       case 64: s = launch_colloop<64, false>(a, st); break;
       case 128: s = launch_colloop<128, false>(a, st); break;
@@ -639,8 +670,8 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
       t.Ah = w.Ehb;
       t.Al = w.Elb;
       t.rowscale = w.einv_b;
-      t.Bh = w.Uth + b * d * BLK + j1 * 32;
-      t.Bl = w.Utl + b * d * BLK + j1 * 32;
+      t.Bh = w.Uth + b * d * BLK + kslab0 + j1 * 32;
+      t.Bl = w.Utl + b * d * BLK + kslab0 + j1 * 32;
       t.N = sb1 - j1;
       t.K = a.bw;
       if ((s = tgemm_enqueue(t, st)) != GPTQ_OK) return s;

@@ -92,6 +92,7 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert q(G.make_qcfg(4, group_size=48)) == G.GPTQ_ERR_INVALID_ARG        # group must divide d
     assert q(G.make_qcfg(4, group_size=384), d=512) == G.GPTQ_ERR_INVALID_ARG  # group must divide d
     assert q(G.make_qcfg(4, group_size=24), d=480) == G.GPTQ_ERR_UNSUPPORTED  # not 16 nor a multiple of 32
+    assert q(G.make_qcfg(4, group_size=96, factor="R"), d=480) == G.GPTQ_ERR_UNSUPPORTED  # cut groups: U form
     assert q(G.make_qcfg(4, group_size=256, factor="R"), d=512) == G.GPTQ_ERR_UNSUPPORTED  # R form: groups <= 128
     bad = G.make_qcfg(4)
     bad.factor = 7

@@ -104,6 +104,9 @@ CASES = [
     ("ternary-g128-static", S.scaled(S.CONFIGS["opt175b-fc1-ternary"], m=512, d=1024, n_tokens=16384), True),
     ("2b-g32-d224", S.scaled(S.CONFIGS["opt175b-fc1-2bit"], m=130, d=224, n_tokens=5000, group=32), False),
     ("3b-sym-g128-static", S.scaled(S.CONFIGS["opt13b-attn"], m=256, d=1024, n_tokens=8192, grid="sym"), True),
+    ("3b-g16", S.scaled(S.CONFIGS["opt13b-attn"], m=128, d=512, n_tokens=8192, group=16), False),
+    ("4b-g96-d480", S.scaled(S.CONFIGS["opt2.7b-fc1"], m=128, d=480, n_tokens=8192, group=96), False),
+    ("4b-g96-d480-static", S.scaled(S.CONFIGS["opt2.7b-fc1"], m=128, d=480, n_tokens=8192, group=96), True),
 ]
 
 
@@ -118,7 +121,7 @@ def test_act_order_layer_parity(label, cfg, static):
 
 
 # the R form takes static groups of any size and dynamic groups up to 128
-CASES_R = [c for c in CASES if c[2] or c[1].group <= 128]
+CASES_R = [c for c in CASES if c[2] or c[1].group in (0, 16, 32, 64, 128)]
 
 
 @pytest.mark.parametrize("label,cfg,static", CASES_R, ids=[c[0] for c in CASES_R])

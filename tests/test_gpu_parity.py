@@ -205,6 +205,11 @@ _SCALED = [
     # several super-blocks with a ragged last block, and groups of three blocks
     ("3b-g32-d992-ragged", S.scaled(S.CONFIGS["opt13b-attn"], m=300, d=992, n_tokens=8192, group=32)),
     ("4b-g384-d1152", S.scaled(S.CONFIGS["opt2.7b-fc1"], m=192, d=1152, n_tokens=8192, group=384)),
+    # groups not aligned to the 128-column block: 16 inside a lane's columns; 96 and 192 cut the lazy blocks
+    ("3b-g16", S.scaled(S.CONFIGS["opt13b-attn"], m=256, d=512, n_tokens=8192, group=16)),
+    ("4b-g96-d480", S.scaled(S.CONFIGS["opt2.7b-fc1"], m=200, d=480, n_tokens=8192, group=96)),
+    ("3b-g192-d768", S.scaled(S.CONFIGS["opt13b-attn"], m=160, d=768, n_tokens=8192, group=192)),
+    ("2b-g160-d1280", S.scaled(S.CONFIGS["opt175b-fc1-2bit"], m=128, d=1280, n_tokens=8192, group=160)),
 ]
 
 
@@ -214,7 +219,7 @@ def test_layer_parity_scaled(label, cfg):
 
 
 # the R form (factor R = U^-1): every group size it takes (groups above 128 need U)
-_SCALED_R = [(label, cfg) for label, cfg in _SCALED if cfg.group <= 128]
+_SCALED_R = [(label, cfg) for label, cfg in _SCALED if cfg.group in (0, 16, 32, 64, 128)]
 
 
 @pytest.mark.parametrize("label,cfg", _SCALED_R, ids=[c[0] for c in _SCALED_R])

@@ -465,3 +465,41 @@ def test_hessian_factor_definition_and_relations():
     np.testing.assert_allclose(r2, [[np.sqrt(a - b * b / c), b / np.sqrt(c)], [0.0, np.sqrt(c)]], rtol=1e-15)
     with pytest.raises(np.linalg.LinAlgError):
         O.hessian_factor(np.array([[1.0, 2.0], [2.0, 1.0]]))
+
+
+@pytest.mark.parametrize("group", [16, 48, 96, 192])
+def test_groups_not_aligned_to_the_block_are_block_size_invariant(group):
+    """Group sizes that neither divide the 128-column block nor are multiples of
+    it: a group fitted at its first column sees every earlier update whatever
+    the block size, so the blocked loop at B in {1, 7, 32, 128} and the
+    unblocked loop give the same codes, grids and W_hat. (A fit on the
+    partially updated weights past the block end would depend on B.)"""
+    rng = np.random.default_rng(group)
+    m, d = 6, 384
+    x = rng.standard_normal((4 * d, d)) @ (rng.standard_normal((d, d)) / np.sqrt(d) + np.eye(d))
+    hd, _ = O.damp(O.hessian(x), 0.01)
+    u = O.inverse_hessian_factor(hd)
+    w = rng.standard_normal((m, d)) * 0.05
+    ref = O.gptq_quantize(w, u, 3, "asym", group, blocked=False)
+    for block in (1, 7, 32, 128):
+        r = O.gptq_quantize(w, u, 3, "asym", group, block=block)
+        near = ref.dist < 1e-9
+        assert np.all((r.codes == ref.codes) | near), block
+        np.testing.assert_allclose(r.scales, ref.scales, rtol=1e-10)
+        np.testing.assert_array_equal(r.zeros, ref.zeros)
+        np.testing.assert_allclose(r.w_hat, ref.w_hat, rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("group", [16, 96])
+def test_unaligned_groups_reduce_to_rtn_when_h_is_diagonal(group):
+    """With a diagonal H no error propagates: the codes are round-to-nearest
+    on groups of the original weights, for unaligned group sizes too."""
+    rng = np.random.default_rng(5)
+    m, d = 5, 384
+    hd = np.diag(rng.uniform(0.5, 2.0, d))
+    u = O.inverse_hessian_factor(hd)
+    w = rng.standard_normal((m, d)) * 0.05
+    g = O.gptq_quantize(w, u, 4, "asym", group)
+    r = O.rtn_quantize(w, 4, "asym", group)
+    np.testing.assert_array_equal(g.codes, r.codes)
+    np.testing.assert_array_equal(g.scales, r.scales)
