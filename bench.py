@@ -97,6 +97,9 @@ def parse():
                    help="quantize the columns in descending H_jj (desc_act)")
     p.add_argument("--block", action="store_true",
                    help="time the quantization of a whole OPT-175B block (q, k, v sharing one Hessian)")
+    p.add_argument("--sequential", action="store_true",
+                   help="with --block: calibrate each sublayer on the block's forward pass through the sublayers "
+                        "quantized before it (the block input is synthetic; the forward runs in torch)")
     p.add_argument("--gemv", action="store_true",
                    help="time the dequantizing matrix-vector product over an OPT-175B block instead")
     p.add_argument("--static-groups", action="store_true",
@@ -394,7 +397,55 @@ class BlockGroup:
         return st
 
 
+def sequential_block_bench(args):
+    """One step = the OPT-175B block quantized sublayer by sublayer, each on the
+    calibration input the block's forward pass produces through the sublayers
+    quantized before it (q, k, v on LN1(x); out on the attention output; fc1 on
+    LN2(h); fc2 on ReLU(fc1)). The forward passes (torch) and the library's
+    quantization are timed apart with HIP events."""
+    from post_weight_quantization_18_amd import opt_block as B
+    dev = torch.device("cuda:0")
+    shape = B.OPT175B
+    _say("sequential block: drawing the block input and the six weight matrices")
+    x = B.block_input(shape, dev)
+    sb = B.SequentialBlock(shape, dev, factor=args.factor)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        sb.run(x)
+        _say(f"sequential block warmup {i + 1}/{args.warmup} done: {sb.stage_s}")
+    fwd, quant = 0.0, {}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        sb.run(x)
+        fwd += sb.stage_s["forward_ms"]
+        for k, v in sb.stage_s["quantize_ms"].items():
+            quant[k] = quant.get(k, 0.0) + v
+        _say(f"sequential block step done: {sb.stage_s}")
+    wall = time.perf_counter() - t0
+    s_block = wall / args.steps
+    n_weights = sum(c.n_weights for c in sb.cfgs.values())
+    result = {
+        "metric": "OPT-175B block quantization time, sublayers calibrated sequentially (one GPU, forward passes "
+                  "included)",
+        "value": s_block, "unit": "s/block", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(s_block * 1e3, 3), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16 MFMA->f32/f64 (H), f64 (R), f32 (column loop), split-f16 MFMA->f32 (trailing GEMM); "
+                 "forward f16 products, f32 attention",
+        "data": "synthetic block input (correlated Gaussian, 128 sequences of 2048 tokens) and synthetic weights",
+        "config": {"workload": "OPT-175B decoder block: q, k, v, out 12288x12288, fc1 49152x12288, fc2 12288x49152; "
+                               "3-bit asym g128; each sublayer calibrated on the forward pass through the quantized "
+                               "sublayers before it; 262144 tokens", "weights": n_weights, "factor": args.factor},
+        "weights_per_s": n_weights / s_block,
+        "forward_ms": round(fwd / args.steps, 3),
+        "quantize_ms": {k: round(v / args.steps, 3) for k, v in quant.items()},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def block_bench(args):
+    if args.sequential:
+        sequential_block_bench(args)
+        return
     dev = torch.device("cuda:0")
     groups = []
     for label, names in BLOCK_GROUPS:
