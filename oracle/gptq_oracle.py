@@ -587,14 +587,19 @@ def unpack_codes(words, bits: int, d: int) -> np.ndarray:
 # A100, 4.5x on A6000) over fp16. One token (batch 1) is a matrix-vector
 # product with every layer's dequantized weights.
 # ---------------------------------------------------------------------------
-def dequant_matvec(words, scales, zeros, bits: int, group: int, x) -> np.ndarray:
+def dequant_matvec(words, scales, zeros, bits: int, group: int, x, g_idx=None) -> np.ndarray:
     """y[r] = sum_j s[r, g(j)] (c[r, j] - z[r, g(j)]) x[j] in fp64, with c the
-    codes unpacked from the row bitstreams, g(j) = j // group (0 for one grid
-    per row). The product of W_hat = s (c - z) with x."""
+    codes unpacked from the row bitstreams and g(j) = j // group (0 for one grid
+    per row), or g(j) = g_idx[j] when a group index is given (act-order
+    without static groups, where the k-th group is the k-th run of columns in
+    the quantization order). The product of W_hat = s (c - z) with x."""
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[0]
     c = unpack_codes(words, bits, d)
-    gidx = np.arange(d) // group if group else np.zeros(d, dtype=np.int64)
+    if g_idx is not None:
+        gidx = np.asarray(g_idx, dtype=np.int64)
+    else:
+        gidx = np.arange(d) // group if group else np.zeros(d, dtype=np.int64)
     s = np.asarray(scales, dtype=np.float64)[:, gidx]
     z = np.asarray(zeros).astype(np.int64)[:, gidx]
     return (s * (c - z)) @ x

@@ -71,3 +71,26 @@ def test_matches_the_quantizers_w_hat(group, grid, bits):
     v = rng.standard_normal(d)
     y = O.dequant_matvec(O.pack_codes(res.codes, bits), res.scales, res.zeros, bits, group, v)
     np.testing.assert_allclose(y, res.w_hat @ v, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("bits,group", [(3, 16), (4, 32)])
+def test_group_index_matches_the_act_order_quantizers_w_hat(bits, group):
+    """Act-order without static groups: the codes stay in natural column order
+    and g_idx names every column's group; y from (codes, scales, zeros, g_idx)
+    equals the ordered quantizer's own W_hat times x."""
+    rng = np.random.default_rng(bits * group)
+    m, d, n = 5, 64, 300
+    x_cal = (rng.standard_normal((n, d)) * np.linspace(0.2, 3.0, d)).astype(np.float16)
+    w = rng.standard_normal((m, d)) * 0.05
+    res, g_idx, perm, _, _, _ = O.quantize_layer_act_order(w, x_cal, bits, "asym", group, static_groups=False,
+                                                           block=16)
+    assert not np.array_equal(g_idx, np.arange(d) // group)   # the groups are not natural runs
+    v = rng.standard_normal(d)
+    y = O.dequant_matvec(O.pack_codes(res.codes, bits), res.scales, res.zeros, bits, group, v, g_idx=g_idx)
+    np.testing.assert_allclose(y, res.w_hat @ v, rtol=1e-12, atol=1e-15)
+    # columns sorted by group (stable) are runs of `group` columns: the natural
+    # grouped product of the sorted codes against x in that order is the same y
+    order = np.argsort(g_idx, kind="stable")
+    assert np.array_equal(g_idx[order], np.arange(d) // group)
+    y_sorted = O.dequant_matvec(O.pack_codes(res.codes[:, order], bits), res.scales, res.zeros, bits, group, v[order])
+    np.testing.assert_allclose(y_sorted, y, rtol=1e-12, atol=1e-15)
