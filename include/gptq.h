@@ -119,9 +119,11 @@ size_t gptq_workspace_bytes(int32_t which, int64_t m, int64_t d, int64_t n, cons
  *  X        device, fp16, token-major [n][ldx]; 16-byte aligned, ldx % 8 == 0.
  *  d        features, d % 32 == 0. n tokens in this call, n >= 0 (n = 0 with
  *           accumulate = 0 zeroes the lower triangle).
- *  Products are exact fp16 x fp16 -> fp32 on the matrix cores; partial sums are
- *  carried in fp32 with their rounding error folded back every 1024 tokens and
- *  combined in fp64, so H is accurate to a fraction of an fp32 ulp.
+ *  Products are exact fp16 x fp16 -> fp32 on the matrix cores. Each 1024-token
+ *  window is summed in fp32 (64 matrix steps, one rounding each) and folded
+ *  into a compensated running sum, combined in fp64 at the end: the error does
+ *  not grow with n beyond the windows' own roundings, each entry within
+ *  2^-17 sum_t 2|x_ti x_tj| (about 1e-7 relative in Frobenius norm measured).
  *  Call it once per chunk of tokens with accumulate = 1 after the first. */
 gptq_status_t gptq_accumulate_hessian(void* H, int32_t h_dtype, int64_t d, int64_t ldh,
                                       const void* X, int64_t n, int64_t ldx, int32_t accumulate,
@@ -261,13 +263,45 @@ gptq_status_t gptq_quantize_layer_ordered(const void* W, int32_t w_dtype, int64_
  *           writes (4-byte aligned).  scales / zeros: device [m][ngroups] as
  *           written by gptq_quantize_layer.
  *  bits     2, 3, 4 or 8 (ternary codes use bits = 2).
- *  group_size 0, or a multiple of 32 dividing d (natural column groups; the
- *           g_idx layout of act-order without static groups is not taken).
+ *  group_size 0, or a multiple of 32 dividing d (natural column groups; for
+ *           the g_idx layout of act-order without static groups see
+ *           gptq_gemv_prepare_act_order).
  *  x        device fp16 [d], 16-byte aligned.   y device float [m], out.
  *  d % 32 == 0. Sums are carried in fp32: per 32-code chunk sum c x and
  *  sum x, then s (sum c x - z sum x), added over chunks and across a wave. */
 gptq_status_t gptq_dequant_gemv(const uint32_t* qcodes, const float* scales, const uint8_t* zeros, int64_t m,
                                 int64_t d, int32_t bits, int32_t group_size, const void* x, float* y, void* stream);
+
+/* Act-order codes for the generation product (ordered quantization without
+ * static groups: codes in natural column order, g_idx[j] the group of column
+ * j). Same sources as gptq_dequant_gemv and gptq_act_order. The group index
+ * scatters a row's groups over the columns; this call, made once per layer,
+ * sorts the columns by group (ties by column index) into col_perm, so that
+ * group k is slots [k group_size, (k + 1) group_size), and rewrites every row's
+ * codes in that order. gptq_dequant_gemv_perm then computes the same y as
+ * sum_j s[r][g_idx[j]] (c[r][j] - z[r][g_idx[j]]) x[j] from the rewritten codes,
+ * the unchanged scales and zeros, and x read in col_perm order.
+ *  qcodes   device uint32 [m][d * bits / 32], natural order (4-byte aligned).
+ *  g_idx    device int32 [d], as gptq_quantize_layer_ordered writes it.
+ *  qcodes_out device uint32 [m][d * bits / 32], out; may not alias qcodes.
+ *  col_perm device int32 [d], out.
+ *  info     device int32, out: 0 when every group holds exactly group_size
+ *           columns and every g_idx lies in [0, d / group_size); otherwise the
+ *           number of faults found (col_perm and qcodes_out are then
+ *           meaningless, but every access stays in bounds).
+ *  bits     2, 3, 4 or 8;  group_size a multiple of 32 dividing d (> 0). */
+gptq_status_t gptq_gemv_prepare_act_order(const uint32_t* qcodes, const int32_t* g_idx, int64_t m, int64_t d,
+                                          int32_t bits, int32_t group_size, uint32_t* qcodes_out, int32_t* col_perm,
+                                          int32_t* info, void* stream);
+
+/* gptq_dequant_gemv for codes in col_perm order (gptq_gemv_prepare_act_order):
+ * x_perm[p] = x[col_perm[p]] is gathered into the caller's x_perm (device fp16
+ * [d], 16-byte aligned, not aliasing x; its contents are overwritten), then
+ * y = W x as gptq_dequant_gemv on (qcodes, scales, zeros, x_perm). Entries of
+ * col_perm outside [0, d) read x[0]. Other arguments as gptq_dequant_gemv. */
+gptq_status_t gptq_dequant_gemv_perm(const uint32_t* qcodes, const float* scales, const uint8_t* zeros, int64_t m,
+                                     int64_t d, int32_t bits, int32_t group_size, const int32_t* col_perm,
+                                     const void* x, void* x_perm, float* y, void* stream);
 
 /* Bit packing of integer codes (one byte per code) into the row-wise LSB-first
  * bitstream gptq_quantize_layer writes (which packs in its own epilogue).

@@ -219,6 +219,33 @@ gptq_status_t gptq_dequant_gemv(const uint32_t* qcodes, const float* scales, con
   return dq_gemv_enqueue(qcodes, scales, zeros, m, d, bits, group_size, (const half_t*)x, y, (hipStream_t)stream);
 }
 
+gptq_status_t gptq_gemv_prepare_act_order(const uint32_t* qcodes, const int32_t* g_idx, int64_t m, int64_t d,
+                                          int32_t bits, int32_t group_size, uint32_t* qcodes_out, int32_t* col_perm,
+                                          int32_t* info, void* stream) {
+  if (!qcodes || !g_idx || !qcodes_out || !col_perm || !info || m <= 0 || d <= 0 || d % 32) return GPTQ_ERR_INVALID_ARG;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_INVALID_ARG;
+  if (group_size <= 0 || group_size % 32 || d % group_size || d > INT32_MAX) return GPTQ_ERR_INVALID_ARG;
+  if (qcodes_out == qcodes) return GPTQ_ERR_INVALID_ARG;
+  GPTQ_CHECK_DEVICE();
+  return gemv_act_order_prepare(qcodes, g_idx, m, d, bits, group_size, qcodes_out, col_perm, info,
+                                (hipStream_t)stream);
+}
+
+gptq_status_t gptq_dequant_gemv_perm(const uint32_t* qcodes, const float* scales, const uint8_t* zeros, int64_t m,
+                                     int64_t d, int32_t bits, int32_t group_size, const int32_t* col_perm,
+                                     const void* x, void* x_perm, float* y, void* stream) {
+  if (!qcodes || !scales || !zeros || !col_perm || !x || !x_perm || !y || m <= 0 || d <= 0 || d % 32)
+    return GPTQ_ERR_INVALID_ARG;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_INVALID_ARG;
+  if (group_size < 0 || (group_size && (group_size % 32 || d % group_size))) return GPTQ_ERR_INVALID_ARG;
+  if (!aligned(x_perm, 16) || !aligned(qcodes, 4) || x_perm == x) return GPTQ_ERR_INVALID_ARG;
+  GPTQ_CHECK_DEVICE();
+  const hipStream_t st = (hipStream_t)stream;
+  gptq_status_t rc = gather_x_enqueue((const half_t*)x, col_perm, d, (half_t*)x_perm, st);
+  if (rc != GPTQ_OK) return rc;
+  return dq_gemv_enqueue(qcodes, scales, zeros, m, d, bits, group_size, (const half_t*)x_perm, y, st);
+}
+
 gptq_status_t gptq_pack_codes(const uint8_t* codes, int64_t m, int64_t d, int32_t bits, uint32_t* out,
                               void* stream) {
   if (!codes || !out || m <= 0 || d <= 0) return GPTQ_ERR_INVALID_ARG;

@@ -26,7 +26,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgptq_mi355x.so")
+# GPTQ_MI355X_LIB may name another build of the library (the debug build,
+# libgptq_mi355x_debug.so, for instance)
+LIB_PATH = os.environ.get("GPTQ_MI355X_LIB") or os.path.join(_HERE, "libgptq_mi355x.so")
 
 GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP, GPTQ_ERR_UNSUPPORTED = range(5)
 GPTQ_F16, GPTQ_F32, GPTQ_F64 = 0, 1, 2
@@ -36,7 +38,8 @@ WS_ACCUMULATE_HESSIAN, WS_PREPARE_HINV, WS_QUANTIZE_LAYER = 0, 1, 2
 EXPORTED = ["gptq_abi_version", "gptq_status_string", "gptq_workspace_bytes", "gptq_accumulate_hessian",
             "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_act_order", "gptq_permute_hessian",
             "gptq_quantize_layer_ordered", "gptq_dequant_gemv", "gptq_pack_codes", "gptq_trace_start",
-            "gptq_trace_stop", "gptq_trace_family", "gptq_accumulate_hessian_noalloc", "gptq_prepare_hchol"]
+            "gptq_trace_stop", "gptq_trace_family", "gptq_accumulate_hessian_noalloc", "gptq_prepare_hchol",
+            "gptq_gemv_prepare_act_order", "gptq_dequant_gemv_perm"]
 TRACE_FAMILIES = 14
 
 
@@ -85,6 +88,10 @@ def load_library(path: str = LIB_PATH):
                                                 vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gptq_dequant_gemv.restype = i32
     lib.gptq_dequant_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp]
+    lib.gptq_gemv_prepare_act_order.restype = i32
+    lib.gptq_gemv_prepare_act_order.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp]
+    lib.gptq_dequant_gemv_perm.restype = i32
+    lib.gptq_dequant_gemv_perm.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]
     lib.gptq_pack_codes.restype = i32
     lib.gptq_pack_codes.argtypes = [vp, i64, i64, i32, vp, vp]
     lib.gptq_accumulate_hessian_noalloc.restype = i32
@@ -317,6 +324,51 @@ def dequant_gemv(qcodes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor
         y = torch.empty(m, dtype=torch.float32, device=x.device)
     _check(lib.gptq_dequant_gemv(_ptr(qcodes), _ptr(scales), _ptr(zeros), m, d, bits, group_size, _ptr(x), _ptr(y),
                                  _stream(x.device)), "gptq_dequant_gemv")
+    return y
+
+
+def gemv_prepare_act_order(qcodes: torch.Tensor, g_idx: torch.Tensor, bits: int, group_size: int):
+    """Act-order codes (natural column order, group index g_idx) rewritten with
+    the columns sorted by group. Returns (qcodes in col_perm order, col_perm
+    int32 [d], info int32 device scalar: 0 when every group holds group_size
+    columns)."""
+    lib = load_library()
+    for t, n in ((qcodes, "qcodes"), (g_idx, "g_idx")):
+        _need_cuda(t, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if g_idx.dtype != torch.int32:
+        raise ValueError("g_idx must be int32")
+    m, d = qcodes.shape[0], g_idx.shape[0]
+    out = torch.empty_like(qcodes)
+    col_perm = torch.empty(d, dtype=torch.int32, device=qcodes.device)
+    info = torch.empty(1, dtype=torch.int32, device=qcodes.device)
+    _check(lib.gptq_gemv_prepare_act_order(_ptr(qcodes), _ptr(g_idx), m, d, bits, group_size, _ptr(out),
+                                           _ptr(col_perm), _ptr(info), _stream(qcodes.device)),
+           "gptq_gemv_prepare_act_order")
+    return out, col_perm, info
+
+
+def dequant_gemv_perm(qcodes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, bits: int, group_size: int,
+                      col_perm: torch.Tensor, x: torch.Tensor, x_perm: torch.Tensor | None = None,
+                      y: torch.Tensor | None = None) -> torch.Tensor:
+    """y fp32 [m] = W x for codes in col_perm order (gemv_prepare_act_order), x
+    fp16 [d] in natural order; x_perm is the fp16 [d] buffer the gather uses."""
+    lib = load_library()
+    for t, n in ((qcodes, "qcodes"), (scales, "scales"), (zeros, "zeros"), (col_perm, "col_perm"), (x, "x")):
+        _need_cuda(t, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if x.dtype != torch.float16 or scales.dtype != torch.float32 or zeros.dtype != torch.uint8:
+        raise ValueError("x fp16, scales fp32, zeros uint8")
+    m, d = qcodes.shape[0], x.shape[0]
+    if x_perm is None:
+        x_perm = torch.empty(d, dtype=torch.float16, device=x.device)
+    if y is None:
+        y = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check(lib.gptq_dequant_gemv_perm(_ptr(qcodes), _ptr(scales), _ptr(zeros), m, d, bits, group_size,
+                                      _ptr(col_perm), _ptr(x), _ptr(x_perm), _ptr(y), _stream(x.device)),
+           "gptq_dequant_gemv_perm")
     return y
 
 

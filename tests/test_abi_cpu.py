@@ -124,6 +124,20 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert lib.gptq_dequant_gemv(fake, fake, fake, 4, 96, 3, 48, fake, fake, None) == G.GPTQ_ERR_INVALID_ARG
     assert lib.gptq_dequant_gemv(fake, fake, fake, 4, 64, 3, 0, _vp((1 << 20) + 2), fake, None) == G.GPTQ_ERR_INVALID_ARG
     assert lib.gptq_dequant_gemv(None, fake, fake, 4, 64, 3, 0, fake, fake, None) == G.GPTQ_ERR_INVALID_ARG
+    # act-order product: group 0 (no groups to sort), group not dividing d, aliasing output, bad bits
+    assert lib.gptq_gemv_prepare_act_order(fake, fake, 4, 64, 3, 0, _vp((2 << 20)), fake, fake,
+                                           None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_gemv_prepare_act_order(fake, fake, 4, 96, 3, 64, _vp((2 << 20)), fake, fake,
+                                           None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_gemv_prepare_act_order(fake, fake, 4, 64, 3, 32, fake, fake, fake, None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_gemv_prepare_act_order(fake, fake, 4, 64, 5, 32, _vp((2 << 20)), fake, fake,
+                                           None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_dequant_gemv_perm(fake, fake, fake, 4, 64, 3, 32, None, fake, _vp((2 << 20)), fake,
+                                      None) == G.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_dequant_gemv_perm(fake, fake, fake, 4, 64, 3, 32, fake, fake, fake, fake,
+                                      None) == G.GPTQ_ERR_INVALID_ARG   # x_perm aliases x
+    assert lib.gptq_dequant_gemv_perm(fake, fake, fake, 4, 64, 3, 32, fake, fake, _vp((2 << 20) + 4), fake,
+                                      None) == G.GPTQ_ERR_INVALID_ARG   # x_perm misaligned
     # pack: d*bits not a multiple of 32
     assert lib.gptq_pack_codes(fake, 4, 12, 3, fake, None) == G.GPTQ_ERR_INVALID_ARG
     assert lib.gptq_pack_codes(fake, 4, 64, 5, fake, None) == G.GPTQ_ERR_INVALID_ARG

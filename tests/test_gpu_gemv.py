@@ -62,9 +62,16 @@ def test_bit_exact_on_exactly_representable_inputs(m, d, bits, group):
     np.testing.assert_array_equal(y, O.dequant_matvec(words, s, z, bits, group, x.astype(np.float64)))
 
 
+# Streaming form (d * bits % 128 == 0, groups dividing or multiples of 2048):
+# 4096/3/128, 2560/4/0, 12288/3/128, 1024/2/32, 49152/3/128, 640/8/64,
+# 1024/3/1024, 8192/2/4096, 6144/3/32 (a ragged last slab: 6144 = 3 slabs;
+# 2560 = 1.25 slabs) and m not a multiple of the 4 rows of a wave; the
+# chunked form: 3072/3/96 and 12288/4/3072 (groups that do not tile the slab),
+# 2080/3/32 (d * bits % 128 != 0)
 @pytest.mark.parametrize("m,d,bits,group", [(1000, 4096, 3, 128), (777, 2560, 4, 0), (129, 12288, 3, 128),
                                             (256, 1024, 2, 32), (64, 49152, 3, 128), (100, 640, 8, 64),
-                                            (4096, 1024, 3, 1024)])
+                                            (4096, 1024, 3, 1024), (33, 8192, 2, 4096), (70, 6144, 3, 32),
+                                            (41, 3072, 3, 96), (9, 12288, 4, 3072), (50, 2080, 3, 32)])
 def test_against_the_oracle(m, d, bits, group):
     say(f"[case] gemv m={m} d={d} bits={bits} group={group}")
     c, s, z, x = _case(m, d, bits, group, seed=m + d + bits)
@@ -97,5 +104,98 @@ def test_with_the_quantizers_outputs():
     zc = res["zeros"].cpu().numpy().astype(np.float64)[:, gidx]
     bound = (sc * (c + zc)) @ np.abs(vd)
     err = np.abs(y.cpu().double().numpy() - want)
+    say(f"  max err / bound = {float(np.max(err / bound)):.2e}")
+    assert np.all(err <= 4e-6 * bound)
+
+
+def _act_order_case(m, d, bits, group, seed, exact=False):
+    """Codes, scales, zeros and x as _case, and a group index that spreads every
+    group's columns over the row (each group keeps `group` columns)."""
+    c, s, z, x = _case(m, d, bits, group, seed, exact)
+    g_idx = np.random.default_rng(seed + 1).permutation(np.arange(d) // group).astype(np.int32)
+    return c, s, z, x, g_idx
+
+
+@pytest.mark.parametrize("m,d,bits,group,exact", [(5, 256, 3, 32, True), (37, 1024, 4, 128, True),
+                                                  (129, 4096, 3, 128, False), (64, 2080, 3, 32, False),
+                                                  (40, 3072, 2, 96, False), (8, 640, 8, 64, True)])
+def test_act_order_product(m, d, bits, group, exact):
+    """gptq_gemv_prepare_act_order sorts the columns by group (col_perm equals
+    a stable argsort of g_idx) and rewrites the codes in that order (bit-exact
+    against packing the permuted codes); gptq_dequant_gemv_perm then matches the
+    oracle's product with the group index (bit-exact on exact inputs, within
+    the rounding bound otherwise)."""
+    say(f"[case] act-order gemv m={m} d={d} bits={bits} group={group} exact={exact}")
+    c, s, z, x, g_idx = _act_order_case(m, d, bits, group, seed=m + d + bits, exact=exact)
+    words = O.pack_codes(c, bits)
+    qd = torch.from_numpy(words.view(np.int32)).to(DEV)
+    q2, col_perm, info = G.gemv_prepare_act_order(qd, torch.from_numpy(g_idx).to(DEV), bits, group)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    want_perm = np.argsort(g_idx, kind="stable")
+    assert np.array_equal(col_perm.cpu().numpy(), want_perm)
+    assert np.array_equal(q2.cpu().numpy().view(np.uint32), O.pack_codes(c[:, want_perm], bits))
+    y = G.dequant_gemv_perm(q2, torch.from_numpy(s.astype(np.float32)).to(DEV),
+                            torch.from_numpy(z.astype(np.uint8)).to(DEV), bits, group, col_perm,
+                            torch.from_numpy(x).to(DEV))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    xd = x.astype(np.float64)
+    want = O.dequant_matvec(words, s, z, bits, group, xd, g_idx=g_idx)
+    if exact:
+        np.testing.assert_array_equal(y, want)
+    else:
+        bound = (s[:, g_idx] * (c + z[:, g_idx])) @ np.abs(xd)
+        err = np.abs(y - want)
+        say(f"  max err / bound = {float(np.max(err / bound)):.2e}")
+        assert np.all(err <= 4e-6 * bound)
+
+
+def test_act_order_prepare_reports_bad_group_index():
+    """A group index with a group of the wrong size, or out of range, is
+    reported in info (the outputs are then meaningless but stay in bounds)."""
+    say("[case] act-order gemv prepare with a bad group index")
+    m, d, bits, group = 4, 256, 3, 32
+    c, _, _, _ = _case(m, d, bits, group, seed=3)
+    qd = torch.from_numpy(O.pack_codes(c, bits).view(np.int32)).to(DEV)
+    g = (np.arange(d) // group).astype(np.int32)
+    g[5] = 1            # group 0 short by one, group 1 one too many
+    _, _, info = G.gemv_prepare_act_order(qd, torch.from_numpy(g).to(DEV), bits, group)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 2
+    g[5] = 99           # out of range and group 0 short
+    _, _, info = G.gemv_prepare_act_order(qd, torch.from_numpy(g).to(DEV), bits, group)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 2
+
+
+def test_act_order_product_on_the_ordered_quantizers_outputs():
+    """A layer quantized in act-order without static groups on the GPU, then y
+    from its natural-order codes and g_idx through the two act-order calls,
+    against the layer's own W_hat x in fp64."""
+    cfg = S.scaled(S.CONFIGS["opt13b-attn"], m=256, d=1024, n_tokens=8192)
+    say(f"[case] act-order gemv on an ordered layer m={cfg.m} d={cfg.d} bits={cfg.bits} group={cfg.group}")
+    w, xcal = S.make_layer(cfg)
+    wd, xd = w.to(DEV), xcal.to(DEV)
+    H = torch.empty(cfg.d, cfg.d, dtype=torch.float64, device=DEV)
+    G.accumulate_hessian(H, xd, accumulate=False)
+    perm = G.act_order(H)
+    Hp = G.permute_hessian(H, perm)
+    U, info, _ = G.prepare_hinv(Hp, cfg.damp)
+    res = G.quantize_layer_ordered(wd, U, perm, cfg.bits, cfg.group, cfg.grid, static_groups=False)
+    q2, col_perm, pinfo = G.gemv_prepare_act_order(res["qcodes"], res["g_idx"], cfg.bits, cfg.group)
+    v = torch.from_numpy(np.random.default_rng(4).standard_normal(cfg.d).astype(np.float16)).to(DEV)
+    y = G.dequant_gemv_perm(q2, res["scales"], res["zeros"], cfg.bits, cfg.group, col_perm, v)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0 and int(pinfo.item()) == 0
+    g_idx = res["g_idx"].cpu().numpy()
+    assert not np.array_equal(g_idx, np.arange(cfg.d) // cfg.group)
+    w_hat = res["w_hat"].cpu().double().numpy()
+    vd = v.cpu().double().numpy()
+    c = O.unpack_codes(res["qcodes"].cpu().numpy().view(np.uint32), cfg.bits, cfg.d)
+    sc = res["scales"].cpu().double().numpy()[:, g_idx]
+    zc = res["zeros"].cpu().numpy().astype(np.float64)[:, g_idx]
+    bound = (sc * (c + zc)) @ np.abs(vd)
+    err = np.abs(y.cpu().double().numpy() - w_hat @ vd)
     say(f"  max err / bound = {float(np.max(err / bound)):.2e}")
     assert np.all(err <= 4e-6 * bound)
