@@ -1,6 +1,10 @@
 """Build libgptq_mi355x.so (gfx950) in-tree with hipcc.
 
-    python -m post_weight_quantization_18_amd.build
+    python -m post_weight_quantization_18_amd.build [--debug]
+
+--debug builds libgptq_mi355x_debug.so instead: -DGPTQ_DEBUG turns on the
+device-side bounds checks (GPTQ_DASSERT), objects under _build/debug/. The
+binding loads it when GPTQ_MI355X_LIB names it.
 
 Each .hip source is compiled to an object under _build/ (in parallel) and the
 objects are linked into post_weight_quantization_18_amd/libgptq_mi355x.so.
@@ -19,6 +23,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgptq_mi355x.so")
+LIB_DEBUG = os.path.join(PKG, "libgptq_mi355x_debug.so")
 SOURCES = ["gptq_api.hip", "syrk.hip", "chain.hip", "quant.hip", "trail.hip", "order.hip", "gemv.hip", "trace.hip",
            "colloop_row.hip", "colloop_g16.hip", "colloop_g32.hip", "colloop_g64.hip", "colloop_g128.hip", "colloop_wide.hip",
            "colloop_static.hip"]
@@ -38,19 +43,22 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+def build(verbose: bool = False, debug: bool = False) -> str:
+    bdir = os.path.join(BUILD, "debug") if debug else BUILD
+    lib = LIB_DEBUG if debug else LIB
+    flags = FLAGS + (["-DGPTQ_DEBUG"] if debug else [])
+    os.makedirs(bdir, exist_ok=True)
+    objs = [os.path.join(bdir, s.replace(".hip", ".o")) for s in SOURCES]
+    cmds = [[HIPCC, *flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))

@@ -157,6 +157,7 @@ template <int KT>
 __device__ __forceinline__ void update_tile(double* A, int64_t d, int64_t ka, int64_t K, int64_t c0, int64_t c1,
                                             int ti, int tj, double (*As)[KT + 1], double (*Bs)[64 + 1]) {
   const int64_t i0 = c0 + (int64_t)ti * 64, j0 = c0 + (int64_t)tj * 64;
+  GPTQ_DASSERT(ti >= tj && i0 < d && j0 < c1 && ka >= 0 && ka + K <= d);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
   double4v acc[2][2];

@@ -204,6 +204,7 @@ __global__ __launch_bounds__(CL_THREADS) void colloop_kernel(ColArgs a) {
   static_assert(!RF || G != -1, "the R form fits groups within a block or from the original weights");
   const int tid = threadIdx.x;
   const int bw = a.bw;
+  GPTQ_DASSERT(bw > 0 && bw <= BLK && bw % 32 == 0 && a.j0 >= 0 && a.j0 + bw <= a.d);
   // strictly upper part of the block's U (zeros on and below the diagonal);
   // R form: U_bb from the compact block inverses (row pitch BLK)
   for (int idx = tid; idx < BLK * BLK / 4; idx += CL_THREADS) {

@@ -436,6 +436,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* codes, int64_t
   __shared__ __attribute__((aligned(16))) uint8_t cs[STAGE > 0 ? STAGE : 16];
   const int64_t r = blockIdx.x;
   if (r >= m) return;
+  GPTQ_DASSERT(d % 32 == 0 && (d * bits) % 32 == 0 && (group == 0 || d % group == 0));
   const uint8_t* crow = codes + r * ldc;
   if constexpr (STAGE > 0) {
     for (int64_t k = threadIdx.x; k < d / 16; k += 256) *(uint4*)(cs + 16 * k) = *(const uint4*)(crow + 16 * k);

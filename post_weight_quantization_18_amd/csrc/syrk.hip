@@ -18,7 +18,8 @@
 //    bank conflicts. v_mfma_f32_32x32x16_f16: fp16 x fp16 products are exact.
 //  * Accuracy: every 1024 tokens the fp32 accumulators are folded into a
 //    second fp32 register (Fast2Sum) and the rounding error is put back into the
-//    MFMA accumulator, so the partial sum is carried to ~2^-48 relative; the
+//    MFMA accumulator, so the running sum loses nothing to the fold: what
+//    remains are the roundings of the 64 matrix steps inside each window. The
 //    final value is outer + acc in fp64, and split-K partials are summed in a
 //    fixed order in fp64 (deterministic).
 #include <mutex>
@@ -181,6 +182,7 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
   const int t = seg_t[sg];
   int bi, bj;
   if (!tile_coords(t, a.d, bi, bj)) continue;  // empty slot (uniform)
+  GPTQ_DASSERT(bj <= 2 * bi + 1 && (int64_t)bi * TI < a.d && t < a.ntiles);
   const int64_t I0 = (int64_t)bi * TI, J0 = (int64_t)bj * TJ;
   double* const part_out = seg_p[sg] < 0 ? nullptr : a.part + (int64_t)seg_p[sg] * TI * TJ;
 
@@ -221,6 +223,7 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
       const bool ok = ((e & 1) ? okI1 : okI0) && (RW * w + 2 * e + rI) < rows;
       if (!ok) src = (const half_t*)kZero16;
     }
+    GPTQ_DASSERT(src == (const half_t*)kZero16 || (src >= a.X && src + 8 <= a.X + (a.n - 1) * a.ldx + a.d));
     dma16(src, ring_lds + b * STAGE_BYTES + (uint32_t)((RW * wu + 2 * e) * TI * 2));
   };
   auto issue_J = [&](int e, int64_t t0, int b, bool full) __attribute__((always_inline)) {
@@ -230,6 +233,7 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
       const bool ok = okJ && (RW * w + 4 * e + rJ) < rows;
       if (!ok) src = (const half_t*)kZero16;
     }
+    GPTQ_DASSERT(src == (const half_t*)kZero16 || (src >= a.X && src + 8 <= a.X + (a.n - 1) * a.ldx + a.d));
     dma16(src, ring_lds + b * STAGE_BYTES + KS * TI * 2 + (uint32_t)((RW * wu + 4 * e) * TJ * 2));
   };
   auto issue = [&](int64_t t0, int b) __attribute__((always_inline)) {

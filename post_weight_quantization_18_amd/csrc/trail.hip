@@ -53,6 +53,7 @@ __global__ __launch_bounds__(NT, 1) void tgemm_kernel(TgemmArgs a, int ntm, int 
   const int within = logical - grp * per_group;
   const int tm = first_m + within % gm, tn = within / gm;
   const int64_t I0 = (int64_t)tm * TM, J0 = (int64_t)tn * TN;
+  GPTQ_DASSERT(tm < ntm && tn < ntn && I0 < a.M && J0 < a.N && a.K % KS == 0);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
