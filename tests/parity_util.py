@@ -318,3 +318,34 @@ def assert_ordered_gates(stats, static_groups, group):
     assert stats["hp_exact"], stats
     assert stats["g_idx_exact"], stats
     assert_gates(stats)
+
+
+N_SAMPLE_ROWS = 256
+
+
+def sample_rows(m, seed, n=N_SAMPLE_ROWS):
+    """n distinct random rows plus the first and the last, sorted."""
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([rng.choice(m, min(n, m), replace=False), [0, m - 1]]))
+
+
+def device_factor_r(d, x, damp, dev=torch.device("cuda:0")):
+    """H over all tokens of x in one call (fp64), then R (fp64, the Cholesky
+    factor of H_d), as the benchmark runs them. Returns (H, R, lambda)."""
+    H = torch.empty(d, d, dtype=torch.float64, device=dev)
+    G.accumulate_hessian(H, x, accumulate=False)
+    R, info, lam = G.prepare_hchol(H, damp, r_dtype=torch.float64)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    return H, R, float(lam.item())
+
+
+def rows_of(res, rows, bits, d):
+    """Host copies of the quantizer's outputs on the given rows."""
+    rt = torch.as_tensor(rows, device=res["qcodes"].device)
+    q = res["qcodes"][rt].cpu().numpy().view(np.uint32)
+    return {"codes": O.unpack_codes(q, bits, d), "qcodes": q,
+            "scales": res["scales"][rt].cpu().numpy(),
+            "zeros": res["zeros"][rt].cpu().numpy().astype(np.int64),
+            "w_hat": res["w_hat"][rt].cpu().numpy(),
+            "err_sq": res["err_sq"][rt].cpu().numpy()}

@@ -1,0 +1,44 @@
+"""Resume logic of the block harness (host only): a layer counts as done when
+its results line and its output file exist; q, k and v share one input, so
+their group runs while any of its requested layers is missing."""
+
+import json
+import os
+
+import block_parity_harness as BH
+
+
+def _done(tmp_path, layers, with_npz=True):
+    with open(tmp_path / "results.jsonl", "w") as fh:
+        for l in layers:
+            fh.write(json.dumps({"config": BH.BLOCK, "layer": l}) + "\n")
+            if with_npz:
+                (tmp_path / f"{l}.npz").write_bytes(b"")
+
+
+def test_fresh_run_plans_every_group():
+    todo = BH.plan(list(BH.LAYERS), set())
+    assert [w for _, w in todo] == [["q", "k", "v"], ["out"], ["fc1"], ["fc2"]]
+
+
+def test_resume_continues_at_the_next_layer(tmp_path):
+    _done(tmp_path, ["q", "k", "v", "out"])
+    done = BH.completed(str(tmp_path))
+    assert done == {"q", "k", "v", "out"}
+    assert [w for _, w in BH.plan(list(BH.LAYERS), done)] == [["fc1"], ["fc2"]]
+
+
+def test_a_layer_without_its_outputs_is_not_done(tmp_path):
+    _done(tmp_path, ["q", "k"], with_npz=False)
+    (tmp_path / "q.npz").write_bytes(b"")
+    done = BH.completed(str(tmp_path))
+    assert done == {"q"}
+    todo = BH.plan(list(BH.LAYERS), done)
+    assert todo[0] == (["q", "k", "v"], ["k", "v"])
+
+
+def test_layer_work_counts():
+    flops, nbytes = BH.layer_work(BH.S.CONFIGS["opt175b-fc2"])
+    m, d, n = 12288, 49152, 262144
+    assert flops["syrk"] == n * d * (d + 1) and flops["chain"] == d ** 3 / 3
+    assert nbytes["x"] == 2 * n * d and nbytes["outputs"] == m * d * 3 // 8 + m * (d // 128) * 5 + 4 * m

@@ -68,7 +68,10 @@ def test_hessian_parity_toy(h_dtype, chunk):
     assert np.all(hg[np.triu_indices(d, 1)] == 7.0)   # strictly upper triangle untouched
 
 
-@pytest.mark.parametrize("n,d", [(3000, 96), (64, 320), (1, 32), (70000, 512)])
+# d = 2336 and 4192: several bands of 4 I-blocks and chunks of 8 J-blocks in the
+# tile order, a last band of 2 and of 1 I-blocks, an empty tile past d; 4192
+# has 306 tiles, so 50 go to the stream-K ranges
+@pytest.mark.parametrize("n,d", [(3000, 96), (64, 320), (1, 32), (70000, 512), (5000, 2336), (1100, 4192)])
 def test_hessian_parity_ragged(n, d):
     say(f"[case] hessian ragged n={n} d={d}")
     rng = np.random.default_rng(n + d)
@@ -76,9 +79,20 @@ def test_hessian_parity_ragged(n, d):
     H = torch.empty(d, d, dtype=torch.float64, device=DEV)
     G.accumulate_hessian(H, x.to(DEV), accumulate=False)
     torch.cuda.synchronize()
-    rel = lower_rel_fro(H.cpu().numpy(), O.hessian(x.numpy()))
-    say(f"  rel_fro={rel:.3e}")
-    assert rel <= 1e-7
+    hg = H.cpu().numpy()
+    ho = O.hessian(x.numpy())
+    rel = lower_rel_fro(hg, ho)
+    # elementwise: the fp16 products are exact in fp32 and each 16-token MFMA
+    # step rounds once; the 64 steps between folds can lose at most 64 fp32
+    # roundings of the running |sum|, bounded by 2 sum_t |x_ti x_tj| (twice
+    # that, for rounding inside the instruction); a missing or doubled tile is
+    # off by |H_ij|, ~1/sqrt(n) of that sum, far above the bound
+    habs = O.hessian(np.abs(x.numpy()))
+    il = np.tril_indices(d)
+    excess = np.abs(hg[il] - ho[il]) - 128 * 2.0 ** -24 * habs[il]
+    say(f"  rel_fro={rel:.3e} worst elementwise excess over the bound {excess.max():.3e}")
+    assert np.all(excess <= 0.0)
+    assert rel <= 5e-7
 
 
 def test_hessian_accumulate_and_empty():

@@ -1,6 +1,6 @@
 """Full-size layers through the C ABI, in the launch configuration the
 benchmark times (one gptq_accumulate_hessian call over all 262144 tokens, fp64
-H, fp32 U).
+H; the R factor for the OPT-175B layers, fp64 U for the OPT-13B one).
 
 * OPT-13B attention projection (5120 x 5120, 262144 tokens, 3-bit g128): the
   whole oracle runs on every row, and the usual parity gates apply.
@@ -38,7 +38,8 @@ import oracle as O
 from post_weight_quantization_18_amd import gptq as G
 from post_weight_quantization_18_amd import synthetic as S
 
-from parity_util import assert_gates, compare_layer, compare_rows, gpu_layer, oracle_factor, say
+from parity_util import (assert_gates, compare_layer, compare_rows, device_factor_r, gpu_layer, oracle_factor,
+                         rows_of, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,37 +55,6 @@ def test_layer_parity_opt13b_attn_full():
     w, x = w.cpu(), x.cpu()
     gpu = gpu_layer(w, x, cfg.bits, cfg.group, cfg.grid, cfg.damp, chunk_tokens=CHUNK)
     assert_gates(compare_layer(w, x, cfg.bits, cfg.group, cfg.grid, gpu, cfg.damp, cfg.name))
-
-
-N_SAMPLE_ROWS = 256
-
-
-def _sample_rows(m, seed):
-    """256 distinct random rows plus the first and the last, sorted."""
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([rng.choice(m, N_SAMPLE_ROWS, replace=False), [0, m - 1]]))
-
-
-def _device_factor(cfg, x):
-    """H over all tokens in one call (fp64), then R = U^-1 (fp64, the Cholesky factor
-    of H_d), as the benchmark runs them."""
-    d = cfg.d
-    H = torch.empty(d, d, dtype=torch.float64, device=DEV)
-    G.accumulate_hessian(H, x, accumulate=False)
-    R, info, lam = G.prepare_hchol(H, cfg.damp, r_dtype=torch.float64)
-    torch.cuda.synchronize()
-    assert int(info.item()) == 0
-    return H, R, float(lam.item())
-
-
-def _rows_of(res, rows, bits, d):
-    rt = torch.as_tensor(rows, device=DEV)
-    q = res["qcodes"][rt].cpu().numpy().view(np.uint32)
-    return {"codes": O.unpack_codes(q, bits, d), "qcodes": q,
-            "scales": res["scales"][rt].cpu().numpy(),
-            "zeros": res["zeros"][rt].cpu().numpy().astype(np.int64),
-            "w_hat": res["w_hat"][rt].cpu().numpy(),
-            "err_sq": res["err_sq"][rt].cpu().numpy()}
 
 
 _CODE_PARITY = [("opt175b-q", ["opt175b-q"]), ("opt175b-fc1", ["opt175b-fc1"]),
@@ -105,13 +75,13 @@ def test_code_parity_full_size_sampled_rows(label, names):
     t0 = time.time()
     w = S.make_weights(c0, DEV)
     x = S.make_activations(c0, DEV)
-    H, U, lam = _device_factor(c0, x)
-    rows = _sample_rows(c0.m, 21)
+    H, U, lam = device_factor_r(c0.d, x, c0.damp)
+    rows = sample_rows(c0.m, 21)
     gpu_rows = []
     for c in cfgs:
         res = G.quantize_layer(w, U, c.bits, c.group, c.grid, factor="R")
         torch.cuda.synchronize()
-        gpu_rows.append(_rows_of(res, rows, c.bits, c.d))
+        gpu_rows.append(rows_of(res, rows, c.bits, c.d))
         del res
     factor = {"H": H.cpu().numpy(), "U": U.cpu().double().numpy(), "lam": lam, "u_eps": 2.0 ** -53, "factor": "R"}
     wn = w[torch.as_tensor(rows, device=DEV)].double().cpu().numpy()
@@ -206,8 +176,8 @@ def test_layer_properties_full_size(name):
 
     du = torch.diagonal(U)
     assert bool((du > 0).all())
-    sample_rows = torch.as_tensor(rng.choice(d, 8, replace=False), device=DEV)
-    for i in sample_rows.tolist():
+    some_rows = torch.as_tensor(rng.choice(d, 8, replace=False), device=DEV)
+    for i in some_rows.tolist():
         assert bool((U[i, :i] == 0).all())
     worst = 0.0
     for j in rng.choice(d, 3, replace=False).tolist():
