@@ -53,14 +53,14 @@ CHUNK_TOKENS = 262144         # the whole calibration set (128 sequences of 2048
 # HBM traffic of one SYRK launch (syrk_kernel) at the default workload, from two
 # rocprofv3 --pmc passes over this command (FETCH_SIZE, WRITE_SIZE, KiB per
 # dispatch), each scaled by what the counter reads for a 1 GiB copy (FETCH_SIZE
-# x2.0, WRITE_SIZE x1.0); see profiles/syrk_kernel_opt2.7b-fc1_traffic.md. The
+# x2.0, WRITE_SIZE x1.0); see profiles/syrk_kernel_opt175b-fc2_traffic.md. The
 # figure is only reported while the kernel source is the one it was taken on.
 SYRK_TRAFFIC = {
-    "config": "opt2.7b-fc1",
+    "config": "opt175b-fc2",
     "chunk_tokens": 262144,
-    "source_sha256_16": "a18f5759056f6268",   # syrk.hip + common.h
-    "fetch_bytes": 3001029.0625 * 1024 * 2.0,
-    "write_bytes": 56320.0 * 1024 * 1.0,
+    "source_sha256_16": "0000000000000000",   # syrk.hip + common.h: no figure for this source yet
+    "fetch_bytes": 292314512.7 * 1024 * 2.0,
+    "write_bytes": 9487356.0 * 1024 * 1.0,
 }
 
 
@@ -108,9 +108,41 @@ def parse():
                    help="tokens per gptq_accumulate_hessian call (the whole X stays resident either way)")
     p.add_argument("--cpu-sample-rows", type=int, default=None)
     p.add_argument("--cpu-sample-tokens", type=int, default=None)
+    p.add_argument("--vendor-gemm", action="store_true",
+                   help="time hipBLASLt fp16 GEMMs at large shapes (context for the SYRK's matrix-core fraction)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only copy 1 GiB device-to-device three times (reference for the HBM byte counters)")
     return p.parse_args()
+
+
+def vendor_gemm():
+    """Context for the SYRK's fraction: hipBLASLt fp16 GEMMs (torch.matmul, fp16 in
+    and out) at large shapes, HIP events around ten products after three warm-ups."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    for m, n, k, tn in [(16384, 16384, 32768, False), (12288, 12288, 32768, True), (49152, 8192, 32768, True)]:
+        if tn:
+            a = torch.randn(k, m, generator=g, device=dev, dtype=torch.float16)
+            b = a if n == m else torch.randn(k, n, generator=g, device=dev, dtype=torch.float16)
+            f = (lambda a=a, b=b: torch.matmul(a.t(), b))
+        else:
+            a = torch.randn(m, k, generator=g, device=dev, dtype=torch.float16)
+            b = torch.randn(k, n, generator=g, device=dev, dtype=torch.float16)
+            f = (lambda a=a, b=b: torch.matmul(a, b))
+        for _ in range(3):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        tf = 2 * m * n * k / (ms * 1e-3) / 1e12
+        print(json.dumps({"vendor_gemm": f"{m}x{k} @ {k}x{n} {'TN' if tn else 'NN'} fp16", "ms": round(ms, 3),
+                          "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_FP16_TFLOPS, 4)}), flush=True)
+        del a, b
 
 
 def copy_calibration():
@@ -294,15 +326,28 @@ def gemv_bench(args):
         x = torch.randn(d, device=dev, generator=gen).half()
         y = torch.empty(m, dtype=torch.float32, device=dev)
         nbytes = m * d * bits // 8 + m * ng * 5 + d * 2 + m * 4
-        layers.append((name, q, sc, z, bits, group, x, y, nbytes))
+        perm = None
+        if args.act_order:
+            # act-order codes: a group index spreading every group over the row,
+            # the codes rewritten in group order once (outside the timed steps)
+            g_idx = torch.randperm(d, device=dev, generator=gen).to(torch.int32) // group
+            q, perm, info = G.gemv_prepare_act_order(q, g_idx.contiguous(), bits, group)
+            torch.cuda.synchronize()
+            assert int(info.item()) == 0
+            perm = (perm, torch.empty(d, dtype=torch.float16, device=dev))
+            nbytes += d * 4 + d * 2 * 2     # col_perm, and x gathered into x_perm and read back
+        layers.append((name, q, sc, z, bits, group, x, y, nbytes, perm))
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers]
 
     def step(timed):
-        for i, (name, q, sc, z, bits, group, x, y, nb) in enumerate(layers):
+        for i, (name, q, sc, z, bits, group, x, y, nb, perm) in enumerate(layers):
             if timed:
                 ev[i][0].record()
-            G.dequant_gemv(q, sc, z, bits, group, x, y)
+            if perm is None:
+                G.dequant_gemv(q, sc, z, bits, group, x, y)
+            else:
+                G.dequant_gemv_perm(q, sc, z, bits, group, perm[0], x, perm[1], y)
             if timed:
                 ev[i][1].record()
 
@@ -331,7 +376,9 @@ def gemv_bench(args):
         "dtype": "u3 codes -> f32 (fp16 x)",
         "data": "synthetic packed codes, scales and zero points of the block's shapes",
         "config": {"workload": "OPT-175B block q, k, v, out (12288x12288), fc1 (49152x12288), fc2 (12288x49152); "
-                               "3-bit g128 packed weights, one token", "block_bytes": total_bytes},
+                               "3-bit g128 packed weights, one token"
+                               + ("; act-order codes (group index, columns sorted by group, x gathered)"
+                                  if args.act_order else ""), "block_bytes": total_bytes},
         "layer_ms": {k: round(v, 5) for k, v in per.items()},
         "block_gbs": round(total_bytes / (sum(per.values()) * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": f"dq_gemv_kernel<3> ({big[0]})", "achieved": round(big_gbs, 1),
@@ -512,12 +559,14 @@ def gemv_cpu_baseline(layers, rows=32):
 
 def main():
     args = parse()
+    if args.vendor_gemm:
+        vendor_gemm()
+        return
     if args.copy_calibration:
         copy_calibration()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path (see the sharding notes in the design "
-              "document); run it with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.static_groups and not args.act_order:
         print("--static-groups needs --act-order", file=sys.stderr)

@@ -112,8 +112,12 @@ class TraceScope {
 
 // Entry points of the individual kernel families (implemented in the .hip files).
 gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const half_t* X, int64_t n,
-                           int64_t ldx, int accumulate, void* ws, size_t ws_bytes, hipStream_t st);
+                           int64_t ldx, int accumulate, void* ws, size_t ws_bytes, hipStream_t st,
+                           bool allow_xt = true);
 size_t syrk_workspace_bytes(int64_t d, int64_t n);
+// The split-K partial tiles alone (what the token-major form needs; the
+// feature-major copy of X is the rest of syrk_workspace_bytes).
+size_t syrk_partials_workspace_bytes(int64_t d, int64_t n);
 
 // Size of the SYRK's static scratch array (gptq_accumulate_hessian_noalloc):
 // 768 fp64 partial tiles of 256 x 128 (192 MiB): the most a launch's split-K

@@ -121,13 +121,14 @@ gptq_status_t gptq_accumulate_hessian_noalloc(void* H, int32_t h_dtype, int64_t 
   if (!H || d <= 0 || d % 32 || ldh < d || n < 0) return GPTQ_ERR_INVALID_ARG;
   if (h_dtype != GPTQ_F32 && h_dtype != GPTQ_F64) return GPTQ_ERR_INVALID_ARG;
   if (n > 0 && (!X || ldx < d || ldx % 8 || !aligned(X, 16))) return GPTQ_ERR_INVALID_ARG;
-  if (syrk_workspace_bytes(d, n) > kStaticScratchBytes) return GPTQ_ERR_WORKSPACE;
+  if (syrk_partials_workspace_bytes(d, n) > kStaticScratchBytes) return GPTQ_ERR_WORKSPACE;
   GPTQ_CHECK_DEVICE();
   void* ws = nullptr;
   if (const gptq_status_t s = static_scratch(&ws)) return s;
   TracePause no_trace_events;  // event creation is an allocation
+  // the token-major form: the array holds the split-K partials only
   return syrk_enqueue(H, h_dtype == GPTQ_F64, d, ldh, (const half_t*)X, n, ldx, accumulate != 0, ws,
-                      kStaticScratchBytes, (hipStream_t)stream);
+                      kStaticScratchBytes, (hipStream_t)stream, /*allow_xt=*/false);
 }
 
 gptq_status_t gptq_prepare_hinv(const void* H, int32_t h_dtype, int64_t d, int64_t ldh, double damp, void* U,

@@ -284,38 +284,47 @@ __global__ void fill_zero_kernel(float* x, int64_t n) {
 
 // R form: Ubb[b] = (R[b0:b1, b0:b1])^-1 for every 128-column block b (upper
 // triangular; fp64 arithmetic from R as given, fp32 result, rows and columns
-// past the block's width zero). One workgroup per block; the inverse X is
-// built row by row from the bottom: X_ii = 1 / R_ii and, for c > i,
-// X_ic = -(sum_{i < k <= c} R_ik X_kc) / R_ii, thread c owning column c.
-__global__ __launch_bounds__(BLK) void rblock_inverse_kernel(const void* R, int r_f64, int64_t d, int64_t ldr,
-                                                             float* Ubb) {
-  __shared__ double X[BLK][BLK];
-  __shared__ double Ti[BLK];
+// past the block's width zero). One workgroup of 1024 threads per block; the
+// inverse X is built row by row from the bottom, right-looking: once row k of
+// X is final, every row i < k adds R_ik X_kc to its running sum S_ic, and row
+// i is final as X_ic = (delta_ic - S_ic) / R_ii. Thread (g, c) keeps column c of
+// rows 16 g .. 16 g + 15, so a step costs 16 independent FMAs per thread and
+// three barriers (the sums S live in A until their row is final).
+constexpr int RBI_THREADS = 1024;
+__global__ __launch_bounds__(RBI_THREADS) void rblock_inverse_kernel(const void* R, int r_f64, int64_t d,
+                                                                     int64_t ldr, float* Ubb) {
+  __shared__ double A[BLK][BLK + 1];
+  __shared__ double col[BLK];
   const int64_t b0 = (int64_t)blockIdx.x * BLK;
   const int bw = (int)((d - b0) < BLK ? (d - b0) : BLK);
-  const int c = threadIdx.x;
+  const int c = threadIdx.x & (BLK - 1), g = threadIdx.x / BLK;  // g = 0 .. 7
+  constexpr int RPT = BLK / (RBI_THREADS / BLK);                  // rows per thread (16)
   auto rv = [&](int i, int k) -> double {
     const int64_t o = (b0 + i) * ldr + b0 + k;
     return r_f64 ? ((const double*)R)[o] : (double)((const float*)R)[o];
   };
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) A[g * RPT + rr][c] = 0.0;
   for (int i = bw - 1; i >= 0; --i) {
-    Ti[c] = (c >= i && c < bw) ? rv(i, c) : 0.0;
+    // column i of R's block, rows 0 .. i
+    if (threadIdx.x < BLK) col[threadIdx.x] = threadIdx.x <= i ? rv(threadIdx.x, i) : 0.0;
     __syncthreads();
-    if (c < bw) {
-      double v = 0.0;
-      if (c == i) {
-        v = 1.0 / Ti[i];
-      } else if (c > i) {
-        double sacc = 0.0;
-        for (int k = i + 1; k <= c; ++k) sacc = fma(Ti[k], X[k][c], sacc);
-        v = -sacc / Ti[i];
-      }
-      X[i][c] = v;
+    if (g == i / RPT && c < bw) A[i][c] = c == i ? 1.0 / col[i] : c > i ? -A[i][c] / col[i] : 0.0;
+    __syncthreads();
+    const double xi = A[i][c];
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) {
+      const int r = g * RPT + rr;
+      if (r < i) A[r][c] = fma(col[r], xi, A[r][c]);
     }
     __syncthreads();
   }
   float* out = Ubb + (int64_t)blockIdx.x * BLK * BLK;
-  for (int i = 0; i < BLK; ++i) out[i * BLK + c] = (i < bw && c < bw && c >= i) ? (float)X[i][c] : 0.0f;
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) {
+    const int r = g * RPT + rr;
+    out[r * BLK + c] = (r < bw && c < bw && c >= r) ? (float)A[r][c] : 0.0f;
+  }
 }
 
 
@@ -538,7 +547,8 @@ gptq_status_t quant_enqueue(const void* W, int w_f32, int64_t m, int64_t d, int6
   if (rform) {
     // the inverses of R's diagonal blocks (from the factor as given, in fp64)
     // and a zero accumulator
-    hipLaunchKernelGGL(rblock_inverse_kernel, dim3((unsigned)nblk), dim3(BLK), 0, st, U, u_f64, d, ldu, w.Ubb);
+    hipLaunchKernelGGL(rblock_inverse_kernel, dim3((unsigned)nblk), dim3(RBI_THREADS), 0, st, U, u_f64, d, ldu,
+                       w.Ubb);
     GPTQ_CHECK_LAUNCH();
     const int64_t n = m * d;
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)(ceil_div(n / 4 + 1, 256) < 8192 ? ceil_div(n / 4 + 1, 256) : 8192)),

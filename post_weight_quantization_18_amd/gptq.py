@@ -170,8 +170,11 @@ def accumulate_hessian(H: torch.Tensor, X: torch.Tensor, accumulate: bool = True
     ldh = _rowmajor_ld(H, "H")
     ldx = _rowmajor_ld(X, "X") if X.shape[0] > 0 else d
     n = X.shape[0]
-    ws = _workspace(workspace_bytes(WS_ACCUMULATE_HESSIAN, 0, d, n), H.device, workspace)
-    nbytes = 0 if ws is None else ws.numel()
+    # a caller's workspace is passed as it is: the call accepts any size (a
+    # smaller one selects the token-major form, then fewer split partials)
+    ws = workspace if workspace is not None else _workspace(workspace_bytes(WS_ACCUMULATE_HESSIAN, 0, d, n),
+                                                           H.device, None)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.gptq_accumulate_hessian(_ptr(H), _DT[H.dtype], d, ldh, _ptr(X) if n else ctypes.c_void_p(0), n, ldx,
                                        int(bool(accumulate)), _ptr(ws), nbytes, _stream(H.device)),
            "gptq_accumulate_hessian")

@@ -68,10 +68,12 @@ def test_hessian_parity_toy(h_dtype, chunk):
     assert np.all(hg[np.triu_indices(d, 1)] == 7.0)   # strictly upper triangle untouched
 
 
-# d = 2336 and 4192: several bands of 4 I-blocks and chunks of 8 J-blocks in the
-# tile order, a last band of 2 and of 1 I-blocks, an empty tile past d; 4192
-# has 306 tiles, so 50 go to the stream-K ranges
-@pytest.mark.parametrize("n,d", [(3000, 96), (64, 320), (1, 32), (70000, 512), (5000, 2336), (1100, 4192)])
+# d = 2336 and 4192: a last I-block of 32 and of 96 features, an empty tile past
+# d; 4192 has 306 tiles, so 50 go to the stream-K ranges. d = 16416 takes the
+# feature-major form (X^T in the workspace): a last I-block of 32 features,
+# 4290 tiles (16 whole rounds, 194 by stream-K), 700 tokens padded to 704.
+@pytest.mark.parametrize("n,d", [(3000, 96), (64, 320), (1, 32), (70000, 512), (5000, 2336), (1100, 4192),
+                                 (700, 16416)])
 def test_hessian_parity_ragged(n, d):
     say(f"[case] hessian ragged n={n} d={d}")
     rng = np.random.default_rng(n + d)

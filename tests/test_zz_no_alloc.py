@@ -1,7 +1,9 @@
 """gptq_accumulate_hessian_noalloc (the Hessian accumulation for callers that
-cannot allocate: split-K partials in the library's static device array)
-against gptq_accumulate_hessian with a caller workspace, through the C ABI:
-the same kernels and plan, so H must agree bit for bit. Two calls in a row,
+cannot allocate: split-K partials in the library's static device array, X
+read token-major) against gptq_accumulate_hessian with a caller workspace,
+through the C ABI. The shapes are narrower than the width where the
+workspace form switches to a feature-major copy of X (d >= 16384), so both
+run the same kernels and plan, and H must agree bit for bit. Two calls in a row,
 the second smaller (the array keeps the first call's partials), on shapes
 that use the token-split partials (d = 2560), the stream-K partials
 (d = 4352) and a small token split (d = 256, 1024 tokens); then a size beyond the
@@ -33,13 +35,15 @@ def test_noalloc_matches_workspace_entry_point(d, n):
     x = S.make_activations(cfg, DEV)
     for (dd, nn) in ((d, n), (d // 2, n // 2)):
         xs = x[:nn, :dd].contiguous()
+        ws = torch.empty(max(1, G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, dd, nn)), dtype=torch.uint8,
+                         device=DEV)
         for h_dtype in (torch.float64, torch.float32):
             ref = torch.empty(dd, dd, dtype=h_dtype, device=DEV)
-            G.accumulate_hessian(ref, xs, accumulate=False)
+            G.accumulate_hessian(ref, xs, accumulate=False, workspace=ws)
             got = torch.full((dd, dd), float("nan"), dtype=h_dtype, device=DEV)
             assert _noalloc(got, xs, False) == G.GPTQ_OK
             # then accumulate a second pass onto it, as a streaming caller would
-            G.accumulate_hessian(ref, xs, accumulate=True)
+            G.accumulate_hessian(ref, xs, accumulate=True, workspace=ws)
             assert _noalloc(got, xs, True) == G.GPTQ_OK
             torch.cuda.synchronize()
             lo = torch.tril(torch.ones(dd, dd, dtype=torch.bool, device=DEV))
