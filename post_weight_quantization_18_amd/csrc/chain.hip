@@ -239,6 +239,135 @@ __global__ __launch_bounds__(256) void update_f64_kernel(double* A, int64_t d, i
   update_tile<KT>(A, d, ka, K, c0, c1, ti, tj, As, Bs);
 }
 
+// The trailing update of an outer panel on wide tiles: A[i][j] -= sum over
+// k in [ka, ka + K) of A[i][k] A[j][k] for i, j in [c0, d), j <= i, on TR x TC
+// tiles of (TR / 32) x (TC / 32) waves of 32 x 32 (fp64 MFMA 16x16x4). K is
+// staged KT columns at a time through LDS with the next slice prefetched into
+// registers; DB = 1 keeps two LDS buffers (one barrier per slice), DB = 0 one
+// buffer (two barriers). Tile t lies in row tile ti with M (ti + 1) column
+// tiles, M = TR / TC, so the tiles before row ti number M ti (ti + 1) / 2.
+// Measured against the 64 x 64 kernel on trailing blocks of 32256 / 8192 /
+// 2048: 128 x 128 KT16 DB 70.4 / 62.7 / 34.5 % of the fp64 peak, 128 x 64 KT32
+// 68.6 / 64.2 / 31.3 %, 64 x 64 62.5 / 60.3 / 37.8 %.
+template <int TR, int TC, int KT, int DB>
+__global__ __launch_bounds__(TR * TC / 16) void update_wide_kernel(double* A, int64_t d, int64_t ka, int64_t K,
+                                                                   int64_t c0) {
+  constexpr int NTH = TR * TC / 16;
+  constexpr int NBUF = DB ? 2 : 1;
+  constexpr int M = TR / TC;
+  constexpr int WC = TC / 32;
+  constexpr int PA = TR * KT / NTH, PB = TC * KT / NTH;
+  static_assert(PA >= 1 && PB >= 1 && TR % TC == 0, "tile shape");
+  __shared__ double As[NBUF][TR][KT + 1];
+  __shared__ double Bs[NBUF][KT][TC + 1];
+  const int t = blockIdx.x;
+  int ti = (int)((sqrt(8.0 * t / M + 1.0) - 1.0) * 0.5);
+  while ((int64_t)M * (ti + 1) * (ti + 2) / 2 <= t) ++ti;
+  while ((int64_t)M * ti * (ti + 1) / 2 > t) --ti;
+  const int tj = t - M * ti * (ti + 1) / 2;
+  const int64_t i0 = c0 + (int64_t)ti * TR, j0 = c0 + (int64_t)tj * TC;
+  GPTQ_DASSERT(tj < M * (ti + 1) && ka >= 0 && ka + K <= c0);
+  if (i0 >= d) return;  // uniform
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wr = (w / WC) * 32, wc = (w % WC) * 32;
+  double4v acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = (double4v){0.0, 0.0, 0.0, 0.0};
+  const int64_t ke = ka + K;
+  double pa[PA], pb[PB];
+  auto fetch = [&](int64_t k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < PA; ++e) {
+      const int idx = tid + NTH * e, r = idx / KT, c = idx % KT;
+      const int64_t gk = k + c;
+      pa[e] = (i0 + r < d && gk < ke) ? A[(i0 + r) * d + gk] : 0.0;
+    }
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int idx = tid + NTH * e, r = idx / KT, c = idx % KT;
+      const int64_t gk = k + c;
+      pb[e] = (j0 + r < d && gk < ke) ? A[(j0 + r) * d + gk] : 0.0;
+    }
+  };
+  auto store = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < PA; ++e) {
+      const int idx = tid + NTH * e;
+      As[b][idx / KT][idx % KT] = pa[e];
+    }
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int idx = tid + NTH * e;
+      Bs[b][idx % KT][idx / KT] = pb[e];
+    }
+  };
+  // v_mfma_f64_16x16x4: A lane l holds A[l%16][l/16], B lane l holds B[l/16][l%16]
+  const int li = lane & 15, lk = lane >> 4;
+  auto compute = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < KT; k += 4) {
+      double av[2], bv[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) av[x] = As[b][wr + x * 16 + li][k + lk];
+#pragma unroll
+      for (int y = 0; y < 2; ++y) bv[y] = Bs[b][k + lk][wc + y * 16 + li];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[x], bv[y], acc[x][y], 0, 0, 0);
+    }
+  };
+  if constexpr (DB == 0) {
+    fetch(ka);
+    for (int64_t k = ka; k < ke; k += KT) {
+      __syncthreads();
+      store(0);
+      __syncthreads();
+      if (k + KT < ke) fetch(k + KT);
+      compute(0);
+    }
+  } else {
+    // slice k computes from buffer b while slice k + KT (already in registers)
+    // goes into the other buffer, which every wave left at the last barrier
+    fetch(ka);
+    store(0);
+    __syncthreads();
+    if (ka + KT < ke) fetch(ka + KT);
+    int b = 0;
+    for (int64_t k = ka; k < ke; k += KT) {
+      compute(b);
+      if (k + KT < ke) {
+        store(b ^ 1);
+        if (k + 2 * KT < ke) fetch(k + 2 * KT);
+      }
+      __syncthreads();
+      b ^= 1;
+    }
+  }
+  // all 16 old values are read before any is written (one memory round trip)
+  double old[2][2][4];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t i = i0 + wr + x * 16 + lk + 4 * r, j = j0 + wc + y * 16 + li;
+        old[x][y][r] = (i < d && j <= i) ? A[i * d + j] : 0.0;
+      }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t i = i0 + wr + x * 16 + lk + 4 * r, j = j0 + wc + y * 16 + li;
+        if (i < d && j <= i) A[i * d + j] = old[x][y][r] - acc[x][y][r];
+      }
+}
+
 // Factor the 64 x 64 diagonal block at k0 (lower Cholesky) and invert the
 // factor, in one workgroup of 4 waves, blocked by 16 columns so that only the
 // 16-column leaves are serial. For each 16-block:
@@ -767,10 +896,22 @@ gptq_status_t chain_enqueue(const void* H, int h_f64, int64_t d, int64_t ldh, do
       if (rest <= 0) break;
     }
     if (pe < d) {
-      const int64_t rb = ceil_div(d - pe, 64);
+      // the tile shape by the trailing block's size (measured on 32256 / 8192 / 2048)
+      const int64_t nrest = d - pe;
       TraceScope tr(st, GPTQ_TRACE_CHAIN_UPDATE);
-      hipLaunchKernelGGL(update_f64_kernel, dim3((unsigned)(rb * (rb + 1) / 2)), dim3(256), 0, st, w.A, d, p0,
-                         pe - p0, pe, d, 1);
+      if (nrest >= 16384) {
+        const int64_t nr = ceil_div(nrest, 128);
+        hipLaunchKernelGGL((update_wide_kernel<128, 128, 16, 1>), dim3((unsigned)(nr * (nr + 1) / 2)), dim3(1024), 0,
+                           st, w.A, d, p0, pe - p0, pe);
+      } else if (nrest >= 4096) {
+        const int64_t nr = ceil_div(nrest, 128);
+        hipLaunchKernelGGL((update_wide_kernel<128, 64, 32, 0>), dim3((unsigned)(nr * (nr + 1))), dim3(512), 0, st,
+                           w.A, d, p0, pe - p0, pe);
+      } else {
+        const int64_t rb = ceil_div(nrest, 64);
+        hipLaunchKernelGGL(update_f64_kernel, dim3((unsigned)(rb * (rb + 1) / 2)), dim3(256), 0, st, w.A, d, p0,
+                           pe - p0, pe, d, 1);
+      }
       GPTQ_CHECK_LAUNCH();
     }
   }

@@ -179,14 +179,17 @@ def _row_stats(stats, wn, gpu, follow, free, h, bits, grid, group, g_idx=None, s
     stats["obs_rel"] = float(np.max(np.abs(gpu["err_sq"] - obs) / np.maximum(obs, ofloor)))
 
 
-def _factor_stats(stats, gpu, h, lam, u, hd):
+def _factor_stats(stats, gpu, h, lam, u, hd, r_oracle=None):
     """H, lambda and the factor the GPU path used (U, or R = U^-1 with factor "R")
-    against the oracle's."""
+    against the oracle's (r_oracle: the oracle's R when already computed)."""
     d = h.shape[0]
     stats["h_rel"] = lower_rel_fro(gpu["H"], h)
     stats["lam_rel"] = abs(gpu["lam"] - lam) / lam
     stats["factor"] = gpu.get("factor", "U")
-    uu = np.triu(O.hessian_factor(hd) if stats["factor"] == "R" else u)
+    if stats["factor"] == "R":
+        uu = np.triu(r_oracle if r_oracle is not None else O.hessian_factor(hd))
+    else:
+        uu = np.triu(u)
     stats["u_rel"] = float(np.linalg.norm(np.triu(gpu["U"]) - uu) / np.linalg.norm(uu))
     stats["kappa_bound"] = kappa_bound(hd, lam)
     # plus the rounding of U to its output precision (fp32 or fp64)

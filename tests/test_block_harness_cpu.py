@@ -42,3 +42,19 @@ def test_layer_work_counts():
     m, d, n = 12288, 49152, 262144
     assert flops["syrk"] == n * d * (d + 1) and flops["chain"] == d ** 3 / 3
     assert nbytes["x"] == 2 * n * d and nbytes["outputs"] == m * d * 3 // 8 + m * (d // 128) * 5 + 4 * m
+
+
+def test_stepwise_oracle_factor_matches_the_oracle():
+    """The harness's stepwise oracle factor (H chunk by chunk, U = R^-1 by column
+    blocks) gives the oracle's H bit for bit and its U to fp64 rounding."""
+    import numpy as np
+
+    from parity_util import oracle_factor
+
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((300, 96)) * np.linspace(0.3, 2.0, 96)).astype(np.float16)
+    h1, lam1, u1, hd1 = oracle_factor(x, 0.01, chunk=128)
+    h2, lam2, u2, hd2, r2 = BH.oracle_factor_in_steps(x, 0.01, chunk=128)
+    assert np.array_equal(h1, h2) and lam1 == lam2 and np.array_equal(hd1, hd2)
+    assert np.linalg.norm(u2 - u1) <= 1e-12 * np.linalg.norm(u1)
+    assert np.allclose(r2 @ r2.T, hd2, rtol=1e-12, atol=1e-12 * np.abs(hd2).max())
