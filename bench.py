@@ -1,15 +1,18 @@
 """Benchmark of the GPTQ layer-quantization hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config opt175b-fc2]
-                    [--act-order [--static-groups]]
-    python bench.py --gemv [--steps K] [--warmup W]
-    python bench.py --block [--steps K] [--warmup W]
+                    [--factor auto|R|U] [--act-order [--static-groups]]
+    python bench.py --gemv [--act-order] [--steps K] [--warmup W]
+    python bench.py --block [--sequential] [--steps K] [--warmup W]
+    python bench.py --vendor-gemm | --copy-calibration
 
 One step = the whole hot path on one layer with W and X already resident in
 HBM: H accumulated over all of the layer's calibration tokens in one call
 (--chunk-tokens splits it into calls of that many tokens, as a caller that
-streams its calibration batches would), the fp64 inverse-Hessian factor, then
-the column loop with lazy 128-column updates, trailing GEMMs and packing.
+streams its calibration batches would), the fp64 factor (R, the Cholesky
+factor of H + lambda I, from d = 8192 on; U = chol(H_d^-1) below, or as
+--factor says), then the column loop with lazy 128-column updates, trailing
+GEMMs and packing.
 With --act-order the step also orders the columns by descending H_jj, gathers
 H into that order before the chain, and runs the column loop in that order
 (--static-groups: grids fitted on the original weights' natural groups).
@@ -87,8 +90,10 @@ def parse():
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--config", default="opt175b-fc2", choices=sorted(S.CONFIGS))
-    p.add_argument("--factor", choices=["R", "U"], default="R",
-                   help="R: the Cholesky factor of H_d (gptq_prepare_hchol, no inverse); "
+    p.add_argument("--factor", choices=["auto", "R", "U"], default="auto",
+                   help="auto: R from d = 8192 on (measured faster there: no triangular inverse), U below (the "
+                        "R form's fixed costs dominate small layers); "
+                        "R: the Cholesky factor of H_d (gptq_prepare_hchol, no inverse); "
                         "U: chol(H_d^-1) (gptq_prepare_hinv)")
     p.add_argument("--no-trace", action="store_true",
                    help="time the steps without the per-kernel trace (no per-family breakdown)")
@@ -400,19 +405,20 @@ BLOCK_GROUPS = [("attn-qkv", ["opt175b-q", "opt175b-k", "opt175b-v"]), ("attn-ou
 class BlockGroup:
     """One input X, its Hessian and factor, and the layers quantized with them."""
 
-    def __init__(self, label, names, dev):
+    def __init__(self, label, names, dev, factor="R"):
         self.label = label
+        self.factor = factor
         self.cfgs = [S.CONFIGS[n] for n in names]
         c0 = self.cfgs[0]
         d = c0.d
         self.x = S.make_activations(c0, dev)
         self.ws = [S.make_weights(c, dev) for c in self.cfgs]
         self.H = torch.empty(d, d, dtype=torch.float64, device=dev)
-        self.U = torch.empty(d, d, dtype=torch.float32, device=dev)
+        self.U = torch.empty(d, d, dtype=torch.float64 if factor == "R" else torch.float32, device=dev)
         self.ws_h = torch.empty(max(1, G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, d, c0.n_tokens)),
                                 dtype=torch.uint8, device=dev)
         self.ws_c = torch.empty(G.workspace_bytes(G.WS_PREPARE_HINV, 0, d), dtype=torch.uint8, device=dev)
-        qb = max(G.workspace_bytes(G.WS_QUANTIZE_LAYER, c.m, d, 0, G.make_qcfg(c.bits, c.group, c.grid))
+        qb = max(G.workspace_bytes(G.WS_QUANTIZE_LAYER, c.m, d, 0, G.make_qcfg(c.bits, c.group, c.grid, factor=factor))
                  for c in self.cfgs)
         self.ws_q = torch.empty(qb, dtype=torch.uint8, device=dev)
         self.outs = []
@@ -431,10 +437,13 @@ class BlockGroup:
         self.ev[0].record()
         G.accumulate_hessian(self.H, self.x, accumulate=False, workspace=self.ws_h)
         self.ev[1].record()
-        _, self.info, _ = G.prepare_hinv(self.H, c0.damp, U=self.U, workspace=self.ws_c)
+        if self.factor == "R":
+            _, self.info, _ = G.prepare_hchol(self.H, c0.damp, R=self.U, workspace=self.ws_c)
+        else:
+            _, self.info, _ = G.prepare_hinv(self.H, c0.damp, U=self.U, workspace=self.ws_c)
         self.ev[2].record()
         for i, (c, w, o) in enumerate(zip(self.cfgs, self.ws, self.outs)):
-            G.quantize_layer(w, self.U, c.bits, c.group, c.grid, workspace=self.ws_q, out=o)
+            G.quantize_layer(w, self.U, c.bits, c.group, c.grid, workspace=self.ws_q, out=o, factor=self.factor)
             self.ev[3 + i].record()
 
     def stage_ms(self):
@@ -455,7 +464,7 @@ def sequential_block_bench(args):
     shape = B.OPT175B
     _say("sequential block: drawing the block input and the six weight matrices")
     x = B.block_input(shape, dev)
-    sb = B.SequentialBlock(shape, dev, factor=args.factor)
+    sb = B.SequentialBlock(shape, dev, factor="U" if args.factor == "U" else "R")
     torch.cuda.synchronize()
     for i in range(args.warmup):
         sb.run(x)
@@ -481,7 +490,7 @@ def sequential_block_bench(args):
         "data": "synthetic block input (correlated Gaussian, 128 sequences of 2048 tokens) and synthetic weights",
         "config": {"workload": "OPT-175B decoder block: q, k, v, out 12288x12288, fc1 49152x12288, fc2 12288x49152; "
                                "3-bit asym g128; each sublayer calibrated on the forward pass through the quantized "
-                               "sublayers before it; 262144 tokens", "weights": n_weights, "factor": args.factor},
+                               "sublayers before it; 262144 tokens", "weights": n_weights, "factor": sb.factor},
         "weights_per_s": n_weights / s_block,
         "forward_ms": round(fwd / args.steps, 3),
         "quantize_ms": {k: round(v / args.steps, 3) for k, v in quant.items()},
@@ -497,7 +506,7 @@ def block_bench(args):
     groups = []
     for label, names in BLOCK_GROUPS:
         _say(f"block: drawing {label} ({', '.join(names)})")
-        groups.append(BlockGroup(label, names, dev))
+        groups.append(BlockGroup(label, names, dev, factor="U" if args.factor == "U" else "R"))
     torch.cuda.synchronize()
     for i in range(args.warmup):
         for g in groups:
@@ -588,6 +597,8 @@ def main():
     torch.cuda.synchronize()
     _say("inputs resident; allocating buffers")
     factor = args.factor
+    if factor == "auto":
+        factor = "R" if cfg.d >= 8192 else "U"
     if factor == "R" and cfg.group > 128 and not (args.act_order and args.static_groups):
         factor = "U"  # groups wider than a block are refitted in the U form only
     run = LayerRun(cfg, w, x, args.chunk_tokens, args.act_order, args.static_groups, factor)

@@ -334,7 +334,7 @@ enum {
   GPTQ_TRACE_SYRK = 0, GPTQ_TRACE_SYRK_REDUCE = 1, GPTQ_TRACE_CHAIN_LOAD = 2, GPTQ_TRACE_CHAIN_PANEL = 3,
   GPTQ_TRACE_CHAIN_UPDATE = 4, GPTQ_TRACE_CHAIN_MERGE = 5, GPTQ_TRACE_CHAIN_STORE = 6, GPTQ_TRACE_QUANT_PREP = 7,
   GPTQ_TRACE_COLLOOP = 8, GPTQ_TRACE_ESPLIT = 9, GPTQ_TRACE_TGEMM = 10, GPTQ_TRACE_PACK = 11,
-  GPTQ_TRACE_ORDER = 12, GPTQ_TRACE_GEMV = 13, GPTQ_TRACE_FAMILIES = 14
+  GPTQ_TRACE_ORDER = 12, GPTQ_TRACE_GEMV = 13, GPTQ_TRACE_SYRK_TRANSPOSE = 14, GPTQ_TRACE_FAMILIES = 15
 };
 int32_t gptq_trace_start(void);
 int32_t gptq_trace_stop(int64_t* launches, double* ms, double* work, int32_t n);

@@ -758,7 +758,7 @@ gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const hal
   const int64_t Tpad = ceil_div(n, KS) * KS;
   half_t* XT = xt ? (half_t*)((char*)ws + part_bytes) : nullptr;
   if (xt) {
-    TraceScope tr(st, GPTQ_TRACE_SYRK_REDUCE);
+    TraceScope tr(st, GPTQ_TRACE_SYRK_TRANSPOSE);
     hipLaunchKernelGGL(syrk_transpose_kernel, dim3((unsigned)(Tpad / 64), (unsigned)ceil_div(d, 64)), dim3(256), 0,
                        st, X, ldx, n, d, XT, Tpad);
     GPTQ_CHECK_LAUNCH();

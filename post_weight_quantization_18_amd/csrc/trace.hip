@@ -43,7 +43,7 @@ hipEvent_t take_event() {
 
 const char* const kFamilyNames[GPTQ_TRACE_FAMILIES] = {
     "syrk", "syrk_reduce", "chain_load", "chain_panel", "chain_update", "chain_merge", "chain_store",
-    "quant_prep", "colloop", "esplit", "tgemm", "pack", "order", "gemv"};
+    "quant_prep", "colloop", "esplit", "tgemm", "pack", "order", "gemv", "syrk_transpose"};
 
 }  // namespace
 

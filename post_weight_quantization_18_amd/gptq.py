@@ -40,7 +40,7 @@ EXPORTED = ["gptq_abi_version", "gptq_status_string", "gptq_workspace_bytes", "g
             "gptq_quantize_layer_ordered", "gptq_dequant_gemv", "gptq_pack_codes", "gptq_trace_start",
             "gptq_trace_stop", "gptq_trace_family", "gptq_accumulate_hessian_noalloc", "gptq_prepare_hchol",
             "gptq_gemv_prepare_act_order", "gptq_dequant_gemv_perm"]
-TRACE_FAMILIES = 14
+TRACE_FAMILIES = 15
 
 
 GPTQ_FACTOR_HINV_CHOL, GPTQ_FACTOR_H_CHOL = 0, 1
