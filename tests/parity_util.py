@@ -51,8 +51,15 @@ LOSS_TOL = 5e-3
 
 
 def say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
+    """A progress line: printed, and also written past pytest's capture, so that
+    a long GPU test (the full-size parity ones take minutes) shows its steps."""
+    try:
+        from conftest import progress_line
+    except ImportError:
+        progress_line = None
+    if progress_line is None or not progress_line(" ".join(str(x) for x in a)):
+        print(*a, flush=True)
+        sys.stdout.flush()
 
 
 def lower_rel_fro(h_gpu: np.ndarray, h_orc: np.ndarray) -> float:
