@@ -53,7 +53,8 @@ PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector
 CHUNK_TOKENS = 262144         # the whole calibration set (128 sequences of 2048) per accumulate call
 
-# HBM traffic of one SYRK launch (syrk_kernel) at the default workload, from two
+# HBM traffic of one SYRK launch (syrk_kernel<true>, the feature-major form) at
+# the default workload, from two
 # rocprofv3 --pmc passes over this command (FETCH_SIZE, WRITE_SIZE, KiB per
 # dispatch), each scaled by what the counter reads for a 1 GiB copy (FETCH_SIZE
 # x2.0, WRITE_SIZE x1.0); see profiles/syrk_kernel_opt175b-fc2_traffic.md. The
@@ -61,8 +62,8 @@ CHUNK_TOKENS = 262144         # the whole calibration set (128 sequences of 2048
 SYRK_TRAFFIC = {
     "config": "opt175b-fc2",
     "chunk_tokens": 262144,
-    "source_sha256_16": "0000000000000000",   # syrk.hip + common.h: no figure for this source yet
-    "fetch_bytes": 292314512.7 * 1024 * 2.0,
+    "source_sha256_16": "57c8133e96f03b31",   # syrk.hip + common.h
+    "fetch_bytes": 177793145.9 * 1024 * 2.0,
     "write_bytes": 9487356.0 * 1024 * 1.0,
 }
 
@@ -534,11 +535,11 @@ def block_bench(args):
         "unit": "s/block",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(s_block * 1e3, 3),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16 MFMA->f32/f64 (H), f64 (U), f32 (column loop, trailing GEMM)",
+        "dtype": "f16 MFMA->f32/f64 (H), f64 (R or U), f32 (column loop), split-f16 MFMA->f32 (trailing GEMM)",
         "data": "synthetic (seeded inputs and weights of the block's shapes; q, k and v share one input)",
         "config": {"workload": "OPT-175B block: q, k, v, out 12288x12288, fc1 49152x12288, fc2 12288x49152; "
-                               "3-bit asym g128; 262144 calibration tokens per input; q/k/v share one H and U",
-                   "weights": n_weights},
+                               "3-bit asym g128; 262144 calibration tokens per input; q/k/v share one H and factor",
+                   "weights": n_weights, "factor": groups[0].factor},
         "weights_per_s": n_weights / s_block,
         "stages_ms": {g.label: {k: round(v / args.steps, 3) for k, v in acc[g.label].items()} for g in groups},
         "model_projection_96_blocks_min": round(96 * s_block / 60, 2),
@@ -703,7 +704,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA->f32/f64 (H), f64 (U), f32 (column loop), split-f16 MFMA->f32 (trailing GEMM)",
+        "dtype": "f16 MFMA->f32/f64 (H), f64 (R or U), f32 (column loop), split-f16 MFMA->f32 (trailing GEMM)",
         "data": "synthetic (seeded correlated-Gaussian X with outlier channels, N(0,0.02^2) W with outlier columns)",
         "config": {"workload": f"{cfg.name}: W {m}x{d} {cfg.w_dtype}, X {n}x{d} fp16, {cfg.bits}-bit {cfg.grid} "
                                f"{'per-row' if cfg.group == 0 else 'g' + str(cfg.group)}, block 128, damp {cfg.damp}"

@@ -53,8 +53,9 @@ def _run(c, s, z, x, bits, group):
     return words, y.cpu().numpy().astype(np.float64)
 
 
+# m >= 32768 takes the 8-rows-per-wave form (33000: a ragged last workgroup)
 @pytest.mark.parametrize("m,d,bits,group", [(1, 32, 3, 0), (5, 96, 3, 32), (17, 256, 4, 128), (64, 256, 2, 64),
-                                            (3, 128, 8, 0), (33, 224, 3, 32)])
+                                            (3, 128, 8, 0), (33, 224, 3, 32), (33000, 64, 3, 32)])
 def test_bit_exact_on_exactly_representable_inputs(m, d, bits, group):
     say(f"[case] gemv exact m={m} d={d} bits={bits} group={group}")
     c, s, z, x = _case(m, d, bits, group, seed=m * 7 + bits, exact=True)
@@ -62,16 +63,15 @@ def test_bit_exact_on_exactly_representable_inputs(m, d, bits, group):
     np.testing.assert_array_equal(y, O.dequant_matvec(words, s, z, bits, group, x.astype(np.float64)))
 
 
-# Streaming form (d * bits % 128 == 0, groups dividing or multiples of 2048):
-# 4096/3/128, 2560/4/0, 12288/3/128, 1024/2/32, 49152/3/128, 640/8/64,
-# 1024/3/1024, 8192/2/4096, 6144/3/32 (a ragged last slab: 6144 = 3 slabs;
-# 2560 = 1.25 slabs) and m not a multiple of the 4 rows of a wave; the
-# chunked form: 3072/3/96 and 12288/4/3072 (groups that do not tile the slab),
-# 2080/3/32 (d * bits % 128 != 0)
+# Chunk counts per row that are not multiples of the wave's 64 lanes (2560,
+# 640, 2080 columns), groups of 96, 1024, 3072 and 4096 columns, row counts
+# that are not multiples of a wave's rows, and tall layers (32790 and 40000
+# rows: 8 rows per wave)
 @pytest.mark.parametrize("m,d,bits,group", [(1000, 4096, 3, 128), (777, 2560, 4, 0), (129, 12288, 3, 128),
                                             (256, 1024, 2, 32), (64, 49152, 3, 128), (100, 640, 8, 64),
                                             (4096, 1024, 3, 1024), (33, 8192, 2, 4096), (70, 6144, 3, 32),
-                                            (41, 3072, 3, 96), (9, 12288, 4, 3072), (50, 2080, 3, 32)])
+                                            (41, 3072, 3, 96), (9, 12288, 4, 3072), (50, 2080, 3, 32),
+                                            (32790, 512, 3, 128), (40000, 256, 8, 64)])
 def test_against_the_oracle(m, d, bits, group):
     say(f"[case] gemv m={m} d={d} bits={bits} group={group}")
     c, s, z, x = _case(m, d, bits, group, seed=m + d + bits)

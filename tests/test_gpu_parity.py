@@ -142,6 +142,28 @@ def test_chain_parity(d, u_dtype):
     assert abs(float(lam.item()) - lam_o) <= 1e-12 * lam_o
 
 
+def test_hchol_parity_wide_tiles():
+    """At d = 16960 the first trailing update (16448 wide) runs on 128 x 128
+    tiles, the next ones on 128 x 64 down to 4096, then 64 x 64; ragged at 128.
+    H = 2 A^T A + diag(c) from a 1024-token A keeps the host's oracle cheap."""
+    d = 16960
+    say(f"[case] hchol wide tiles d={d}")
+    rng = np.random.default_rng(d)
+    a = rng.standard_normal((1024, d)) * np.linspace(0.2, 3.0, d)
+    h = 2 * a.T @ a + np.diag(rng.uniform(0.5, 2.0, d))
+    R, info, lam = G.prepare_hchol(torch.from_numpy(h).to(DEV), 0.01, r_dtype=torch.float64)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    hd_o, lam_o = O.damp(h, 0.01)
+    ro = O.hessian_factor(hd_o)
+    rg = R.cpu().numpy()
+    rel = np.linalg.norm(rg - ro) / np.linalg.norm(ro)
+    say(f"  R rel={rel:.3e}")
+    assert np.all(np.tril(rg, -1) == 0)
+    assert rel <= 1e-12
+    assert abs(float(lam.item()) - lam_o) <= 1e-12 * lam_o
+
+
 @pytest.mark.parametrize("d,r_dtype", [(768, torch.float64), (768, torch.float32), (40, torch.float64),
                                        (1000, torch.float64), (8256, torch.float64), (1537, torch.float64)])
 def test_hchol_parity(d, r_dtype):
