@@ -106,15 +106,39 @@ struct SyrkArgs {
   int h_f64, accumulate;
 };
 
-// Tile t -> (bi, bj): the tiles of I-block bi are bj = 0 .. 2 bi + 1, so t lies
-// in [bi (bi + 1), (bi + 1)(bi + 2)). Consecutive tiles (which one XCD runs
-// together) share their I columns. Tiles past d are empty.
+// Tile slot t -> (bi, bj), the same order in the SYRK and in the reductions.
+// The tiles of I-block bi are bj = 0 .. 2 bi + 1. Slots run over bands of
+// kBand I-blocks (band q: I-blocks r0 = q kBand .. r0 + n - 1, n = kBand but
+// for the last band), the tiles before band q numbering r0 (r0 + 1). Inside a
+// band the tiles go column by column: columns 0 .. 2 r0 + 1 hold all n rows,
+// then come pairs of columns with n - 1, n - 2, .., 1 rows (row bi ends at
+// column 2 bi + 1). The 32 workgroups that one XCD runs together (consecutive
+// slots) then cover 4 I-blocks x 8 J-blocks, 2048 features of X per stage,
+// instead of 1 x 32 (4352 features) in row order, so more of their DMA hits
+// that XCD's L2. Tiles past d are empty.
+constexpr int kBand = 4;
 __device__ inline bool tile_coords(int t, int64_t d, int& bi, int& bj) {
-  int b = (int)((sqrtf(4.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-  while ((b + 1) * (b + 2) <= t) ++b;
-  while (b * (b + 1) > t) --b;
-  bi = b;
-  bj = t - b * (b + 1);
+  const int nb = (int)((d + TI - 1) / TI);
+  int q = (int)(sqrtf((float)t) / kBand);
+  while (q > 0 && (q * kBand) * (q * kBand + 1) > t) --q;
+  while (((q + 1) * kBand) * ((q + 1) * kBand + 1) <= t && (q + 1) * kBand < nb) ++q;
+  const int r0 = q * kBand, n = nb - r0 < kBand ? nb - r0 : kBand;
+  int u = t - r0 * (r0 + 1);
+  const int full = (2 * r0 + 2) * n;
+  if (u < full) {
+    bj = u / n;
+    bi = r0 + u % n;
+  } else {
+    u -= full;
+    int p = 0;
+    while (u >= 2 * (n - 1 - p)) {
+      u -= 2 * (n - 1 - p);
+      ++p;
+    }
+    const int cnt = n - 1 - p;
+    bj = 2 * r0 + 2 + 2 * p + u / cnt;
+    bi = r0 + 1 + p + u % cnt;
+  }
   return (int64_t)bj * TJ < d;
 }
 
@@ -588,7 +612,7 @@ int syrk_ntiles(int64_t d) {
 }
 
 constexpr int64_t kLaunchTokens = 32768;
-constexpr int64_t kXtMinD = 16384;     // the feature-major form from this width on
+constexpr int64_t kXtMinD = 12288;     // the feature-major form from this width on
 constexpr int kSkMax = 256;            // stream-K workgroups: one round
 constexpr int64_t kSkMinStages = 16;   // at least 1024 tokens per stream-K range
 

@@ -48,7 +48,7 @@ def test_status_strings_and_version(lib):
 def test_workspace_sizes(lib):
     d, n = 2560, 262144
     tile = 256 * 128 * 8                        # one fp64 partial tile
-    # partials, then (d >= 16384) the feature-major copy of one launch's tokens (fp16)
+    # partials, then (d >= 12288) the feature-major copy of one launch's tokens (fp16)
     # 110 tiles < 256: one launch of all tokens, split in two, one partial tile per tile and split
     assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, d, n) == 2 * 110 * tile
     assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 768, 4096) == 3 * 12 * tile
@@ -57,10 +57,10 @@ def test_workspace_sizes(lib):
     assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 49152, n) == 256 * 2 * tile + 49152 * 32768 * 2
     # 256 x 257 tiles: whole rounds only, no partials
     assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 65536, n) == 65536 * 32768 * 2
-    # the copy starts at d = 16384 (20000 tokens round up to 20032 there); below,
+    # the copy starts at d = 12288 (20000 tokens round up to 20032 there); below,
     # the partials alone (at most 512 tiles of the stream-K round)
-    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 16384, 20000) >= 16384 * 20032 * 2
-    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 16352, 20000) <= 512 * tile
+    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 12288, 20000) >= 12288 * 20032 * 2
+    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 12256, 20000) <= 512 * tile
     chain = G.workspace_bytes(G.WS_PREPARE_HINV, 0, d)
     assert chain >= d * d * 8
     cfg = G.make_qcfg(4)

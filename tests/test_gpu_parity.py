@@ -69,11 +69,13 @@ def test_hessian_parity_toy(h_dtype, chunk):
 
 
 # d = 2336 and 4192: a last I-block of 32 and of 96 features, an empty tile past
-# d; 4192 has 306 tiles, so 50 go to the stream-K ranges. d = 16416 takes the
-# feature-major form (X^T in the workspace): a last I-block of 32 features,
-# 4290 tiles (16 whole rounds, 194 by stream-K), 700 tokens padded to 704.
+# d; 4192 has 306 tiles, so 50 go to the stream-K ranges. From d = 12288 the
+# feature-major form (X^T in the workspace): d = 13024 has 51 I-blocks (the
+# last band of the tile order holds 3, the last I-block 224 features; 2652
+# tiles, 92 by stream-K), d = 16416 a last I-block of 32 features (4290 tiles,
+# 194 by stream-K), 700 tokens padded to 704.
 @pytest.mark.parametrize("n,d", [(3000, 96), (64, 320), (1, 32), (70000, 512), (5000, 2336), (1100, 4192),
-                                 (700, 16416)])
+                                 (900, 13024), (700, 16416)])
 def test_hessian_parity_ragged(n, d):
     say(f"[case] hessian ragged n={n} d={d}")
     rng = np.random.default_rng(n + d)

@@ -2,7 +2,7 @@
 cannot allocate: split-K partials in the library's static device array, X
 read token-major) against gptq_accumulate_hessian with a caller workspace,
 through the C ABI. The shapes are narrower than the width where the
-workspace form switches to a feature-major copy of X (d >= 16384), so both
+workspace form switches to a feature-major copy of X (d >= 12288), so both
 run the same kernels and plan, and H must agree bit for bit. Two calls in a row,
 the second smaller (the array keeps the first call's partials), on shapes
 that use the token-split partials (d = 2560), the stream-K partials
