@@ -552,10 +552,12 @@ def gemv_cpu_baseline(layers, rows=32):
     packed codes), scaled by m / rows per layer."""
     import oracle as O
     total, measured = 0.0, 0.0
-    for name, q, sc, z, bits, group, x, y, nb in layers:
+    for name, q, sc, z, bits, group, x, y, nb, perm in layers:
         m = q.shape[0]
         qs = q[:rows].cpu().numpy().view(np.uint32)
         ss, zs, xs = sc[:rows].cpu().numpy(), z[:rows].cpu().numpy(), x.cpu().numpy()
+        if perm is not None:
+            xs = xs[perm[0].cpu().numpy()]  # act-order: the codes are in group order, x gathered to match
         t0 = time.perf_counter()
         O.dequant_matvec(qs, ss, zs, bits, group, xs)
         dt = time.perf_counter() - t0

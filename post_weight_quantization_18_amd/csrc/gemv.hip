@@ -5,8 +5,6 @@
 // findings": 3-bit OPT-175B generation kernels run about 3.25x (A100) and 4.5x
 // (A6000) faster than fp16. At batch 1 the product reads every weight once
 // and does two flops with it: it is bound by HBM bandwidth.
-#include <type_traits>
-
 #include "common.h"
 
 namespace gptq {
@@ -14,20 +12,24 @@ namespace {
 
 // Rows per wave, sharing each chunk of x: 8 for tall layers (more code bytes
 // per x chunk and per look-ahead), 4 otherwise (a 12288-row layer would fill
-// only 384 workgroups with 8). Measured on the OPT-175B block: fc1 (49152 rows)
-// 70.8 us with 8 against 74.9 us with 4; fc2 (12288 rows) 88.5 against 79.8 us.
+// only 384 workgroups with 8). Measured on the OPT-175B block (HIP events per
+// call): fc1 (49152 rows) 58.4 us with 8 rows per wave, 58.5 / 59.3 / 61.1 /
+// 63.3 us with 7 / 6 / 5 / 4; the 12288-row layers within 3 % of each other
+// for 4 to 6 rows, slower with 2 or 3.
 constexpr int kTallRows = 32768;
 
 typedef half_t half2v __attribute__((ext_vector_type(2)));
 
 // The 32 codes of a chunk are consumed in pairs (a, b) whose fields lie 16 bits
-// apart in one 32-bit word: masking such a word keeps both codes, OR-ing in
-// 0x6400 per half makes each the fp16 number 1024 + code (the code sits in the
-// low mantissa bits under the exponent of 2^10), and subtracting 1024 in both
-// halves leaves the two codes exactly. One dot2 instruction then adds a x_a +
-// b x_b to an fp32 sum (the fp16 x fp16 products are exact in fp32). Per pair
-// that is a shift, an and-or, a packed subtract and the dot product: two
-// vector instructions per code.
+// apart in one 32-bit word, at the same bit p of the two halves. For p + BITS
+// <= 10 the field sits inside an fp16 mantissa: masking the word to the two
+// fields and OR-ing in the fp16 exponent of 2^(10 - p) in both halves makes
+// each half the number 2^(10 - p) + code exactly (mantissa bit p weighs
+// 2^(10 - p - 10 + p) = 1), and subtracting 2^(10 - p) in both halves leaves
+// the two codes. Fields at p > 10 - BITS or p >= 8 are first brought down by
+// 8 bits (one shift per word serves all of them). One dot2 instruction then adds
+// a x_a + b x_b to an fp32 sum (the products are exact in fp32). Per pair that
+// is an and-or, a packed subtract and the dot product.
 //
 // Pairs of a chunk, by bit width (code index a, b):
 //  2 bits: word k holds codes 16k .. 16k+15; pairs (16k + i, 16k + 8 + i), i < 8
@@ -38,66 +40,110 @@ typedef half_t half2v __attribute__((ext_vector_type(2)));
 //          Y = S[16,32) | S[64,80) << 16 and Z = S[32,48) | S[80,96) << 16 hold
 //          pairs (i, 16 + i) at bit 3i (i < 5), (6 + i, 22 + i) at 2 + 3i
 //          (i < 4) and (11 + i, 27 + i) at 1 + 3i (i < 5); codes 5, 10, 21 and
-//          26 straddle those halves and are taken one by one.
+//          26 straddle those halves and are paired as (5, 21) and (10, 26) in
+//          words of their own.
 template <int BITS>
 struct ChunkPairs {
   static constexpr int NP = 16;  // pairs
-  static constexpr int NS = 0;   // single codes
   static constexpr int A(int p) { return (p / (16 / BITS)) * (32 / BITS) + p % (16 / BITS); }
   static constexpr int B(int p) { return A(p) + 16 / BITS; }
-  static constexpr int S(int) { return 0; }
 };
 template <>
 struct ChunkPairs<3> {
-  static constexpr int NP = 14;
-  static constexpr int NS = 4;
-  static constexpr int A(int p) { return p < 5 ? p : p < 9 ? 6 + (p - 5) : 11 + (p - 9); }
+  static constexpr int NP = 16;  // 14 from X, Y, Z, then (5, 21) and (10, 26)
+  static constexpr int A(int p) { return p < 5 ? p : p < 9 ? 6 + (p - 5) : p < 14 ? 11 + (p - 9) : p == 14 ? 5 : 10; }
   static constexpr int B(int p) { return A(p) + 16; }
-  static constexpr int S(int q) { return q == 0 ? 5 : q == 1 ? 10 : q == 2 ? 21 : 26; }
 };
 
-// magic = 0x64006400 held in a register: with the mask in a scalar register
-// the and-or is one v_and_or_b32 (a gfx9 vector instruction reads at most one
-// scalar operand, and neither constant is an inline one).
-template <int BITS>
-__device__ __forceinline__ half2v code_pair(uint32_t t, int shift, uint32_t magic) {
-  constexpr uint32_t mask = ((1u << BITS) - 1u) * 0x00010001u;
-  const uint32_t v = ((t >> shift) & mask) | magic;
-  return __builtin_bit_cast(half2v, v) - (half2v){(half_t)1024.0f, (half_t)1024.0f};
+// The OR constants (fp16 2^(10 - p) in both halves, p = 0 .. 7), held in
+// registers: with the mask in a scalar register the and-or is one
+// v_and_or_b32 (a gfx9 vector instruction reads at most one scalar operand,
+// and neither constant is an inline one).
+struct Magics {
+  uint32_t m[8];
+  __device__ __forceinline__ Magics() {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      uint32_t v = (uint32_t)(25 - p) << 10;
+      v |= v << 16;
+      asm volatile("" : "+v"(v));  // keep it in a vector register
+      m[p] = v;
+    }
+  }
+};
+
+// The pair of fields at bit P of the halves of t (P + BITS <= 10), as fp16 codes.
+template <int BITS, int P>
+__device__ __forceinline__ half2v code_pair(uint32_t t, const Magics& mg) {
+  static_assert(P + BITS <= 10 && P < 8, "field inside the fp16 mantissa, one of the eight OR constants");
+  constexpr uint32_t mask = (((1u << BITS) - 1u) << P) * 0x00010001u;
+  const uint32_t v = (t & mask) | mg.m[P];
+  constexpr float off = (float)(1 << (10 - P));
+  return __builtin_bit_cast(half2v, v) - (half2v){(half_t)off, (half_t)off};
 }
 
-// sum_j c_j x_j over one chunk: xp[p] = (x_A(p), x_B(p)), xs[q] = x_S(q).
-template <int BITS>
-__device__ __forceinline__ float chunk_dot(const uint32_t (&w)[BITS], const half2v (&xp)[ChunkPairs<BITS>::NP],
-                                           const float (&xs)[ChunkPairs<BITS>::NS > 0 ? ChunkPairs<BITS>::NS : 1],
-                                           uint32_t magic) {
-  float acc = 0.0f;
-  if constexpr (BITS == 3) {
-    const uint32_t X = (w[0] & 0xFFFFu) | (w[1] & 0xFFFF0000u);
-    const uint32_t Y = __builtin_amdgcn_alignbit(w[2], w[0], 16);
-    const uint32_t Z = (w[1] & 0xFFFFu) | (w[2] & 0xFFFF0000u);
-#pragma unroll
-    for (int i = 0; i < 5; ++i) acc = __builtin_amdgcn_fdot2(code_pair<3>(X, 3 * i, magic), xp[i], acc, false);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(code_pair<3>(Y, 2 + 3 * i, magic), xp[5 + i], acc, false);
-#pragma unroll
-    for (int i = 0; i < 5; ++i) acc = __builtin_amdgcn_fdot2(code_pair<3>(Z, 1 + 3 * i, magic), xp[9 + i], acc, false);
-    const uint32_t c5 = (w[0] >> 15) & 7u;
-    const uint32_t c10 = __builtin_amdgcn_alignbit(w[1], w[0], 30) & 7u;
-    const uint32_t c21 = __builtin_amdgcn_alignbit(w[2], w[1], 31) & 7u;
-    const uint32_t c26 = (w[2] >> 14) & 7u;
-    acc = fmaf((float)c5, xs[0], acc);
-    acc = fmaf((float)c10, xs[1], acc);
-    acc = fmaf((float)c21, xs[2], acc);
-    acc = fmaf((float)c26, xs[3], acc);
-  } else {
-    constexpr int PW = 16 / BITS;  // pairs per word
-#pragma unroll
-    for (int k = 0; k < BITS; ++k)
-#pragma unroll
-      for (int i = 0; i < PW; ++i)
-        acc = __builtin_amdgcn_fdot2(code_pair<BITS>(w[k], BITS * i, magic), xp[k * PW + i], acc, false);
+// Pair at bit P of word t (any P <= 16 - BITS), t8 = t >> 8: in place for
+// P < 8 and P + BITS <= 10, else from t8 (at P - 8 < 8, P - 8 + BITS <= 8).
+template <int BITS, int P>
+__device__ __forceinline__ half2v pair_at(uint32_t t, uint32_t t8, const Magics& mg) {
+  if constexpr (P + BITS <= 10 && P < 8)
+    return code_pair<BITS, P>(t, mg);
+  else
+    return code_pair<BITS, P - 8>(t8, mg);
+}
+
+template <int BITS, int K, int I>
+__device__ __forceinline__ void word_pairs(uint32_t t, uint32_t t8, half2v* cp, const Magics& mg) {
+  if constexpr (I < 16 / BITS) {
+    cp[K * (16 / BITS) + I] = pair_at<BITS, BITS * I>(t, t8, mg);
+    word_pairs<BITS, K, I + 1>(t, t8, cp, mg);
   }
+}
+
+template <int BITS, int K>
+__device__ __forceinline__ void words(const uint32_t (&w)[BITS], half2v* cp, const Magics& mg) {
+  if constexpr (K < BITS) {
+    word_pairs<BITS, K, 0>(w[K], w[K] >> 8, cp, mg);
+    words<BITS, K + 1>(w, cp, mg);
+  }
+}
+
+// 3-bit: the pairs of word t whose fields start at bit P0 + 3 i, i < N, into
+// cp[X0 + i].
+template <int P0, int N, int X0, int I = 0>
+__device__ __forceinline__ void word3(uint32_t t, uint32_t t8, half2v* cp, const Magics& mg) {
+  if constexpr (I < N) {
+    cp[X0 + I] = pair_at<3, P0 + 3 * I>(t, t8, mg);
+    word3<P0, N, X0, I + 1>(t, t8, cp, mg);
+  }
+}
+
+// sum_j c_j x_j over one chunk: xp[p] = (x_A(p), x_B(p)). All 16 code pairs are
+// formed before the dot products, so that no dot waits on the subtract just
+// before it.
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(const uint32_t (&w)[BITS], const half2v (&xp)[16], const Magics& mg) {
+  half2v cp[16];
+  if constexpr (BITS == 3) {
+    const uint32_t X = __builtin_amdgcn_perm(w[1], w[0], 0x07060100u);  // w0 low half, w1 high half
+    const uint32_t Y = __builtin_amdgcn_alignbit(w[2], w[0], 16);
+    const uint32_t Z = __builtin_amdgcn_perm(w[2], w[1], 0x07060100u);  // w1 low half, w2 high half
+    word3<0, 5, 0>(X, X >> 8, cp, mg);
+    word3<2, 4, 5>(Y, Y >> 8, cp, mg);
+    word3<1, 5, 9>(Z, Z >> 8, cp, mg);
+    // code 5 = S[15,18) = w0 >> 15, code 21 = S[63,66) = (w2:w1) >> 31,
+    // code 10 = S[30,33) = (w1:w0) >> 30, code 26 = S[78,81) = w2 >> 14:
+    // each pair's low half-words joined into one word, fields at bit 0
+    const uint32_t P = __builtin_amdgcn_perm(__builtin_amdgcn_alignbit(w[2], w[1], 31), w[0] >> 15, 0x05040100u);
+    const uint32_t Q = __builtin_amdgcn_perm(w[2] >> 14, __builtin_amdgcn_alignbit(w[1], w[0], 30), 0x05040100u);
+    cp[14] = code_pair<3, 0>(P, mg);
+    cp[15] = code_pair<3, 0>(Q, mg);
+  } else {
+    words<BITS, 0>(w, cp, mg);
+  }
+  float acc = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) acc = __builtin_amdgcn_fdot2(cp[p], xp[p], acc, false);
   return acc;
 }
 
@@ -105,60 +151,69 @@ __device__ __forceinline__ float chunk_dot(const uint32_t (&w)[BITS], const half
 // each row (chunk k = words [k BITS, (k + 1) BITS) of the row, which lie in one
 // group because groups are multiples of 32 columns). Per chunk the lane forms
 // cx = sum c_j x_j (code pairs and dot2, above) and sx = sum x_j in fp32 and
-// adds s (cx - z sx); the lanes' sums are added across the wave. The codes, scales, zero points and x of the
-// lane's next chunk are loaded before the current one is used, so that two
-// chunks per row are in flight. The look-ahead load is unconditional (the last
-// chunk loads itself again), so that the wait before each chunk's use counts
-// only the older loads.
+// adds s (cx - z sx); the lanes' sums are added across the wave. The codes,
+// scales, zero points and x of the lane's next chunk are loaded before the
+// current one is used, into the other of two register sets (two chunks per
+// row in flight, and no copies between the sets). The look-ahead load is
+// unconditional (the last chunk loads itself again), so that the wait before
+// each chunk's use counts only the older loads. Row addresses are wave-uniform
+// (rows past m repeat the last row, unused), lane offsets 32-bit.
+template <int BITS, int GV_ROWS>
+struct ChunkRegs {
+  uint32_t w[GV_ROWS][BITS];
+  float s[GV_ROWS];
+  uint32_t z[GV_ROWS];
+  half8 x[4];
+};
+
 template <int BITS, int GV_ROWS>
 __global__ __launch_bounds__(256) void dq_gemv_kernel(const uint32_t* q, const float* scales, const uint8_t* zeros,
                                                       int64_t m, int64_t d, int group, int ngroups, const half_t* x,
                                                       float* y) {
   const int lane = threadIdx.x & 63;
-  const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * GV_ROWS;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform: row pointers in SGPRs
+  const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * GV_ROWS;
   if (r0 >= m) return;  // uniform per wave
-  const int64_t nch = d / 32, wpr = d * BITS / 32;
+  const int nch = (int)(d / 32);
+  const int64_t wpr = d * BITS / 32;
+  const uint32_t* qrow[GV_ROWS];
+  const float* srow[GV_ROWS];
+  const uint8_t* zrow[GV_ROWS];
+#pragma unroll
+  for (int rr = 0; rr < GV_ROWS; ++rr) {
+    const int64_t r = r0 + rr < m ? r0 + rr : m - 1;
+    qrow[rr] = q + r * wpr;
+    srow[rr] = scales + r * ngroups;
+    zrow[rr] = zeros + r * ngroups;
+  }
   float acc[GV_ROWS];
 #pragma unroll
   for (int rr = 0; rr < GV_ROWS; ++rr) acc[rr] = 0.0f;
-  uint32_t magic;
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
-  uint32_t wc[GV_ROWS][BITS];
-  float sc[GV_ROWS];
-  uint32_t zc[GV_ROWS];
-  half8 xc[4];
-  auto load = [&](int64_t k, uint32_t (&w)[GV_ROWS][BITS], float (&sv)[GV_ROWS], uint32_t (&zv)[GV_ROWS],
-                  half8 (&xv)[4]) {
-    const int64_t g = group ? (32 * k) / group : 0;
-    GPTQ_DASSERT(k >= 0 && k < nch && g < ngroups);
+  const Magics mg;
+  using Regs = ChunkRegs<BITS, GV_ROWS>;
+  auto load = [&](int k, Regs& c) __attribute__((always_inline)) {
+    // 32-bit byte offsets from wave-uniform bases (scalar-base addressing)
+    const uint32_t g = group ? (uint32_t)(32 * k) / (uint32_t)group : 0u, kb = (uint32_t)k * (4 * BITS);
+    GPTQ_DASSERT(k >= 0 && k < nch && (int)g < ngroups);
 #pragma unroll
     for (int rr = 0; rr < GV_ROWS; ++rr) {
-      const int64_t r = r0 + rr < m ? r0 + rr : m - 1;  // rows past m repeat the last row, unused
 #pragma unroll
-      for (int b = 0; b < BITS; ++b) w[rr][b] = q[r * wpr + k * BITS + b];
-      sv[rr] = scales[r * ngroups + g];
-      zv[rr] = zeros[r * ngroups + g];
+      for (int b = 0; b < BITS; ++b) c.w[rr][b] = ((const uint32_t*)((const char*)qrow[rr] + kb))[b];
+      c.s[rr] = *(const float*)((const char*)srow[rr] + 4 * g);
+      c.z[rr] = zrow[rr][g];
     }
-    const half8* xp = (const half8*)(x + 32 * k);
+    const half8* xp = (const half8*)((const char*)x + 64 * (uint32_t)k);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) xv[v] = xp[v];
+    for (int v = 0; v < 4; ++v) c.x[v] = xp[v];
   };
-  if (lane < nch) load(lane, wc, sc, zc, xc);
-  for (int64_t k = lane; k < nch; k += 64) {
-    uint32_t wn[GV_ROWS][BITS];
-    float sn[GV_ROWS];
-    uint32_t zn[GV_ROWS];
-    half8 xn[4];
-    load(k + 64 < nch ? k + 64 : k, wn, sn, zn, xn);
-    asm volatile("" ::: "memory");  // the look-ahead loads stay ahead of this chunk's arithmetic
+  auto compute = [&](const Regs& c) __attribute__((always_inline)) {
     using CP = ChunkPairs<BITS>;
     half_t xh[32];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xh[8 * v + e] = xc[v][e];
-    half2v xp[CP::NP];
-    float xs[CP::NS > 0 ? CP::NS : 1];
+      for (int e = 0; e < 8; ++e) xh[8 * v + e] = c.x[v][e];
+    half2v xp[16];
     float sx = 0.0f;
 #pragma unroll
     for (int p = 0; p < CP::NP; ++p) {
@@ -166,24 +221,21 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const uint32_t* q, const f
       sx = __builtin_amdgcn_fdot2(xp[p], (half2v){(half_t)1.0f, (half_t)1.0f}, sx, false);
     }
 #pragma unroll
-    for (int q = 0; q < CP::NS; ++q) {
-      xs[q] = (float)xh[CP::S(q)];
-      sx += xs[q];
-    }
-#pragma unroll
     for (int rr = 0; rr < GV_ROWS; ++rr) {
-      const float cx = chunk_dot<BITS>(wc[rr], xp, xs, magic);
-      acc[rr] = fmaf(sc[rr], fmaf(-(float)zc[rr], sx, cx), acc[rr]);
+      const float cx = chunk_dot<BITS>(c.w[rr], xp, mg);
+      acc[rr] = fmaf(c.s[rr], fmaf(-(float)c.z[rr], sx, cx), acc[rr]);
     }
-#pragma unroll
-    for (int rr = 0; rr < GV_ROWS; ++rr) {
-#pragma unroll
-      for (int b = 0; b < BITS; ++b) wc[rr][b] = wn[rr][b];
-      sc[rr] = sn[rr];
-      zc[rr] = zn[rr];
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) xc[v] = xn[v];
+  };
+  Regs ca, cb;
+  if (lane < nch) load(lane, ca);
+  for (int k = lane; k < nch; k += 128) {
+    load(k + 64 < nch ? k + 64 : k, cb);
+    asm volatile("" ::: "memory");  // the look-ahead loads stay ahead of this chunk's arithmetic
+    compute(ca);
+    if (k + 64 >= nch) break;
+    load(k + 128 < nch ? k + 128 : k + 64, ca);
+    asm volatile("" ::: "memory");
+    compute(cb);
   }
 #pragma unroll
   for (int rr = 0; rr < GV_ROWS; ++rr) {

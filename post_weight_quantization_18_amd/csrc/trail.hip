@@ -34,7 +34,10 @@ constexpr int TM = 256, TN = 128, KS = 32, NT = 512, NBUF = 3;
 constexpr int ROWB = KS * 2;                       // bytes per LDS panel row (32 halves)
 constexpr uint32_t OFF_AH = 0, OFF_AL = TM * ROWB, OFF_BH = 2 * TM * ROWB, OFF_BL = 2 * TM * ROWB + TN * ROWB;
 constexpr uint32_t STAGE_BYTES = (2 * TM + 2 * TN) * ROWB;  // 48 KB
-constexpr int GROUP_M = 8;
+#ifndef GPTQ_TGEMM_GROUP_M
+#define GPTQ_TGEMM_GROUP_M 4
+#endif
+constexpr int GROUP_M = GPTQ_TGEMM_GROUP_M;
 
 __device__ const uint4 kZeroT[1] = {{0u, 0u, 0u, 0u}};
 
