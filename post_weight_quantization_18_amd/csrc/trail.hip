@@ -21,9 +21,11 @@
 //    the 16-byte chunks of a row are XOR-swizzled by (row / 4) mod 4, chosen on
 //    the global side, which makes the fragment reads (ds_read_b128, 32 rows x 2
 //    chunks per wave) free of bank conflicts.
-//  * Workgroups run in groups of 8 row tiles per column tile, and the groups
+//  * Workgroups run in groups of 4 row tiles per column tile, and the groups
 //    are laid out contiguously per XCD, so that the tiles resident on one XCD
 //    share their A and B panels in its L2.
+//  * Wide updates (the super-block GEMMs) take 256 x 256 tiles instead
+//    (tgemm_wide_kernel below).
 #include "common.h"
 
 namespace gptq {
@@ -34,10 +36,7 @@ constexpr int TM = 256, TN = 128, KS = 32, NT = 512, NBUF = 3;
 constexpr int ROWB = KS * 2;                       // bytes per LDS panel row (32 halves)
 constexpr uint32_t OFF_AH = 0, OFF_AL = TM * ROWB, OFF_BH = 2 * TM * ROWB, OFF_BL = 2 * TM * ROWB + TN * ROWB;
 constexpr uint32_t STAGE_BYTES = (2 * TM + 2 * TN) * ROWB;  // 48 KB
-#ifndef GPTQ_TGEMM_GROUP_M
-#define GPTQ_TGEMM_GROUP_M 4
-#endif
-constexpr int GROUP_M = GPTQ_TGEMM_GROUP_M;
+constexpr int GROUP_M = 4;  // row tiles per column tile in the grouped order (the 32 workgroups of an XCD on 4 x 8 tiles)
 
 __device__ const uint4 kZeroT[1] = {{0u, 0u, 0u, 0u}};
 
@@ -226,16 +225,204 @@ __global__ __launch_bounds__(NT, 1) void tgemm_kernel(TgemmArgs a, int ntm, int 
   }
 }
 
+// The same product on 256 x 256 output tiles, for wide updates (N of a few
+// thousand columns and more): 8 waves of 64 x 128 (32 accumulator blocks of
+// 32 x 32 per wave in 128 fp32 registers); each 32-deep K stage is 64 KB of
+// operand panels (A hi/lo 256 x 32, B hi/lo 256 x 32) in a 2-deep ring, so the
+// DMA moves a third fewer bytes per flop than on 256 x 128 tiles and the
+// fragment reads a quarter fewer. Stage s + 1 is issued into the other buffer
+// right after the barrier that ends stage s - 1's reads.
+constexpr int TNW = 256, NBUFW = 2;
+constexpr uint32_t W_OFF_AH = 0, W_OFF_AL = TM * ROWB, W_OFF_BH = 2 * TM * ROWB, W_OFF_BL = 2 * TM * ROWB + TNW * ROWB;
+constexpr uint32_t W_STAGE_BYTES = (2 * TM + 2 * TNW) * ROWB;  // 64 KB
+
+__global__ __launch_bounds__(NT, 1) void tgemm_wide_kernel(TgemmArgs a, int ntm, int ntn) {
+  __shared__ __attribute__((aligned(1024))) char ring[NBUFW * W_STAGE_BYTES];
+
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int per_group = GROUP_M * ntn;
+  const int grp = logical / per_group, first_m = grp * GROUP_M;
+  const int gm = (ntm - first_m) < GROUP_M ? (ntm - first_m) : GROUP_M;
+  const int within = logical - grp * per_group;
+  const int tm = first_m + within % gm, tn = within / gm;
+  const int64_t I0 = (int64_t)tm * TM, J0 = (int64_t)tn * TNW;
+  GPTQ_DASSERT(tm < ntm && tn < ntn && I0 < a.M && J0 < a.N && a.K % KS == 0);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int wi = w >> 1, wj = w & 1;  // wave tile: rows 64 wi .., cols 128 wj ..
+  const int nst = (int)(a.K / KS);
+
+  // DMA plan: wave w moves A rows 32w .. 32w+31 and B rows (columns of the
+  // update) 32w .. 32w+31, hi and lo: eight 1 KB instructions per stage, lane
+  // l on row (l / 4) of the instruction's 16 rows at LDS chunk position l % 4
+  // (global chunk (l % 4) ^ ((row / 4) % 4)), as in tgemm_kernel.
+  const int lrow = lane >> 2;
+  const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  int64_t srcA[2], srcB[2];
+  bool okA[2], okB[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int64_t r = I0 + 32 * w + 16 * e + lrow;
+    okA[e] = r < a.M;
+    srcA[e] = (okA[e] ? r : 0) * 32 + 8 * chunk;
+    const int64_t c = J0 + 32 * w + 16 * e + lrow;
+    okB[e] = c < a.N;
+    srcB[e] = (okB[e] ? c : 0) * 32 + 8 * chunk;
+  }
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GPTQ_LDS void*)ring);
+  // instruction e (0..7) of stage s into ring buffer b: e = 0..3 A (hi h0, hi
+  // h1, lo h0, lo h1), e = 4..7 B likewise
+  auto issue = [&](int e, int s, int b) {
+    const int64_t k0 = (int64_t)s * KS;
+    const int h = e & 1;
+    const void* src;
+    uint32_t off;
+    if (e < 4) {
+      const half_t* base = (e < 2) ? a.Ah : a.Al;
+      src = okA[h] ? (const void*)(base + (k0 >> 5) * a.a_kslab + srcA[h]) : (const void*)kZeroT;
+      off = ((e < 2) ? W_OFF_AH : W_OFF_AL) + (uint32_t)((32 * wu + 16 * h) * ROWB);
+    } else {
+      const half_t* base = (e < 6) ? a.Bh : a.Bl;
+      src = okB[h] ? (const void*)(base + (k0 >> 7) * a.b_block + ((k0 & 127) >> 5) * a.b_kslab + srcB[h])
+                   : (const void*)kZeroT;
+      off = ((e < 6) ? W_OFF_BH : W_OFF_BL) + (uint32_t)((32 * wu + 16 * h) * ROWB);
+    }
+    dma16(src, ring_lds + (uint32_t)b * W_STAGE_BYTES + off);
+  };
+
+  const int frow = lane & 31, fsw = (lane >> 2) & 3, fhi = lane >> 5;
+  uint32_t offA[2][2], offB[4][2];  // [subtile][kk]
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const uint32_t pos = (uint32_t)(((2 * kk + fhi) ^ fsw) * 16);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) offA[x][kk] = (uint32_t)((64 * wi + 32 * x + frow) * ROWB) + pos;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) offB[y][kk] = (uint32_t)((128 * wj + 32 * y + frow) * ROWB) + pos;
+  }
+
+  float16v acc[2][4];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
+
+  auto compute = [&](int b, bool refill, int s_next, int b_next) {
+    const char* st = ring + (size_t)b * W_STAGE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      half8 ah[2], al[2], bh[4], bl[4];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        ah[x] = lds_frag(st, W_OFF_AH + offA[x][kk]);
+        al[x] = lds_frag(st, W_OFF_AL + offA[x][kk]);
+      }
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        bh[y] = lds_frag(st, W_OFF_BH + offB[y][kk]);
+        bl[y] = lds_frag(st, W_OFF_BL + offB[y][kk]);
+      }
+      if (refill) {
+#pragma unroll
+        for (int e = 4 * kk; e < 4 * kk + 4; ++e) issue(e, s_next, b_next);
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[x], bh[y], acc[x][y], 0, 0, 0);
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[x], bl[y], acc[x][y], 0, 0, 0);
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[x], bh[y], acc[x][y], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (nst > 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) issue(e, 0, 0);
+  }
+  for (int s = 0; s < nst; ++s) {
+    // stage s's eight loads are the only ones in flight; after the barrier no
+    // wave reads the other buffer (stage s - 1) any more, so stage s + 1 may
+    // land there while this one is computed
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    lds_barrier();
+    compute(s & 1, s + 1 < nst, s + 1, (s + 1) & 1);
+  }
+
+  // ---- epilogue: C -= acc * rowscale[i] * cscale (loads of a 16-row group
+  // before its stores, as in tgemm_kernel) ----
+  const float cs = *a.cscale;
+  const int hl = lane >> 5, col = lane & 31;
+  const bool full = (I0 + TM <= a.M) && (J0 + TNW <= a.N);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int64_t ib = I0 + 64 * wi + 32 * x + 4 * hl;
+    float sc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t i = ib + 8 * (r >> 2) + (r & 3);
+      sc[r] = (i < a.M) ? a.rowscale[i] : 0.0f;
+    }
+#pragma unroll
+    for (int yh = 0; yh < 2; ++yh) {  // two 32-column blocks at a time keep the staged values to 32 registers
+      if (full) {
+        float cv[2][16];
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            cv[y][r] = a.C[(ib + 8 * (r >> 2) + (r & 3)) * a.ldc + J0 + 128 * wj + 32 * (2 * yh + y) + col];
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            a.C[(ib + 8 * (r >> 2) + (r & 3)) * a.ldc + J0 + 128 * wj + 32 * (2 * yh + y) + col] =
+                fmaf(-acc[x][2 * yh + y][r], sc[r] * cs, cv[y][r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t i = ib + 8 * (r >> 2) + (r & 3);
+          if (i >= a.M) continue;
+#pragma unroll
+          for (int y = 0; y < 2; ++y) {
+            const int64_t j = J0 + 128 * wj + 32 * (2 * yh + y) + col;
+            if (j < a.N) {
+              float* c = a.C + i * a.ldc + j;
+              *c = fmaf(-acc[x][2 * yh + y][r], sc[r] * cs, *c);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 gptq_status_t tgemm_enqueue(const TgemmArgs& a, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return GPTQ_OK;
   if (a.K % KS) return GPTQ_ERR_INVALID_ARG;
-  const int64_t ntm = ceil_div(a.M, TM), ntn = ceil_div(a.N, TN);
+  // 256 x 256 tiles for the super-block GEMMs; the narrow updates inside a
+  // super-block keep twice as many 256 x 128 tiles
+  const bool wide = a.N >= 4096;
+  const int tn = wide ? TNW : TN;
+  const int64_t ntm = ceil_div(a.M, TM), ntn = ceil_div(a.N, tn);
   if (ntm * ntn > 0x7fffffff) return GPTQ_ERR_UNSUPPORTED;
   // executed: three fp16 passes over the padded tiles
-  TraceScope tr(st, GPTQ_TRACE_TGEMM, 3.0 * 2.0 * (double)(ntm * TM) * (double)(ntn * TN) * (double)a.K);
-  hipLaunchKernelGGL(tgemm_kernel, dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a, (int)ntm, (int)ntn);
+  TraceScope tr(st, GPTQ_TRACE_TGEMM, 3.0 * 2.0 * (double)(ntm * TM) * (double)(ntn * tn) * (double)a.K);
+  if (wide)
+    hipLaunchKernelGGL(tgemm_wide_kernel, dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a, (int)ntm, (int)ntn);
+  else
+    hipLaunchKernelGGL(tgemm_kernel, dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a, (int)ntm, (int)ntn);
   GPTQ_CHECK_LAUNCH();
   return GPTQ_OK;
 }
