@@ -104,7 +104,7 @@ const char* gptq_status_string(int32_t status);
 /* Bytes of workspace the named call needs for these sizes (0 = none).
  *  which = GPTQ_WS_ACCUMULATE_HESSIAN: uses d and n (tokens per call): the
  *          split-K partial tiles, then for d >= 12288 a feature-major copy
- *          of the call's tokens (d x n fp16, at most d x 32768 when the call
+ *          of the call's tokens (d x n fp16, at most d x 65536 when the call
  *          is cut into launches). A smaller workspace (even NULL / 0) is accepted: without
  *          room for the copy X is read token-major (a slower form of the same
  *          sum), without room for the partials the token-split parallelism

@@ -611,14 +611,17 @@ int syrk_ntiles(int64_t d) {
   return (int)(T * (T + 1));
 }
 
-constexpr int64_t kLaunchTokens = 32768;
+constexpr int64_t kLaunchTokens = 65536;
 constexpr int64_t kXtMinD = 12288;     // the feature-major form from this width on
 constexpr int kSkMax = 256;            // stream-K workgroups: one round
 constexpr int64_t kSkMinStages = 16;   // at least 1024 tokens per stream-K range
 
 // Tokens per launch: with whole rounds of tiles to run (ntiles >= 256) a long
-// token range is cut into launches of kLaunchTokens (measured faster at
-// d = 12288 than one long launch); otherwise one launch takes them all.
+// token range is cut into launches of kLaunchTokens, which bounds the
+// feature-major copy in the workspace (d x 65536 fp16); otherwise one launch
+// takes them all. Measured over 262144 tokens: at d = 49152 launches of 65536
+// tokens take 1.4 % less than launches of 32768 (one launch of all 262144
+// 1.8 % less, with a 25.8 GB copy); at d = 12288 they are even.
 int64_t syrk_launch_tokens(int64_t d, int64_t n) {
   return (syrk_ntiles(d) >= kSkMax && n > 2 * kLaunchTokens) ? kLaunchTokens : n;
 }
@@ -776,8 +779,8 @@ gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const hal
   }
   const size_t part_bytes = syrk_partial_bytes(p, d);
   // the feature-major copy when the workspace holds it after the partials and
-  // d is wide enough to repay the transpose (measured: 2.5 % faster at
-  // d = 49152, 1.5 % slower at d = 12288, 13 % slower at d = 2560)
+  // d is wide enough to repay the transpose (measured with the banded tile
+  // order: 3.8 % faster at d = 12288; 13 % slower at d = 2560 in row order)
   const bool xt = allow_xt && d >= kXtMinD && ws != nullptr && ws_bytes >= part_bytes + syrk_xt_bytes(d, n);
   const int64_t Tpad = ceil_div(n, KS) * KS;
   half_t* XT = xt ? (half_t*)((char*)ws + part_bytes) : nullptr;

@@ -52,11 +52,11 @@ def test_workspace_sizes(lib):
     # 110 tiles < 256: one launch of all tokens, split in two, one partial tile per tile and split
     assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, d, n) == 2 * 110 * tile
     assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 768, 4096) == 3 * 12 * tile
-    # 37056 tiles: launches of 32768 tokens; 144 whole rounds, then 192 tiles over
+    # 37056 tiles: launches of 65536 tokens; 144 whole rounds, then 192 tiles over
     # one stream-K round of 256 workgroups with two partial tiles each
-    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 49152, n) == 256 * 2 * tile + 49152 * 32768 * 2
+    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 49152, n) == 256 * 2 * tile + 49152 * 65536 * 2
     # 256 x 257 tiles: whole rounds only, no partials
-    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 65536, n) == 65536 * 32768 * 2
+    assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 65536, n) == 65536 * 65536 * 2
     # the copy starts at d = 12288 (20000 tokens round up to 20032 there); below,
     # the partials alone (at most 512 tiles of the stream-K round)
     assert G.workspace_bytes(G.WS_ACCUMULATE_HESSIAN, 0, 12288, 20000) >= 12288 * 20032 * 2
