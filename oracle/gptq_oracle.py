@@ -66,6 +66,13 @@ GRID_SYM = "sym"
 # ---------------------------------------------------------------------------
 # Step 1: the Hessian of the layer-wise objective.
 # ---------------------------------------------------------------------------
+# numpy hands products of the form x.T @ x, and LAPACK its Cholesky updates,
+# to the BLAS symmetric rank-k update, which in the OpenBLAS build here crashes
+# once the output has 2^31 entries (d >= 46341: the OPT-175B fc2 width). From
+# that size on, hessian and hessian_factor take the same results another way.
+BLAS_SYRK_MAX = 2 ** 31
+
+
 def hessian(x_chunks) -> np.ndarray:
     """H = 2 * sum_c X_c^T X_c in fp64 over token-major chunks X_c [n_c, d].
 
@@ -79,7 +86,8 @@ def hessian(x_chunks) -> np.ndarray:
     h = None
     for xc in x_chunks:
         x = np.asarray(xc, dtype=np.float64)
-        part = x.T @ x
+        # from BLAS_SYRK_MAX on, a general product of an explicit copy of x^T
+        part = x.T @ x if x.shape[1] ** 2 < BLAS_SYRK_MAX else np.ascontiguousarray(x.T) @ x
         h = part if h is None else h + part
     return 2.0 * h
 
@@ -148,7 +156,7 @@ def inverse_hessian_factor(h_damped) -> np.ndarray:
     return np.triu(lower.T)
 
 
-def hessian_factor(h_damped) -> np.ndarray:
+def hessian_factor(h_damped, block=None, progress=None) -> np.ndarray:
     """R upper triangular with positive diagonal and R R^T = H_d, so that
     R^-1 is the factor U of inverse_hessian_factor (U^T U = H_d^-1 gives
     H_d = U^-1 U^-T).
@@ -156,13 +164,50 @@ def hessian_factor(h_damped) -> np.ndarray:
     [FDE] section 01: the needed rows of the inverse Hessian are taken from a
     Cholesky decomposition of the Hessian. The definition is written out with
     the reversal permutation J: L = chol(J H_d J) (lower), R = J L J.
-    Raises numpy.linalg.LinAlgError when H_d is not positive definite.
+    Raises numpy.linalg.LinAlgError when H_d is not positive definite. block:
+    take L by the blocked algorithm with that block width (always used once
+    d * d reaches BLAS_SYRK_MAX); progress(k, d), when given, is called after
+    each of its column blocks (k columns done).
     """
     hd = np.asarray(h_damped, dtype=np.float64)
     d = hd.shape[0]
-    rev = np.arange(d)[::-1]
-    lower = np.linalg.cholesky(hd[np.ix_(rev, rev)])
-    return np.triu(lower[np.ix_(rev, rev)])
+    a = np.ascontiguousarray(hd[::-1, ::-1])  # J H_d J
+    if block is None and d * d < BLAS_SYRK_MAX:
+        lower = np.linalg.cholesky(a)
+    else:
+        # from BLAS_SYRK_MAX on, the same factor by the blocked algorithm below
+        lower = _cholesky_lower_blocked(a, block or 4096, progress)
+    return np.triu(lower[::-1, ::-1])  # J L J
+
+
+def _cholesky_lower_blocked(a, b, progress=None):
+    """The lower Cholesky factor of the symmetric positive definite a, b
+    columns at a time (the textbook right-looking block algorithm; a is
+    overwritten): the diagonal block A11 = L11 L11^T (LAPACK), the block column
+    below it L21 = A21 L11^-T (a solve with L11), and the rest of the lower
+    triangle A22 -= L21 L21^T (general matrix products of explicit copies, one
+    column block at a time)."""
+    d = a.shape[0]
+    for k0 in range(0, d, b):
+        k1 = min(k0 + b, d)
+        l11 = np.linalg.cholesky(a[k0:k1, k0:k1])
+        a[k0:k1, k0:k1] = l11
+        if k1 == d:
+            if progress is not None:
+                progress(k1, d)
+            break
+        l21 = np.linalg.solve(l11, a[k1:, k0:k1].T).T  # L11 L21^T = A21^T
+        a[k1:, k0:k1] = l21
+        l21c = np.ascontiguousarray(l21)
+        for j0 in range(k1, d, b):
+            j1 = min(j0 + b, d)
+            # rows from j0 on: the lower triangle of the column block
+            a[j0:, j0:j1] -= l21c[j0 - k1:] @ np.ascontiguousarray(l21c[j0 - k1:j1 - k1].T)
+        if progress is not None:
+            progress(k1, d)
+    for k0 in range(0, d, b):  # the strict upper triangle (never written) to zero
+        a[k0:k0 + b, k0 + 1:] = np.tril(a[k0:k0 + b, k0 + 1:], -1)
+    return a
 
 
 # ---------------------------------------------------------------------------

@@ -91,32 +91,51 @@ def write_record(out_dir, rec):
     print(line, flush=True)
 
 
+def upper_inverse(r, leaf=4096, say=None):
+    """The inverse of the upper triangular r by halves: [[A, B], [0, C]]^-1 =
+    [[A^-1, -A^-1 B C^-1], [0, C^-1]], leaves of at most `leaf` columns by a
+    triangular solve. Only general matrix products of explicit copies touch
+    the whole width (the BLAS routines for symmetric or triangular operands
+    are not trusted with arrays of 2^31 entries)."""
+    import scipy.linalg as sl
+    n = r.shape[0]
+    if n <= leaf:
+        return sl.solve_triangular(r, np.eye(n), lower=False)
+    k = max(leaf, (n // 2) // leaf * leaf)
+    ai = upper_inverse(r[:k, :k], leaf, say)
+    ci = upper_inverse(r[k:, k:], leaf, say)
+    out = np.zeros((n, n))
+    out[:k, :k] = ai
+    out[k:, k:] = ci
+    out[:k, k:] = -(ai @ np.ascontiguousarray(r[:k, k:])) @ ci
+    if say is not None:
+        say(f"[harness] oracle U = R^-1: block of {n} columns done")
+    return out
+
+
 def oracle_factor_in_steps(xh, damp, chunk=4096):
     """The oracle's H over the tokens chunk by chunk (each chunk's 2 X_c^T X_c
-    summed in order, which is exactly the oracle's own sum), lambda, and U as
-    the inverse of the oracle's R = hessian_factor(H_d), column block by column
-    block (U = R^-1 is pinned in the oracle's tests). Every step prints a line,
-    so that the longest silent step is one chunk or one block."""
+    summed in order, which is exactly the oracle's own sum), lambda, its R =
+    hessian_factor(H_d) (a line per column block), and U = R^-1 (pinned in
+    the oracle's tests) by halves. Every step prints a line, so that the
+    longest silent step is one chunk or one block."""
     import oracle as O
-    import scipy.linalg as sl
     n, d = xh.shape
     h = None
     for t0 in range(0, n, chunk):
         part = O.hessian(xh[t0:t0 + chunk])
-        h = part if h is None else h + part
+        if h is None:
+            h = part
+        else:
+            h += part  # the oracle's sum over chunks, in place
+        del part
         print(f"[harness] oracle H: {min(t0 + chunk, n)} / {n} tokens", flush=True)
     hd, lam = O.damp(h, damp)
-    r = O.hessian_factor(hd)
+    r = O.hessian_factor(hd, progress=lambda k, dd: print(f"[harness] oracle R: {k} / {dd} columns", flush=True))
     print("[harness] oracle R = hessian_factor(H_d) done", flush=True)
-    u = np.empty_like(r)
-    blk = 4096
-    for c0 in range(0, d, blk):
-        c1 = min(c0 + blk, d)
-        e = np.zeros((d, c1 - c0))
-        e[c0:c1] = np.eye(c1 - c0)
-        u[:, c0:c1] = sl.solve_triangular(r, e, lower=False)
-        print(f"[harness] oracle U = R^-1: columns {c1} / {d}", flush=True)
-    return h, lam, np.triu(u), hd, r
+    u = upper_inverse(r, say=lambda m: print(m, flush=True))  # upper triangular by construction
+    print("[harness] oracle U = R^-1 done", flush=True)
+    return h, lam, u, hd, r
 
 
 def compare_rows_in_steps(wn, gpu, oracle, bits, group, grid, label):

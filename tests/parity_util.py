@@ -62,13 +62,22 @@ def say(*a):
         sys.stdout.flush()
 
 
-def lower_rel_fro(h_gpu: np.ndarray, h_orc: np.ndarray) -> float:
-    il = np.tril_indices(h_orc.shape[0])
-    a = h_gpu[il].astype(np.float64)
-    b = h_orc[il]
-    # off-diagonal entries count twice in the symmetric matrix
-    wgt = np.where(il[0] == il[1], 1.0, 2.0)
-    return float(np.sqrt(np.sum(wgt * (a - b) ** 2) / np.sum(wgt * b * b)))
+def lower_rel_fro(h_gpu: np.ndarray, h_orc: np.ndarray, rows: int = 2048) -> float:
+    """Relative Frobenius distance of the symmetric matrices whose lower
+    triangles h_gpu and h_orc hold (off-diagonal entries count twice), taken
+    over blocks of rows so that no index array of the whole triangle is made."""
+    d = h_orc.shape[0]
+    num = den = 0.0
+    for i0 in range(0, d, rows):
+        i1 = min(i0 + rows, d)
+        a = np.asarray(h_gpu[i0:i1, :i1], dtype=np.float64)
+        b = np.asarray(h_orc[i0:i1, :i1], dtype=np.float64)
+        ii = np.arange(i0, i1)[:, None]
+        jj = np.arange(i1)[None, :]
+        wgt = np.where(jj < ii, 2.0, np.where(jj == ii, 1.0, 0.0))
+        num += float(np.sum(wgt * (a - b) ** 2))
+        den += float(np.sum(wgt * b * b))
+    return float(np.sqrt(num / den))
 
 
 def gpu_layer(w: torch.Tensor, x: torch.Tensor, bits, group, grid, damp=0.01, chunk_tokens=None,

@@ -58,3 +58,30 @@ def test_stepwise_oracle_factor_matches_the_oracle():
     assert np.array_equal(h1, h2) and lam1 == lam2 and np.array_equal(hd1, hd2)
     assert np.linalg.norm(u2 - u1) <= 1e-12 * np.linalg.norm(u1)
     assert np.allclose(r2 @ r2.T, hd2, rtol=1e-12, atol=1e-12 * np.abs(hd2).max())
+
+
+def test_upper_inverse_by_halves():
+    """upper_inverse (halves down to small leaves, ragged splits included)
+    against numpy's general inverse, and upper triangular."""
+    import numpy as np
+    rng = np.random.default_rng(9)
+    for n, leaf in ((300, 64), (129, 32), (64, 64), (7, 2)):
+        r = np.triu(rng.standard_normal((n, n))) + np.diag(np.full(n, 4.0))
+        u = BH.upper_inverse(r, leaf=leaf)
+        assert np.all(np.tril(u, -1) == 0.0)
+        np.testing.assert_allclose(u, np.linalg.inv(r), rtol=1e-9, atol=1e-12)
+
+
+def test_lower_rel_fro_by_row_blocks():
+    """The blockwise distance of the lower triangles equals the symmetric
+    Frobenius distance written out on a small case (upper parts ignored)."""
+    import numpy as np
+
+    from parity_util import lower_rel_fro
+    rng = np.random.default_rng(11)
+    d = 37
+    a, b = rng.standard_normal((d, d)), rng.standard_normal((d, d))
+    sym = lambda m: np.tril(m) + np.tril(m, -1).T  # noqa: E731
+    want = np.linalg.norm(sym(a) - sym(b)) / np.linalg.norm(sym(b))
+    for rows in (5, 16, 64):
+        assert abs(lower_rel_fro(a, b, rows=rows) - want) <= 1e-13 * want

@@ -467,6 +467,53 @@ def test_hessian_factor_definition_and_relations():
         O.hessian_factor(np.array([[1.0, 2.0], [2.0, 1.0]]))
 
 
+@pytest.mark.parametrize("d,block", [(300, 64), (257, 100), (64, 64), (5, 2)])
+def test_hessian_factor_blocked_path(d, block):
+    """The blocked path (taken at widths whose d * d reaches 2^31) on small
+    matrices, ragged last blocks included: R upper with a positive diagonal
+    and R R^T = H_d (which fix R uniquely), the diagonal and 2 x 2 closed forms,
+    the unblocked path's R within rounding, and LinAlgError on an indefinite
+    matrix."""
+    rng = np.random.default_rng(d + block)
+    x = rng.standard_normal((3 * d + 5, d)) @ rng.standard_normal((d, d))
+    hd, _ = O.damp(O.hessian(x), 0.01)
+    r = O.hessian_factor(hd, block=block)
+    assert np.all(np.tril(r, -1) == 0.0) and np.all(np.diag(r) > 0)
+    np.testing.assert_allclose(r @ r.T, hd, rtol=1e-12, atol=1e-12 * np.abs(hd).max())
+    np.testing.assert_allclose(r, O.hessian_factor(hd), rtol=1e-9, atol=1e-12 * np.abs(r).max())
+    np.testing.assert_array_equal(O.hessian_factor(np.diag([4.0, 9.0, 0.25]), block=2), np.diag([2.0, 3.0, 0.5]))
+    a, b, c = 5.0, 2.0, 4.0
+    np.testing.assert_allclose(O.hessian_factor(np.array([[a, b], [b, c]]), block=1),
+                               [[np.sqrt(a - b * b / c), b / np.sqrt(c)], [0.0, np.sqrt(c)]], rtol=1e-15)
+    with pytest.raises(np.linalg.LinAlgError):
+        O.hessian_factor(np.array([[1.0, 2.0, 0.0], [2.0, 1.0, 0.0], [0.0, 0.0, 1.0]]), block=1)
+
+
+def test_large_width_forms(monkeypatch):
+    """From BLAS_SYRK_MAX entries on (the fc2 width with the real limit),
+    hessian takes a general product of an explicit copy of X^T and
+    hessian_factor the blocked algorithm; with the limit lowered, both on a
+    small input against the plain forms."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((200, 90)).astype(np.float16)
+    h_plain = O.hessian(x)
+    r_plain = O.hessian_factor(O.damp(h_plain, 0.01)[0])
+    import oracle.gptq_oracle as OM  # the module whose global the two functions read
+    monkeypatch.setattr(OM, "BLAS_SYRK_MAX", 90 * 90)
+    calls = []
+    blocked = OM._cholesky_lower_blocked
+    monkeypatch.setattr(OM, "_cholesky_lower_blocked", lambda a, b, p=None: calls.append(b) or blocked(a, b, p))
+    h = O.hessian(x)
+    np.testing.assert_allclose(h, h_plain, rtol=1e-13, atol=1e-12)
+    assert np.all(h == h.T)
+    hd = O.damp(h, 0.01)[0]
+    r = O.hessian_factor(hd)
+    assert np.all(np.tril(r, -1) == 0.0) and np.all(np.diag(r) > 0)
+    np.testing.assert_allclose(r @ r.T, hd, rtol=1e-12, atol=1e-12 * np.abs(hd).max())
+    np.testing.assert_allclose(r, r_plain, rtol=1e-9, atol=1e-12 * np.abs(r).max())
+    assert calls == [4096]  # the factor took the blocked path
+
+
 @pytest.mark.parametrize("group", [16, 48, 96, 192])
 def test_groups_not_aligned_to_the_block_are_block_size_invariant(group):
     """Group sizes that neither divide the 128-column block nor are multiples of
