@@ -16,12 +16,16 @@
 //  * The MFMA operands (8 consecutive tokens per lane) come out of LDS with the
 //    transpose read ds_read_b64_tr_b16; the swizzle keeps these reads free of
 //    bank conflicts. v_mfma_f32_32x32x16_f16: fp16 x fp16 products are exact.
-//  * Accuracy: every 1024 tokens the fp32 accumulators are folded into a
-//    second fp32 register (Fast2Sum) and the rounding error is put back into the
-//    MFMA accumulator, so the running sum loses nothing to the fold: what
-//    remains are the roundings of the 64 matrix steps inside each window. The
-//    final value is outer + acc in fp64, and split-K partials are summed in a
-//    fixed order in fp64 (deterministic).
+//  * Accuracy: every W tokens the fp32 accumulators are folded into a second
+//    fp32 register (Fast2Sum) and the rounding error is put back into the MFMA
+//    accumulator, so the running sum loses nothing to the fold: what remains
+//    are the roundings of the W/16 matrix steps inside each window, whose sum
+//    over a call of n tokens grows as W / sqrt(n) relative to H. W is chosen
+//    per call as 1024 sqrt(n / 262144) rounded down to a power of two within
+//    [256, 1024] (1024 from 262144 tokens, 512 from 65536, 256 below), which
+//    keeps that error at the level of a 262144-token call with W = 1024 down to
+//    16384 tokens. The final value is outer + acc in fp64, and split-K
+//    partials are summed in a fixed order in fp64 (deterministic).
 #include <mutex>
 #include <type_traits>
 
@@ -47,7 +51,7 @@ namespace {
 constexpr int TI = 256;            // tile rows (i features)
 constexpr int TJ = 128;            // tile cols (j features)
 constexpr int KS = GPTQ_SYRK_KS;   // tokens per LDS stage
-constexpr int FOLD = 1024 / KS;    // stages between error folds (1024 tokens)
+constexpr int kFoldMinTokens = 256, kFoldMaxTokens = 1024;  // fold window W, tokens
 #ifndef GPTQ_SYRK_WAVES
 #define GPTQ_SYRK_WAVES 8
 #endif
@@ -104,6 +108,7 @@ struct SyrkArgs {
   void* H;
   int64_t ldh;
   int h_f64, accumulate;
+  int fold_mask;    // W / KS - 1 (W / KS a power of two): fold after stages s with (s + 1) & fold_mask == 0
 };
 
 // Tile slot t -> (bi, bj), the same order in the SYRK and in the reductions.
@@ -447,7 +452,7 @@ __global__ __launch_bounds__(NT, 1) void syrk_kernel(SyrkArgs a) {
             acc[f][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[slot][f], bf[slot][h], acc[f][h], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if ((s + 1) % FOLD == 0) fold();
+      if (((s + 1) & a.fold_mask) == 0) fold();
       cur = cnext;
     }
   };
@@ -747,8 +752,17 @@ gptq_status_t static_scratch(void** ptr) {
   return GPTQ_OK;
 }
 
-gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const half_t* X, int64_t n,
-                           int64_t ldx, int accumulate, void* ws, size_t ws_bytes, hipStream_t st, bool allow_xt) {
+namespace {
+// Fold window W of a call of n tokens (see the accuracy note at the top).
+int syrk_fold_tokens(int64_t n) {
+  int w = kFoldMaxTokens;
+  while (w > kFoldMinTokens && (double)w * w * 262144.0 > (double)kFoldMaxTokens * kFoldMaxTokens * (double)n) w /= 2;
+  return w;
+}
+
+gptq_status_t syrk_enqueue_launches(void* H, int h_f64, int64_t d, int64_t ldh, const half_t* X, int64_t n,
+                                    int64_t ldx, int accumulate, void* ws, size_t ws_bytes, hipStream_t st,
+                                    bool allow_xt, int fold_tokens) {
   const int nt = syrk_ntiles(d);
   if (n == 0) {
     if (!accumulate) {
@@ -762,8 +776,8 @@ gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const hal
   if (nl < n) {
     for (int64_t t0 = 0; t0 < n; t0 += nl) {
       const int64_t nc = n - t0 < nl ? n - t0 : nl;
-      gptq_status_t s =
-          syrk_enqueue(H, h_f64, d, ldh, X + t0 * ldx, nc, ldx, accumulate || t0 > 0, ws, ws_bytes, st, allow_xt);
+      gptq_status_t s = syrk_enqueue_launches(H, h_f64, d, ldh, X + t0 * ldx, nc, ldx, accumulate || t0 > 0, ws,
+                                              ws_bytes, st, allow_xt, fold_tokens);
       if (s != GPTQ_OK) return s;
     }
     return GPTQ_OK;
@@ -806,6 +820,7 @@ gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const hal
   a.ldh = ldh;
   a.h_f64 = h_f64;
   a.accumulate = accumulate;
+  a.fold_mask = fold_tokens / KS - 1;
   {
     // executed: every non-empty tile over the launch's stages (diagonal tiles whole)
     const int64_t T = ceil_div(d, TI), Tj = ceil_div(d, TJ);
@@ -837,6 +852,14 @@ gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const hal
     GPTQ_CHECK_LAUNCH();
   }
   return GPTQ_OK;
+}
+}  // namespace
+
+gptq_status_t syrk_enqueue(void* H, int h_f64, int64_t d, int64_t ldh, const half_t* X, int64_t n,
+                           int64_t ldx, int accumulate, void* ws, size_t ws_bytes, hipStream_t st, bool allow_xt) {
+  // the fold window follows the whole call's token count, not one launch's
+  return syrk_enqueue_launches(H, h_f64, d, ldh, X, n, ldx, accumulate, ws, ws_bytes, st, allow_xt,
+                               syrk_fold_tokens(n));
 }
 
 }  // namespace gptq

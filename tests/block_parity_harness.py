@@ -113,12 +113,16 @@ def upper_inverse(r, leaf=4096, say=None):
     return out
 
 
-def oracle_factor_in_steps(xh, damp, chunk=4096):
+def _print_line(text):
+    print(text, flush=True)
+
+
+def oracle_factor_in_steps(xh, damp, chunk=4096, log=_print_line):
     """The oracle's H over the tokens chunk by chunk (each chunk's 2 X_c^T X_c
     summed in order, which is exactly the oracle's own sum), lambda, its R =
     hessian_factor(H_d) (a line per column block), and U = R^-1 (pinned in
     the oracle's tests) by halves. Every step prints a line, so that the
-    longest silent step is one chunk or one block."""
+    longest silent step is one chunk or one block (log: where the lines go)."""
     import oracle as O
     n, d = xh.shape
     h = None
@@ -129,16 +133,16 @@ def oracle_factor_in_steps(xh, damp, chunk=4096):
         else:
             h += part  # the oracle's sum over chunks, in place
         del part
-        print(f"[harness] oracle H: {min(t0 + chunk, n)} / {n} tokens", flush=True)
+        log(f"[harness] oracle H: {min(t0 + chunk, n)} / {n} tokens")
     hd, lam = O.damp(h, damp)
-    r = O.hessian_factor(hd, progress=lambda k, dd: print(f"[harness] oracle R: {k} / {dd} columns", flush=True))
-    print("[harness] oracle R = hessian_factor(H_d) done", flush=True)
-    u = upper_inverse(r, say=lambda m: print(m, flush=True))  # upper triangular by construction
-    print("[harness] oracle U = R^-1 done", flush=True)
+    r = O.hessian_factor(hd, progress=lambda k, dd: log(f"[harness] oracle R: {k} / {dd} columns"))
+    log("[harness] oracle R = hessian_factor(H_d) done")
+    u = upper_inverse(r, say=log)  # upper triangular by construction
+    log("[harness] oracle U = R^-1 done")
     return h, lam, u, hd, r
 
 
-def compare_rows_in_steps(wn, gpu, oracle, bits, group, grid, label):
+def compare_rows_in_steps(wn, gpu, oracle, bits, group, grid, label, log=_print_line):
     """compare_rows for wide layers, a line after each step (the factor
     statistics, the oracle's follow mode, its free run)."""
     import oracle as O
@@ -147,11 +151,11 @@ def compare_rows_in_steps(wn, gpu, oracle, bits, group, grid, label):
     t0 = time.time()
     stats = {"label": label, "rows": wn.shape[0]}
     _factor_stats(stats, gpu, h, lam, u, hd, r_oracle=r)
-    print(f"[harness] {label}: factor statistics done", flush=True)
+    log(f"[harness] {label}: factor statistics done")
     follow = O.gptq_quantize(wn, u, bits, grid, group, follow_codes=gpu["codes"], follow_zeros=gpu["zeros"])
-    print(f"[harness] {label}: oracle follow mode done", flush=True)
+    log(f"[harness] {label}: oracle follow mode done")
     free = O.gptq_quantize(wn, u, bits, grid, group)
-    print(f"[harness] {label}: oracle free run done", flush=True)
+    log(f"[harness] {label}: oracle free run done")
     _row_stats(stats, wn, gpu, follow, free, h, bits, grid, group)
     stats["oracle_s"] = time.time() - t0
     return stats

@@ -11,10 +11,16 @@ H; the R factor for the OPT-175B layers, fp64 U for the OPT-13B one).
   tokens, damps it and factors it, then runs follow mode and a free run on
   258 sampled rows (rows are independent given U, and every grid is fitted
   within its row). The usual gates apply to those rows.
-* OPT-175B fc2 (12288 x 49152): the oracle's own H would cost 6.3e14 fp64
-  flops on the host, about 20 minutes on 16 cores, more than a test may take;
-  its code parity is not measured. The checks there are on sampled outputs the
-  oracle computes one by one, and on properties that hold at any size:
+* OPT-175B fc2 (12288 x 49152): the oracle's own H over all 262144 tokens
+  would cost 1.3e15 fp64 flops on the host, about half an hour on 16 cores,
+  more than a test may take. Code parity there runs on a token-count stand-in:
+  the whole layer on the GPU at its full width, calibrated on the first 16384
+  of its tokens (fewer tokens than features, so H is singular before damping:
+  a harder case for the factor's accuracy than the full token count), against
+  the oracle's own H over those tokens, its factor and follow mode on 258
+  sampled rows, with every gate. The full token count has the checks on
+  sampled outputs the oracle computes one by one, and on properties that hold
+  at any size:
   - sampled entries of H against the oracle's fp64 Hessian of those columns;
   - lambda against damp * mean(diag H) (diag in fp64 from X);
   - U upper with a positive diagonal, and U^T U H_d e_j = e_j on sampled
@@ -97,6 +103,44 @@ def test_code_parity_full_size_sampled_rows(label, names):
         gr.update(factor)
         stats = compare_rows(wn, gr, h, lam_o, u, hd, c.bits, c.group, c.grid, f"{c.name} ({len(rows)} rows)")
         assert_gates(stats)
+
+
+FC2_STAND_IN_TOKENS = 16384
+
+
+@pytest.mark.timeout(1200)
+def test_code_parity_fc2_full_width_token_stand_in():
+    """OPT-175B fc2 at its full width (12288 x 49152) on the first 16384 of its
+    262144 tokens: the GPU's H, R and whole layer in the benchmark's path; the
+    oracle's H over the same tokens chunk by chunk, lambda, its R and U = R^-1,
+    then follow mode and a free run on 258 sampled rows; every gate."""
+    from block_parity_harness import compare_rows_in_steps, oracle_factor_in_steps
+
+    cfg = S.CONFIGS["opt175b-fc2"]
+    n = FC2_STAND_IN_TOKENS
+    say(f"[case] fc2 full-width code parity m={cfg.m} d={cfg.d} on the first {n} of {cfg.n_tokens} tokens")
+    t0 = time.time()
+    w = S.make_weights(cfg, DEV)
+    x = S.make_activations(cfg, DEV)[:n].contiguous()
+    torch.cuda.empty_cache()
+    H, R, lam = device_factor_r(cfg.d, x, cfg.damp)
+    res = G.quantize_layer(w, R, cfg.bits, cfg.group, cfg.grid, factor="R")
+    torch.cuda.synchronize()
+    rows = sample_rows(cfg.m, 21 + cfg.layer_id)
+    gr = rows_of(res, rows, cfg.bits, cfg.d)
+    gr.update({"H": H.cpu().numpy(), "U": R.cpu().numpy(), "lam": lam, "u_eps": 2.0 ** -53, "factor": "R"})
+    wn = w[torch.as_tensor(rows, device=DEV)].double().cpu().numpy()
+    xh = x.cpu().numpy()
+    del H, R, x, w, res
+    torch.cuda.empty_cache()
+    say(f"[step] fc2 stand-in: GPU layer done in {time.time() - t0:.1f} s; oracle H over {n} tokens")
+    oracle = oracle_factor_in_steps(xh, cfg.damp, log=say)
+    del xh
+    stats = compare_rows_in_steps(wn, gr, oracle, cfg.bits, cfg.group, cfg.grid,
+                                  f"{cfg.name} first {n} tokens ({len(rows)} rows)", log=say)
+    say(f"[parity] fc2 stand-in: hard={stats['hard']} identical={stats['identical']:.7f} "
+        f"scale_rel={stats['scale_rel']:.3e} u_rel={stats['u_rel']:.3e} h_rel={stats['h_rel']:.3e}")
+    assert_gates(stats)
 
 
 def _run_full(cfg):
