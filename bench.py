@@ -62,8 +62,8 @@ CHUNK_TOKENS = 262144         # the whole calibration set (128 sequences of 2048
 SYRK_TRAFFIC = {
     "config": "opt175b-fc2",
     "chunk_tokens": 262144,
-    "source_sha256_16": "385e6a0458213101",   # syrk.hip + common.h
-    "fetch_bytes": 175880480.2 * 1024 * 2.0,
+    "source_sha256_16": "52974eca4cb9822b",   # syrk.hip + common.h
+    "fetch_bytes": 176326002.7 * 1024 * 2.0,
     "write_bytes": 9488112.0 * 1024 * 1.0,
 }
 
