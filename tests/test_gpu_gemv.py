@@ -53,9 +53,12 @@ def _run(c, s, z, x, bits, group):
     return words, y.cpu().numpy().astype(np.float64)
 
 
-# m >= 32768 takes the 8-rows-per-wave form (33000: a ragged last workgroup)
+# m >= 32768 takes the 8-rows-per-wave form (33000: a ragged last workgroup);
+# 20480 and 14336 columns give each lane 10 and 7 chunks of a row, so that the
+# look-ahead loop ends at each of its register sets
 @pytest.mark.parametrize("m,d,bits,group", [(1, 32, 3, 0), (5, 96, 3, 32), (17, 256, 4, 128), (64, 256, 2, 64),
-                                            (3, 128, 8, 0), (33, 224, 3, 32), (33000, 64, 3, 32)])
+                                            (3, 128, 8, 0), (33, 224, 3, 32), (33000, 64, 3, 32),
+                                            (9, 20480, 3, 128), (7, 14336, 2, 64), (6, 12288, 3, 128)])
 def test_bit_exact_on_exactly_representable_inputs(m, d, bits, group):
     say(f"[case] gemv exact m={m} d={d} bits={bits} group={group}")
     c, s, z, x = _case(m, d, bits, group, seed=m * 7 + bits, exact=True)
