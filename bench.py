@@ -269,7 +269,7 @@ def cpu_baseline(cfg, w, x, rows=None, tokens=None, act_order=False, static_grou
         threads = os.cpu_count()
     d = cfg.d
     if tokens is None:
-        tokens = int(min(16384, max(256, 2.5e12 / d ** 2)) // 256 * 256)
+        tokens = int(min(16384, max(256, 5e12 / d ** 2)) // 256 * 256)
     if rows is None:
         rows = int(min(512, max(16, 2e11 / d ** 2)))
     rows = min(rows, cfg.m)
